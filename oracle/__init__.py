@@ -1,0 +1,241 @@
+"""fp64 CPU oracle for the speculative-sampling verification step.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package. The HIP library
+and its Python binding never import it, and it never imports them: the two
+share no code. The arithmetic lives in ``spec_verify_ref.c`` (plain C, fp64,
+scalar loops); this module only builds it with gcc and marshals numpy arrays.
+
+Parity status of each function (what pins it is in the tests):
+  softmax_row          pinned: scipy/torch fp64 softmax, closed forms
+  argmax_row           pinned: numpy.argmax (first occurrence) on planted ties
+  philox4x32_10        pinned: rocRAND's Philox4x32-10 engine (compiled host-side)
+  draw_inverse_cdf     pinned: brute-force interval membership on small cases
+  round_sampling       pinned: red/blue example, exact enumeration, forced rounds
+  round_greedy         pinned: worked rounds, argmax agreement by hand
+  spec_verify_ref      pinned: chi-square of emitted tokens against p, accepted
+                       length against the closed form, worked rounds
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_verify_ref.c")
+_LIB = os.path.join(_HERE, "_build", "libspecverify_oracle.so")
+
+F32 = 0
+BF16 = 1
+
+SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO = range(5)
+DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.ref_softmax_row.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_double, P]
+        lib.ref_softmax_row.restype = None
+        lib.ref_argmax_row.argtypes = [P, ctypes.c_int, ctypes.c_int64]
+        lib.ref_argmax_row.restype = ctypes.c_int64
+        lib.ref_philox4x32_10.argtypes = [P, ctypes.c_uint64, P]
+        lib.ref_philox4x32_10.restype = None
+        lib.ref_uniform24.argtypes = [ctypes.c_uint32]
+        lib.ref_uniform24.restype = ctypes.c_double
+        lib.ref_draw_inverse_cdf.argtypes = [P, ctypes.c_int64, ctypes.c_double, P, P, P]
+        lib.ref_draw_inverse_cdf.restype = ctypes.c_int64
+        lib.ref_round_sampling.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, P, P, P, P,
+                                           P, P, P, P, P, P]
+        lib.ref_round_sampling.restype = ctypes.c_int
+        lib.ref_round_greedy.argtypes = [P, P, ctypes.c_int, P]
+        lib.ref_round_greedy.restype = ctypes.c_int
+        lib.spec_verify_ref.argtypes = [P, P, ctypes.c_int, P, P, P, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                        ctypes.c_uint32] + [P] * 11
+        lib.spec_verify_ref.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logits(a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError("logits must be float32 or uint16 (bf16 bit patterns)")
+
+
+def softmax_row(row: np.ndarray, tau: float) -> np.ndarray:
+    row, dt = _logits(row)
+    out = np.empty(row.shape[-1], dtype=np.float64)
+    _load().ref_softmax_row(_ptr(row), dt, row.shape[-1], float(tau), _ptr(out))
+    return out
+
+
+def argmax_row(row: np.ndarray) -> int:
+    row, dt = _logits(row)
+    return int(_load().ref_argmax_row(_ptr(row), dt, row.shape[-1]))
+
+
+def philox4x32_10(counter, seed: int) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint32).reshape(4))
+    out = np.empty(4, dtype=np.uint32)
+    _load().ref_philox4x32_10(_ptr(c), ctypes.c_uint64(seed & (2**64 - 1)), _ptr(out))
+    return out
+
+
+def uniform24(word: int) -> float:
+    return float(_load().ref_uniform24(ctypes.c_uint32(word)))
+
+
+def draw_inverse_cdf(w: np.ndarray, v: float):
+    """Returns (token, S, margin, fallback)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    S = np.zeros(1)
+    m = np.zeros(1)
+    fb = np.zeros(1, dtype=np.int32)
+    x = _load().ref_draw_inverse_cdf(_ptr(w), w.shape[0], float(v), _ptr(S), _ptr(m), _ptr(fb))
+    return int(x), float(S[0]), float(m[0]), bool(fb[0])
+
+
+def round_sampling(p: np.ndarray, q: np.ndarray, g, u, v):
+    """One sampling round from explicit probabilities and uniforms.
+
+    p: [L+1, V], q: [L, V], g: [L], u: [L], v: [L+1].
+    Returns dict(n, out, S, row, kind, margin_accept, margin_draw, status).
+    """
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    L = p.shape[0] - 1
+    V = p.shape[1]
+    n_pad = max(L, 1)  # C side never reads q, g, u when L == 0
+    qa = np.zeros((n_pad, V))
+    ga = np.zeros(n_pad, dtype=np.int32)
+    ua = np.zeros(n_pad)
+    if L:
+        qa[:L] = np.asarray(q, dtype=np.float64).reshape(L, V)
+        ga[:L] = np.asarray(g, dtype=np.int32).reshape(L)
+        ua[:L] = np.asarray(u, dtype=np.float64).reshape(L)
+    q, g, u = qa, ga, ua
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(L + 1))
+    w = np.empty(V)
+    out = np.full(L + 1, -1, dtype=np.int32)
+    S = np.full(1, np.nan)
+    row = np.full(1, -1, dtype=np.int32)
+    kind = np.zeros(1, dtype=np.int32)
+    macc = np.full(n_pad, np.nan)
+    mdraw = np.full(1, np.nan)
+    status = np.zeros(1, dtype=np.int32)
+    n = _load().ref_round_sampling(_ptr(p), _ptr(q), _ptr(g), L, V, _ptr(u), _ptr(v), _ptr(w),
+                                   _ptr(out), _ptr(S), _ptr(row), _ptr(kind), _ptr(macc),
+                                   _ptr(mdraw), _ptr(status))
+    return dict(n=int(n), out=out, S=float(S[0]), row=int(row[0]), kind=int(kind[0]),
+                margin_accept=macc[:L], margin_draw=float(mdraw[0]), status=int(status[0]))
+
+
+def round_greedy(amax, g):
+    amax = np.ascontiguousarray(np.asarray(amax, dtype=np.int64))
+    L = amax.shape[0] - 1
+    ga = np.zeros(max(L, 1), dtype=np.int32)
+    if L:
+        ga[:L] = np.asarray(g, dtype=np.int32).reshape(L)
+    g = ga
+    out = np.full(L + 1, -1, dtype=np.int32)
+    n = _load().ref_round_greedy(_ptr(amax), _ptr(g), L, _ptr(out))
+    return int(n), out
+
+
+def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
+                    draft_len, temperature, seed: int, seq_base: int = 0,
+                    nthreads: int = 1) -> dict:
+    """The whole step on host arrays (see spec_verify_ref.c for the contract).
+
+    target [B, k+1, V] and draft [B, k, V] are float32 or uint16 (bf16 bits).
+    ``nthreads`` > 1 runs disjoint slices of sequences in parallel threads;
+    each slice keeps its global sequence index, so results do not change.
+    """
+    target, dt = _logits(target)
+    draft, dt2 = _logits(draft)
+    assert dt == dt2, "target and draft must share a dtype"
+    B, k1, V = target.shape
+    k = k1 - 1
+    assert draft.shape == (B, k, V), (draft.shape, (B, k, V))
+    tokens = np.ascontiguousarray(np.asarray(draft_tokens, dtype=np.int32).reshape(B, k))
+    if draft_len is None:
+        lens = None
+    else:
+        lens = np.ascontiguousarray(np.asarray(draft_len, dtype=np.int32).reshape(B))
+    temp = np.asarray(temperature, dtype=np.float32)
+    temp = np.ascontiguousarray(np.broadcast_to(temp, (B,)).copy())
+
+    res = dict(
+        out_tokens=np.full((B, k + 1), -1, dtype=np.int32),
+        num_accepted=np.zeros(B, dtype=np.int32),
+        seq_status=np.zeros(B, dtype=np.int32),
+        p_g=np.full((B, k), np.nan),
+        q_g=np.full((B, k), np.nan),
+        argmax=np.full((B, k + 1), -1, dtype=np.int32),
+        resid_mass=np.full(B, np.nan),
+        margin_accept=np.full((B, k), np.nan),
+        margin_draw=np.full(B, np.nan),
+        draw_row=np.full(B, -1, dtype=np.int32),
+        draw_kind=np.zeros(B, dtype=np.int32),
+    )
+    lib = _load()
+
+    def run(b0: int, b1: int) -> int:
+        if b1 <= b0:
+            return 0
+        sl = slice(b0, b1)
+        outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
+                                     "argmax", "resid_mass", "margin_accept", "margin_draw",
+                                     "draw_row", "draw_kind")]
+        return lib.spec_verify_ref(
+            _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
+            _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]),
+            b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
+            ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs])
+
+    if nthreads <= 1 or B <= 1:
+        rc = run(0, B)
+        if rc != 0:
+            raise MemoryError("oracle scratch allocation failed")
+    else:
+        step = (B + nthreads - 1) // nthreads
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            rcs = list(ex.map(lambda b0: run(b0, min(B, b0 + step)), range(0, B, step)))
+        if any(rcs):
+            raise MemoryError("oracle scratch allocation failed")
+    return res

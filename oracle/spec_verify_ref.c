@@ -1,0 +1,414 @@
+/*
+ * spec_verify_ref.c -- plain fp64 CPU oracle for the speculative-sampling
+ * verification step.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the reference the HIP library is checked
+ * against. Only the test suite, the smoke check and the benchmark's CPU
+ * baseline load it; the product path never does. It shares no code, header,
+ * table or helper with the HIP library.
+ *
+ * It is deliberately slow and literal: every probability row is widened to
+ * fp64, normalised in full, and every decision is taken in the order the
+ * pages describe. No blocking, no fusion, no reordering.
+ *
+ * Sources (cited below by the short tag in brackets):
+ *   [ART] "Speculative Decoding and the Art of Fast LLM Inference"
+ *         (mesuvash.github.io blog), sections "The Algorithm, Step by Step"
+ *         and "Why It Stays Exact".
+ *   [TLS] thelatentsource.com article "speculative-decoding-llm-speed",
+ *         section "The correction that keeps the target in charge"
+ *         (P_accept, the accept_token snippet, r(x), the red/blue example).
+ *   [TAI] techaiinterview.com, "How does speculative decoding work, why is it
+ *         lossless, and how much does it speed things up?", sections
+ *         "Core explanation" (algorithm, steps 1-4) and "Deep dive:
+ *         correctness and speedup" (greedy rule).
+ *   [PHX] J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel
+ *         Random Numbers: As Easy as 1, 2, 3", SC'11 -- Philox4x32, 10 rounds.
+ *
+ * Readings taken where the pages leave a step open (each one is listed with
+ * its reason in the design notes of the repository):
+ *   R1  temperature: p = softmax(logits / tau) for target and draft alike,
+ *       one tau per sequence; tau == 0 selects the greedy rule.
+ *   R2  random draws: Philox4x32-10, key = seed, counter = (position, global
+ *       sequence index, 0, 0); word 0 -> acceptance uniform, word 1 -> the
+ *       residual/bonus uniform; uniform = (word >> 8) * 2^-24 in [0, 1).
+ *   R3  acceptance: accept iff u < min(1, p(g)/q(g)), strict.
+ *   R4  inverse CDF: ascending token id, C(x) = sum_{y<=x} w(y) summed
+ *       sequentially, pick the smallest x with C(x) > v*S.
+ *   R5  greedy: accept g_i iff it equals the target argmax at i (lowest id
+ *       on ties); the correction/bonus is that argmax.
+ *   R6  row alignment: target row i and draft row i score draft position i
+ *       (0-based); the bonus is target row L (L = the sequence's draft length).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { REF_F32 = 0, REF_BF16 = 1 };
+
+enum {
+    REF_SEQ_OK = 0,
+    REF_SEQ_BAD_TOKEN = 1,
+    REF_SEQ_BAD_LEN = 2,
+    REF_SEQ_BAD_TEMP = 3,
+    REF_SEQ_QZERO = 4
+};
+
+enum {
+    REF_DRAW_NONE = 0,           /* sequence rejected by a status check      */
+    REF_DRAW_GREEDY = 1,         /* greedy correction / bonus (argmax)       */
+    REF_DRAW_RESIDUAL = 2,       /* sample from norm(max(0, p - q))          */
+    REF_DRAW_BONUS = 3,          /* sample from p at row L                   */
+    REF_DRAW_RESIDUAL_AS_P = 4   /* residual mass rounded to 0: sample p     */
+};
+
+/* ------------------------------------------------------------------ */
+/* Input widening (exact): fp32 -> fp64; bf16 -> fp32 -> fp64.          */
+/* ------------------------------------------------------------------ */
+static double ref_logit(const void *buf, int dtype, size_t idx)
+{
+    if (dtype == REF_F32)
+        return (double)((const float *)buf)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)buf)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------ */
+/* Softmax of one logit row at temperature tau (reading R1).            */
+/* [ART] "Verify in parallel": the target returns a distribution p_i at */
+/* each position; [ART] "Why It Stays Exact", key limitation: draft and */
+/* target must use the same sampling parameters (temperature).          */
+/* p(x) = exp(x/tau - max_y y/tau) / sum_z exp(z/tau - max_y y/tau).    */
+/* ------------------------------------------------------------------ */
+void ref_softmax_row(const void *row, int dtype, int64_t V, double tau, double *p)
+{
+    double mx = -INFINITY;
+    for (int64_t x = 0; x < V; x++) {
+        double s = ref_logit(row, dtype, (size_t)x) / tau;
+        if (s > mx)
+            mx = s;
+    }
+    double z = 0.0;
+    for (int64_t x = 0; x < V; x++) {
+        p[x] = exp(ref_logit(row, dtype, (size_t)x) / tau - mx);
+        z += p[x];
+    }
+    for (int64_t x = 0; x < V; x++)
+        p[x] /= z;
+}
+
+/* Lowest token id holding the row maximum (reading R5). */
+int64_t ref_argmax_row(const void *row, int dtype, int64_t V)
+{
+    int64_t best = 0;
+    double bv = ref_logit(row, dtype, 0);
+    for (int64_t x = 1; x < V; x++) {
+        double s = ref_logit(row, dtype, (size_t)x);
+        if (s > bv) {
+            bv = s;
+            best = x;
+        }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 [PHX] (reading R2).                                    */
+/* Each round multiplies counter words 0 and 2 by the two Philox        */
+/* multipliers, keeps both halves of each 64-bit product, and mixes the */
+/* high halves with the two other counter words and the round key; the */
+/* key advances by the two Weyl constants between rounds.               */
+/* ------------------------------------------------------------------ */
+void ref_philox4x32_10(const uint32_t ctr[4], uint64_t seed, uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    for (int round = 0; round < 10; round++) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        uint64_t prod0 = (uint64_t)M0 * c0;
+        uint64_t prod1 = (uint64_t)M1 * c2;
+        uint32_t n0 = (uint32_t)(prod1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)prod1;
+        uint32_t n2 = (uint32_t)(prod0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)prod0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* 24 high bits of a word as a uniform in [0, 1): exact in fp32 and fp64. */
+double ref_uniform24(uint32_t word)
+{
+    return (double)(word >> 8) * (1.0 / 16777216.0);
+}
+
+/* The two uniforms of draft position `pos` of global sequence `seq`. */
+void ref_position_uniforms(uint64_t seed, uint32_t seq, uint32_t pos, double *u, double *v)
+{
+    uint32_t ctr[4] = {pos, seq, 0u, 0u};
+    uint32_t w[4];
+    ref_philox4x32_10(ctr, seed, w);
+    *u = ref_uniform24(w[0]);
+    *v = ref_uniform24(w[1]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Inverse-CDF draw from non-negative weights w[0..V-1] (reading R4).   */
+/* S = sum of w (sequential, so S equals C(V-1)); returns the smallest  */
+/* x with C(x) > v*S. A zero-weight id is never returned. If rounding   */
+/* left no such x, the largest id with w > 0 is returned and *fallback  */
+/* is set. Returns -1 when S <= 0. *margin = distance of v to the       */
+/* nearer CDF boundary of the chosen id, in units of S.                 */
+/* ------------------------------------------------------------------ */
+int64_t ref_draw_inverse_cdf(const double *w, int64_t V, double v, double *S_out,
+                             double *margin, int *fallback)
+{
+    double S = 0.0;
+    for (int64_t x = 0; x < V; x++)
+        S += w[x];
+    *S_out = S;
+    *fallback = 0;
+    *margin = NAN;
+    if (!(S > 0.0))
+        return -1;
+    double t = v * S;
+    double c = 0.0;
+    for (int64_t x = 0; x < V; x++) {
+        double before = c;
+        c += w[x];
+        if (c > t) {
+            double lo = fabs(v - before / S), hi = fabs(c / S - v);
+            *margin = lo < hi ? lo : hi;
+            return x;
+        }
+    }
+    *fallback = 1;
+    for (int64_t x = V - 1; x >= 0; x--)
+        if (w[x] > 0.0) {
+            *margin = 0.0;
+            return x;
+        }
+    return -1;
+}
+
+/* ------------------------------------------------------------------ */
+/* One sampling round for one sequence, given the probability rows and  */
+/* the uniforms ([ART] steps "Accept or reject, left to right", "Stop   */
+/* at the first rejection", "Bonus token"; [TLS] P_accept, the          */
+/* accept_token rule and r(x); [TAI] algorithm steps 3-4).              */
+/*                                                                      */
+/*   p : (L+1) x V target probabilities; row L is the bonus position    */
+/*   q : L x V draft probabilities                                      */
+/*   g : L drafted tokens                                               */
+/*   u : L acceptance uniforms;  v : L+1 draw uniforms (row i uses v[i])*/
+/*   w : V doubles of scratch                                           */
+/* Outputs: out[0..n] (n = accepted count, out[n] = correction/bonus),  */
+/* *S (mass of the weights drawn from), *row = n, *kind, margins.       */
+/* Returns n, or -1 with *status = REF_SEQ_QZERO when a drafted token   */
+/* has no draft probability ([TLS] accept_token raises in that case).   */
+/* ------------------------------------------------------------------ */
+int ref_round_sampling(const double *p, const double *q, const int32_t *g, int L, int64_t V,
+                       const double *u, const double *v, double *w, int32_t *out, double *S,
+                       int *row, int *kind, double *margin_accept, double *margin_draw,
+                       int *status)
+{
+    *status = REF_SEQ_OK;
+    for (int i = 0; i < L; i++) {
+        const double *pi = p + (size_t)i * V;
+        const double *qi = q + (size_t)i * V;
+        double pg = pi[g[i]], qg = qi[g[i]];
+        if (!(qg > 0.0)) {
+            *status = REF_SEQ_QZERO;
+            return -1;
+        }
+        double ratio = pg / qg;
+        double thr = ratio < 1.0 ? ratio : 1.0;
+        margin_accept[i] = fabs(u[i] - thr);
+        if (u[i] < thr) {
+            out[i] = g[i];
+            continue;
+        }
+        /* First rejection: discard g_i and everything after it, and draw
+         * the correction from max(0, p_i - q_i), renormalised. */
+        for (int64_t x = 0; x < V; x++) {
+            double d = pi[x] - qi[x];
+            w[x] = d > 0.0 ? d : 0.0;
+        }
+        int fb = 0;
+        int64_t x = ref_draw_inverse_cdf(w, V, v[i], S, margin_draw, &fb);
+        *kind = REF_DRAW_RESIDUAL;
+        if (x < 0) {
+            /* Only reachable through rounding: exactly, a rejection implies
+             * sum max(0, p - q) >= q(g) - p(g) > 0. */
+            x = ref_draw_inverse_cdf(pi, V, v[i], S, margin_draw, &fb);
+            *kind = REF_DRAW_RESIDUAL_AS_P;
+        }
+        out[i] = (int32_t)x;
+        *row = i;
+        return i;
+    }
+    /* Every draft accepted: one more token from the bonus position. */
+    int fb = 0;
+    int64_t x = ref_draw_inverse_cdf(p + (size_t)L * V, V, v[L], S, margin_draw, &fb);
+    out[L] = (int32_t)x;
+    *row = L;
+    *kind = REF_DRAW_BONUS;
+    return L;
+}
+
+/* One greedy round: accept while the target argmax equals the drafted token
+ * ([TAI] "Deep dive", greedy remark; reading R5). amax has L+1 entries. */
+int ref_round_greedy(const int64_t *amax, const int32_t *g, int L, int32_t *out)
+{
+    for (int i = 0; i < L; i++) {
+        if (amax[i] == g[i]) {
+            out[i] = g[i];
+            continue;
+        }
+        out[i] = (int32_t)amax[i];
+        return i;
+    }
+    out[L] = (int32_t)amax[L];
+    return L;
+}
+
+/* ------------------------------------------------------------------ */
+/* The whole step for a batch of B sequences.                           */
+/*                                                                      */
+/* target: [B, k+1, V], draft: [B, k, V] (dtype REF_F32 or REF_BF16 as  */
+/* raw bits); draft_tokens [B, k]; draft_len [B] or NULL (= k);          */
+/* temperature [B] fp32. Sequence b draws with global index seq_base+b. */
+/*                                                                      */
+/* Outputs (all caller-allocated; optional ones may be NULL):           */
+/*   out_tokens [B, k+1]: accepted prefix, then the correction or bonus,*/
+/*                        then -1;  num_accepted [B];  seq_status [B]    */
+/*   p_g, q_g [B, k]: p_i(g_i), q_i(g_i) for sampling rows i < L, NaN   */
+/*                    elsewhere                                          */
+/*   argmax [B, k+1]: target argmax of rows 0..L of greedy sequences, -1 */
+/*   resid_mass [B]: mass S of the weights of the final draw (NaN for   */
+/*                   greedy)                                             */
+/*   margin_accept [B, k]: |u - min(1, p/q)| per acceptance test, NaN   */
+/*   margin_draw [B]: CDF-boundary distance of the final draw, NaN      */
+/*   draw_row [B], draw_kind [B]: row of the final token and REF_DRAW_*  */
+/* Returns 0, or -1 if a scratch allocation failed.                     */
+/* ------------------------------------------------------------------ */
+int spec_verify_ref(const void *target, const void *draft, int dtype,
+                    const int32_t *draft_tokens, const int32_t *draft_len,
+                    const float *temperature, int32_t B, int32_t k, int64_t V, uint64_t seed,
+                    uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
+                    int32_t *seq_status, double *p_g, double *q_g, int32_t *argmax,
+                    double *resid_mass, double *margin_accept, double *margin_draw,
+                    int32_t *draw_row, int32_t *draw_kind)
+{
+    const size_t esz = dtype == REF_F32 ? 4 : 2;
+    double *p = malloc(sizeof(double) * (size_t)(k + 1) * (size_t)V);
+    double *q = malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)V);
+    double *w = malloc(sizeof(double) * (size_t)V);
+    double *u = malloc(sizeof(double) * (size_t)(k + 1));
+    double *v = malloc(sizeof(double) * (size_t)(k + 1));
+    int64_t *amax = malloc(sizeof(int64_t) * (size_t)(k + 1));
+    double *macc = malloc(sizeof(double) * (size_t)(k + 1));
+    if (!p || !q || !w || !u || !v || !amax || !macc) {
+        free(p), free(q), free(w), free(u), free(v), free(amax), free(macc);
+        return -1;
+    }
+
+    for (int32_t b = 0; b < B; b++) {
+        int32_t *out = out_tokens + (size_t)b * (k + 1);
+        const int32_t *g = draft_tokens + (size_t)b * k;
+        const char *trow0 = (const char *)target + (size_t)b * (k + 1) * V * esz;
+        const char *drow0 = (const char *)draft + (size_t)b * k * V * esz;
+        int L = draft_len ? draft_len[b] : k;
+        double tau = (double)temperature[b];
+
+        for (int i = 0; i <= k; i++)
+            out[i] = -1;
+        for (int i = 0; i < k; i++) {
+            if (p_g) p_g[(size_t)b * k + i] = NAN;
+            if (q_g) q_g[(size_t)b * k + i] = NAN;
+            if (margin_accept) margin_accept[(size_t)b * k + i] = NAN;
+        }
+        for (int i = 0; i <= k; i++)
+            if (argmax) argmax[(size_t)b * (k + 1) + i] = -1;
+        if (resid_mass) resid_mass[b] = NAN;
+        if (margin_draw) margin_draw[b] = NAN;
+        if (draw_row) draw_row[b] = -1;
+        if (draw_kind) draw_kind[b] = REF_DRAW_NONE;
+        num_accepted[b] = 0;
+
+        /* Input checks, in this order: length, temperature, tokens. A
+         * temperature must be 0 (greedy) or a normal positive fp32. */
+        int status = REF_SEQ_OK;
+        if (L < 0 || L > k)
+            status = REF_SEQ_BAD_LEN;
+        else if (!(tau == 0.0 || (tau >= (double)1.17549435e-38f && isfinite(tau))))
+            status = REF_SEQ_BAD_TEMP;
+        else
+            for (int i = 0; i < L; i++)
+                if (g[i] < 0 || (int64_t)g[i] >= V)
+                    status = REF_SEQ_BAD_TOKEN;
+        if (status != REF_SEQ_OK) {
+            if (seq_status) seq_status[b] = status;
+            continue;
+        }
+
+        int n;
+        if (tau == 0.0) {
+            for (int i = 0; i <= L; i++) {
+                amax[i] = ref_argmax_row(trow0 + (size_t)i * V * esz, dtype, V);
+                if (argmax) argmax[(size_t)b * (k + 1) + i] = (int32_t)amax[i];
+            }
+            n = ref_round_greedy(amax, g, L, out);
+            if (draw_row) draw_row[b] = n;
+            if (draw_kind) draw_kind[b] = REF_DRAW_GREEDY;
+        } else {
+            for (int i = 0; i <= L; i++)
+                ref_softmax_row(trow0 + (size_t)i * V * esz, dtype, V, tau, p + (size_t)i * V);
+            for (int i = 0; i < L; i++)
+                ref_softmax_row(drow0 + (size_t)i * V * esz, dtype, V, tau, q + (size_t)i * V);
+            for (int i = 0; i < L; i++) {
+                if (p_g) p_g[(size_t)b * k + i] = p[(size_t)i * V + g[i]];
+                if (q_g) q_g[(size_t)b * k + i] = q[(size_t)i * V + g[i]];
+            }
+            for (int i = 0; i <= L; i++)
+                ref_position_uniforms(seed, seq_base + (uint32_t)b, (uint32_t)i, &u[i], &v[i]);
+            for (int i = 0; i <= L; i++)
+                macc[i] = NAN;
+            double S = NAN, mdraw = NAN;
+            int row = -1, kind = REF_DRAW_NONE;
+            n = ref_round_sampling(p, q, g, L, V, u, v, w, out, &S, &row, &kind, macc, &mdraw,
+                                   &status);
+            if (status != REF_SEQ_OK) {
+                for (int i = 0; i <= k; i++)
+                    out[i] = -1;
+                if (seq_status) seq_status[b] = status;
+                continue;
+            }
+            for (int i = 0; i < L; i++)
+                if (margin_accept) margin_accept[(size_t)b * k + i] = macc[i];
+            if (resid_mass) resid_mass[b] = S;
+            if (margin_draw) margin_draw[b] = mdraw;
+            if (draw_row) draw_row[b] = row;
+            if (draw_kind) draw_kind[b] = kind;
+        }
+        num_accepted[b] = n;
+        if (seq_status) seq_status[b] = REF_SEQ_OK;
+    }
+
+    free(p), free(q), free(w), free(u), free(v), free(amax), free(macc);
+    return 0;
+}
