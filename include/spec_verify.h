@@ -1,0 +1,163 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-sampling verification step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call verifies a batch of B drafted continuations. For each sequence b
+ * it takes the target model's logits at k+1 positions, the draft model's
+ * logits at k positions and the k drafted tokens, and returns the accepted
+ * draft prefix followed by exactly one more token:
+ *
+ *   - sampling (temperature > 0): p_i = softmax(target_i / tau),
+ *     q_i = softmax(draft_i / tau); drafted token g_i is accepted iff
+ *     u_i < min(1, p_i(g_i) / q_i(g_i)), scanning left to right and stopping
+ *     at the first rejection; at a rejection the token is drawn from
+ *     norm(max(0, p_i - q_i)); when every draft is accepted a bonus token is
+ *     drawn from the target distribution at the position after the last
+ *     draft.
+ *     ["Speculative Decoding and the Art of Fast LLM Inference",
+ *      "The Algorithm, Step by Step", steps 3-5; thelatentsource.com
+ *      "speculative-decoding-llm-speed", "The correction that keeps the
+ *      target in charge", P_accept and r(x); techaiinterview.com
+ *      speculative-decoding question, "Core explanation", steps 3-4.]
+ *   - greedy (temperature == 0): accept g_i while it equals the target
+ *     argmax at i (lowest token id on ties); the extra token is that argmax.
+ *     [techaiinterview.com, "Deep dive: correctness and speedup", greedy
+ *      remark.]
+ *
+ * Random draws. The pages leave the generator open. This library draws, for
+ * draft position i of global sequence s = seq_base + b, one Philox4x32-10
+ * block (Salmon et al., SC'11) with key = seed (low word first) and counter
+ * (i, s, 0, 0). Word 0 gives the acceptance uniform u_i, word 1 the uniform
+ * v_i of a correction/bonus draw at row i; a uniform is (word >> 8) * 2^-24.
+ * The draw at a row picks the smallest token id x whose cumulative weight
+ * C(x) = sum_{y <= x} w(y) exceeds v * sum_y w(y). Outputs are therefore a
+ * deterministic function of (inputs, seed, seq_base), and splitting a batch
+ * across calls with matching seq_base gives identical results.
+ *
+ * Memory. Every pointer argument is device memory owned by the caller,
+ * except `aux` (a host struct whose members are device pointers). The
+ * library allocates nothing and keeps no state between calls; calls on
+ * different streams with different workspaces may run concurrently. Inputs
+ * are only read. All work is enqueued on `stream` (a hipStream_t, NULL for
+ * the default stream); the call does not synchronise.
+ *
+ * Errors. Problems visible on the host (null required pointer, bad sizes or
+ * dtype, misaligned pointer, workspace too small) return a status at once
+ * and enqueue nothing. Problems in device data are reported per sequence in
+ * aux->seq_status (SPEC_SEQ_*); such a sequence gets num_accepted = 0 and
+ * out_tokens all -1. Logits must be finite; non-finite logits give
+ * unspecified (but memory-safe) results.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of the logits. */
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+/* Host-side return codes. */
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = 1,     /* bad pointer, size, dtype or alignment          */
+    SPEC_EWORKSPACE = 2, /* workspace null, misaligned or too small         */
+    SPEC_ELAUNCH = 3     /* a kernel launch failed (see hipGetLastError)    */
+} spec_status_t;
+
+/* Per-sequence device status codes, written to aux->seq_status. */
+enum {
+    SPEC_SEQ_OK = 0,
+    SPEC_SEQ_BAD_TOKEN = 1, /* a drafted token g_i (i < L) outside [0, V)     */
+    SPEC_SEQ_BAD_LEN = 2,   /* draft length outside [0, k]                   */
+    SPEC_SEQ_BAD_TEMP = 3,  /* temperature NaN, infinite, negative, or       */
+                            /* positive but below FLT_MIN                    */
+    SPEC_SEQ_QZERO = 4      /* the scan reached a drafted token whose fp32   */
+                            /* draft probability is 0 (the acceptance ratio  */
+                            /* is undefined; thelatentsource.com accept_token */
+                            /* raises in this case)                          */
+};
+
+/* How the last emitted token of a sequence was produced (aux->draw_kind). */
+enum {
+    SPEC_DRAW_NONE = 0,           /* sequence failed a status check          */
+    SPEC_DRAW_GREEDY = 1,         /* target argmax (greedy correction/bonus) */
+    SPEC_DRAW_RESIDUAL = 2,       /* drawn from norm(max(0, p - q))          */
+    SPEC_DRAW_BONUS = 3,          /* drawn from p at row L                   */
+    SPEC_DRAW_RESIDUAL_AS_P = 4   /* residual mass rounded to 0: drawn from p */
+};
+
+/* Largest supported number of drafted positions. */
+#define SPEC_MAX_K 63
+
+/* Optional diagnostic outputs. Every member may be NULL. Device pointers,
+ * caller-owned, fully overwritten on each call. */
+typedef struct {
+    float *p_g;          /* [B, k]: p_i(g_i) for i < L of sampling sequences; NaN elsewhere */
+    float *q_g;          /* [B, k]: q_i(g_i), same positions                              */
+    float *resid_mass;   /* [B]: total weight of the final draw (sum max(0, p-q) at a     */
+                         /*      rejection, sum p for a bonus); NaN for greedy or errors   */
+    int32_t *argmax;     /* [B, k+1]: target argmax of rows 0..L of greedy sequences; -1   */
+    int32_t *seq_status; /* [B]: SPEC_SEQ_*                                                */
+    int32_t *draw_row;   /* [B]: row of the last emitted token (= num_accepted), -1 on error */
+    int32_t *draw_kind;  /* [B]: SPEC_DRAW_*                                               */
+    void *event_begin;   /* hipEvent_t or NULL: recorded on `stream` right before the     */
+    void *event_end;     /* row-statistics kernel, and right after it                      */
+} spec_verify_aux_t;
+
+/* Bytes of scratch device memory one spec_verify call with these sizes
+ * needs. Returns 0 for invalid sizes. */
+size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int32_t dtype);
+
+/*
+ * Verify B drafted continuations.
+ *
+ *   target_logits [B, k+1, V] row-major, dtype. Row i of sequence b scores
+ *                 draft position i; row L_b is the bonus position. Rows
+ *                 beyond L_b are never read.
+ *   draft_logits  [B, k, V] row-major, dtype. Only rows i < L_b of sampling
+ *                 sequences are read (greedy sequences never read it).
+ *                 May be NULL when k == 0.
+ *   dtype         SPEC_F32 or SPEC_BF16.
+ *   draft_tokens  [B, k] int32. Entries at i >= L_b are ignored. May be NULL
+ *                 when k == 0.
+ *   draft_len     [B] int32, L_b in [0, k]; NULL means every L_b = k.
+ *   temperature   [B] fp32; 0 selects the greedy rule for that sequence.
+ *   B, k, V       B >= 0 (B == 0 does nothing), 0 <= k <= SPEC_MAX_K,
+ *                 1 <= V < 2^31.
+ *   seed          Philox key (see above).
+ *   seq_base      global index of sequence 0 for the Philox counter.
+ *   out_tokens    [B, k+1] int32 out: g_0..g_{n-1}, then the correction or
+ *                 bonus token at position n, then -1 up to position k.
+ *   num_accepted  [B] int32 out: n in [0, L_b]; the round emits n+1 tokens.
+ *   aux           NULL, or optional diagnostics (see spec_verify_aux_t).
+ *   workspace     device scratch of at least spec_verify_workspace_size()
+ *                 bytes, 256-byte aligned; its contents need no
+ *                 initialisation and are clobbered.
+ *   stream        hipStream_t (NULL = default stream).
+ *
+ * Logit pointers must be aligned to their element size; int32 and fp32
+ * arrays to 4 bytes. Returns SPEC_OK once all work is enqueued.
+ */
+int spec_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
+                const int32_t *draft_tokens, const int32_t *draft_len,
+                const float *temperature, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
+                const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Static, human-readable text for a spec_status_t value. */
+const char *spec_verify_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,208 @@
+"""GPU-versus-oracle parity protocol (test infrastructure).
+
+Compares the outputs of the HIP library with the fp64 oracle on the same
+inputs, sequence by sequence:
+
+* status codes must match (a draft probability that underflows fp32 is the
+  one documented exception: the GPU reports QZERO where the oracle's exact
+  q(g) is positive but below FLT_MIN);
+* greedy sequences: argmax rows, tokens and counts bit-exact;
+* sampling sequences: p_i(g_i) and q_i(g_i) within ``rel`` (plus an absolute
+  floor for fp32 underflow), and every accept decision and the final token
+  bit-exact, except where the oracle's uniform lies within ``band`` of its
+  decision threshold or CDF boundary. The first such draw of a sequence
+  ends the comparison of that sequence (a flip there cascades) and is
+  counted as flagged. The residual mass S is compared wherever the final
+  draw is compared.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import DRAW_GREEDY, SEQ_OK, SEQ_QZERO, spec_verify_ref
+
+FLT_MIN = float(np.finfo(np.float32).tiny)
+
+
+def host_threads(cap: int = 16) -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def oracle_on(host: dict, seed: int, seqs=None, nthreads: int = 1) -> dict:
+    """Run the oracle on all sequences, or on the listed ones (each with its
+    own global index as the Philox sequence index)."""
+    t, d, g, L, tau = (host["target"], host["draft"], host["draft_tokens"], host["draft_len"],
+                       host["temperature"])
+    if seqs is None:
+        return spec_verify_ref(t, d, g, L, tau, seed, seq_base=0, nthreads=nthreads)
+    seqs = [int(b) for b in seqs]
+
+    def one(b):
+        return spec_verify_ref(t[b:b + 1], d[b:b + 1], g[b:b + 1], L[b:b + 1], tau[b:b + 1], seed,
+                               seq_base=b)
+
+    if nthreads > 1:
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            parts = list(ex.map(one, seqs))
+    else:
+        parts = [one(b) for b in seqs]
+    return {key: np.concatenate([p[key] for p in parts]) for key in parts[0]}
+
+
+@dataclass
+class Report:
+    """Counts over compared draws. A draw is one acceptance test or one final
+    (correction/bonus) draw. ``flagged`` counts draws whose oracle margin is
+    below the band; ``flagged_disagree`` those of them where the GPU took the
+    other branch/token (allowed); ``mismatches`` lists disagreements outside
+    the band (never allowed) and value/status errors."""
+
+    sequences: int = 0
+    draws: int = 0
+    flagged: int = 0
+    flagged_disagree: int = 0
+    boundary_status: int = 0
+    compared_tokens: int = 0
+    max_disagree_margin: float = 0.0
+    band_counts: dict = field(default_factory=dict)
+    mismatches: list = field(default_factory=list)
+
+    def merge(self, other: "Report") -> "Report":
+        self.sequences += other.sequences
+        self.draws += other.draws
+        self.flagged += other.flagged
+        self.flagged_disagree += other.flagged_disagree
+        self.boundary_status += other.boundary_status
+        self.compared_tokens += other.compared_tokens
+        self.max_disagree_margin = max(self.max_disagree_margin, other.max_disagree_margin)
+        for key, v in other.band_counts.items():
+            self.band_counts[key] = self.band_counts.get(key, 0) + v
+        self.mismatches += other.mismatches
+        return self
+
+    @property
+    def flagged_fraction(self) -> float:
+        return self.flagged / max(1, self.draws)
+
+    def ok(self) -> bool:
+        return not self.mismatches
+
+    def summary(self) -> str:
+        bands = " ".join(f"<{b:g}:{n}" for b, n in sorted(self.band_counts.items(), reverse=True))
+        head = (f"sequences={self.sequences} draws={self.draws} flagged={self.flagged} "
+                f"({self.flagged_fraction:.2e}) flagged_disagree={self.flagged_disagree} "
+                f"max_disagree_margin={self.max_disagree_margin:.2e} margins[{bands}] "
+                f"boundary_status={self.boundary_status} mismatches={len(self.mismatches)}")
+        return head + ("" if not self.mismatches else "\n  " + "\n  ".join(self.mismatches[:20]))
+
+
+BANDS = (1e-6, 1e-7, 1e-8, 1e-9)
+
+
+def _close(a: float, b: float, rel: float, floor: float) -> bool:
+    if np.isnan(a) and np.isnan(b):
+        return True
+    return abs(a - b) <= rel * abs(b) + floor
+
+
+def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel: float = 1e-5,
+            floor: float = 1e-30, band: float = 1e-6, label: str = "") -> Report:
+    """Compare GPU outputs (numpy, for the sequences in ``rows`` of the GPU
+    batch, or all) with oracle outputs for the same sequences."""
+    rep = Report(band_counts={b: 0 for b in BANDS})
+    n_ref = ref["num_accepted"].shape[0]
+    rows = list(range(n_ref)) if rows is None else [int(r) for r in rows]
+
+    def draw(margin: float, agree: bool, what: str) -> bool:
+        """Account one draw; returns False when the comparison must stop."""
+        rep.draws += 1
+        for b_ in BANDS:
+            if margin < b_:
+                rep.band_counts[b_] += 1
+        if margin < band:
+            rep.flagged += 1
+            if not agree:
+                rep.flagged_disagree += 1
+                rep.max_disagree_margin = max(rep.max_disagree_margin, margin)
+                return False
+            return True
+        if not agree:
+            rep.max_disagree_margin = max(rep.max_disagree_margin, margin)
+            rep.mismatches.append(what + f" (oracle margin {margin:.3e})")
+            return False
+        return True
+
+    for j, b in enumerate(rows):
+        rep.sequences += 1
+        tag = f"{label}b={b}"
+        L = int(draft_len[b])
+        tau = float(temperature[b])
+        gs, rs = int(gpu["seq_status"][b]), int(ref["seq_status"][j])
+        g_out, r_out = gpu["out_tokens"][b], ref["out_tokens"][j]
+        g_n, r_n = int(gpu["num_accepted"][b]), int(ref["num_accepted"][j])
+        if gs != rs:
+            qg = ref["q_g"][j]
+            if gs == SEQ_QZERO and rs == SEQ_OK and np.nanmin(qg[:max(L, 1)]) < FLT_MIN:
+                rep.boundary_status += 1
+                continue
+            rep.mismatches.append(f"{tag}: status gpu={gs} oracle={rs}")
+            continue
+        if gs != SEQ_OK:
+            if not (np.all(g_out == -1) and g_n == 0):
+                rep.mismatches.append(f"{tag}: error status {gs} but outputs not cleared")
+            continue
+        if tau == 0.0:
+            rep.draws += 1
+            if not np.array_equal(gpu["argmax"][b, :L + 1], ref["argmax"][j, :L + 1]):
+                rep.mismatches.append(f"{tag}: greedy argmax {gpu['argmax'][b, :L + 1]} vs "
+                                      f"{ref['argmax'][j, :L + 1]}")
+            if g_n != r_n or not np.array_equal(g_out, r_out):
+                rep.mismatches.append(f"{tag}: greedy tokens {g_out}/{g_n} vs {r_out}/{r_n}")
+            if int(gpu["draw_kind"][b]) != DRAW_GREEDY:
+                rep.mismatches.append(f"{tag}: greedy draw_kind {gpu['draw_kind'][b]}")
+            rep.compared_tokens += r_n + 1
+            continue
+        # sampling: gathered probabilities at every valid position
+        for i in range(L):
+            for key in ("p_g", "q_g"):
+                a, o = float(gpu[key][b, i]), float(ref[key][j, i])
+                if not _close(a, o, rel, floor):
+                    rep.mismatches.append(f"{tag}: {key}[{i}] gpu={a!r} oracle={o!r} "
+                                          f"rel={abs(a - o) / max(abs(o), 1e-300):.2e}")
+        # acceptance tests, left to right, until the two sides part
+        going = True
+        for i in range(min(r_n + 1, L)):
+            ref_acc = i < r_n
+            gpu_acc = g_n > i
+            if not draw(float(ref["margin_accept"][j, i]), ref_acc == gpu_acc,
+                        f"{tag}: accept test {i}: gpu {gpu_acc} oracle {ref_acc}"):
+                going = False
+                break
+            if ref_acc:
+                rep.compared_tokens += 1
+                if g_out[i] != r_out[i]:
+                    rep.mismatches.append(f"{tag}: accepted token {i}: {g_out[i]} vs {r_out[i]}")
+        if not going:
+            continue
+        if g_n != r_n:
+            rep.mismatches.append(f"{tag}: accepted count {g_n} vs {r_n}")
+            continue
+        if int(gpu["draw_kind"][b]) != int(ref["draw_kind"][j]):
+            rep.mismatches.append(f"{tag}: draw kind {gpu['draw_kind'][b]} vs {ref['draw_kind'][j]}")
+        S_g, S_r = float(gpu["resid_mass"][b]), float(ref["resid_mass"][j])
+        if not _close(S_g, S_r, rel, floor):
+            rep.mismatches.append(f"{tag}: resid_mass gpu={S_g!r} oracle={S_r!r}")
+        if not np.array_equal(g_out[r_n + 1:], r_out[r_n + 1:]):
+            rep.mismatches.append(f"{tag}: padding {g_out} vs {r_out}")
+        if draw(float(ref["margin_draw"][j]), g_out[r_n] == r_out[r_n],
+                f"{tag}: final token {g_out[r_n]} vs {r_out[r_n]}"):
+            rep.compared_tokens += 1
+    return rep
