@@ -106,7 +106,7 @@ typedef struct {
     int32_t *draw_row;   /* [B]: row of the last emitted token (= num_accepted), -1 on error */
     int32_t *draw_kind;  /* [B]: SPEC_DRAW_*                                               */
     void *event_begin;   /* hipEvent_t or NULL: recorded on `stream` right before the     */
-    void *event_end;     /* row-statistics kernel, and right after it                      */
+    void *event_end;     /* main verification kernel, and right after it                   */
 } spec_verify_aux_t;
 
 /* Bytes of scratch device memory one spec_verify call with these sizes
