@@ -64,7 +64,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kChunkBytes = 32768;  // one row-statistics item
 constexpr int kTiles = 8;           // 16-byte vectors per thread per chunk
 constexpr int kLagDecide = 32;      // target-row-0 items of sequence b decide b - kLagDecide
-constexpr int kLagSum = 64;         // ... and sum one draw chunk of b - kLagSum
+constexpr int kLagSum = 80;         // ... and sum one draw chunk of b - kLagSum
 constexpr int kMaxLdsChunks = 256;  // chunk sums staged in LDS by the locate
 constexpr int kFoldBatch = 8;       // partial loads in flight per lane when folding
 constexpr int kDeviceVersion = 200;  // 0.2.0
@@ -301,14 +301,12 @@ struct __align__(16) Decision {
 struct __align__(16) SeqState {
     int32_t rows_done;  // row-statistics chunks finished
     int32_t flag;       // see below
-    int32_t sums_done;  // draw-weight chunks finished
-    int32_t unused;
+    int32_t unused0, unused1;
 };
 // Life of a sequence: kPending (row statistics running) -> kReady (every
-// partial published) -> kDeciding (one workgroup took the decision) ->
-// kDraw (decision published, draw-weight chunks to sum) or kDone (greedy,
-// error) -> kSummed (every chunk summed, locate pending) -> kDone.
-enum { kPending = 0, kReady = 1, kDeciding = 2, kDraw = 3, kSummed = 4, kDone = 5 };
+// partial published) -> kDraw (decision published; draw-weight chunks to
+// sum, then the locate) or kDone (greedy or error: finished).
+enum { kPending = 0, kReady = 1, kDraw = 2, kDone = 3 };
 
 struct AuxDev {
     float *p_g, *q_g, *resid_mass;
@@ -326,7 +324,7 @@ struct Params {
     Decision *decisions;  // [B]
     double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the drawn row
     SeqState *state;      // [B]
-    int32_t *chunk_claim; // [B][nc]: draw-weight chunk taken (0 / 1)
+    int32_t *chunk_claim; // [B][nc]: draw-weight chunk summed (0 / 1)
     int32_t *out_tokens, *num_accepted;
     AuxDev aux;
 };
@@ -361,11 +359,7 @@ __device__ inline void flag_store(int32_t *ptr, int32_t v)
 {
     __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline bool flag_swap(int32_t *ptr, int32_t expect, int32_t want)
-{
-    return __hip_atomic_compare_exchange_strong(ptr, &expect, want, __ATOMIC_RELAXED,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+
 
 __device__ inline void publish_pair(void *ptr, uint32_t lo, uint32_t hi)
 {
@@ -942,15 +936,51 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, const Decisio
     // Segment totals go to LDS: sh.wd[wave][u] for the tiles, sh.ht for
     // head (0) and tail (1).
     int last = -1;
+    if (sp.vec) {
+        // all of the chunk's 16-byte loads in flight at once
+        const u32x4 *vt = reinterpret_cast<const u32x4 *>(r.t + sp.a);
+        const u32x4 *vd = reinterpret_cast<const u32x4 *>(r.d + sp.a);
+        u32x4 lt[kTiles], ld[kTiles];
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            const int64_t gi = (int64_t)u * kThreads + tid;
+            const bool in = gi < sp.ngroups;
+            lt[u] = in ? vt[gi] : u32x4{0u, 0u, 0u, 0u};
+            ld[u] = in && r.resid ? vd[gi] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            const int64_t gi = (int64_t)u * kThreads + tid;
+            float sel = 0.f;
+            if (gi < sp.ngroups) {
+                float ft[D::kVec], fd[D::kVec], w[D::kVec];
+                D::unpack(lt[u], ft);
+                D::unpack(ld[u], fd);
+#pragma unroll
+                for (int j = 0; j < D::kVec; ++j) {
+                    const Weights x = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd,
+                                                   r.resid);
+                    w[j] = use_p ? x.p : x.w;
+                    if (w[j] > 0.f)
+                        last = (int)(sp.a + gi * D::kVec + j);
+                }
+                sel = pairwise(w);
+            }
+            const double v = wave_sum((double)sel);
+            if (lane == 0)
+                sh.wd[wave][u] = v;
+        }
+    } else {
 #pragma unroll 1
-    for (int u = 0; u < kTiles; ++u) {
-        float gw = 0.f, gp = 0.f;
-        const int64_t gi = (int64_t)u * kThreads + tid;
-        if (gi < sp.ngroups)
-            group_weight_sums<D>(r, sp, gi, dec, use_p, gw, gp, last);
-        const double v = wave_sum((double)(use_p ? gp : gw));
-        if (lane == 0)
-            sh.wd[wave][u] = v;
+        for (int u = 0; u < kTiles; ++u) {
+            float gw = 0.f, gp = 0.f;
+            const int64_t gi = (int64_t)u * kThreads + tid;
+            if (gi < sp.ngroups)
+                group_weight_sums<D>(r, sp, gi, dec, use_p, gw, gp, last);
+            const double v = wave_sum((double)(use_p ? gp : gw));
+            if (lane == 0)
+                sh.wd[wave][u] = v;
+        }
     }
     double hv = 0.0, tv = 0.0;
     if (sp.s + tid < sp.a) {
@@ -1058,18 +1088,23 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, const Decisio
 }
 
 // ===========================================================================
-// Sum draw-weight chunk c of sequence h, if the sequence is waiting for its
-// sums and nobody has taken that chunk. The workgroup that finishes the
-// last chunk marks the sequence kSummed.
+// Sum draw-weight chunk c of sequence h if its decision is published and
+// the chunk is not summed yet, then mark it summed. Each chunk has exactly
+// one designated workgroup in k_verify and one in k_finish_sums, which runs
+// after k_verify, so a chunk is never summed twice and nothing needs a
+// claim or a completion count: the launch boundary orders the marks.
 // ===========================================================================
 template <class D>
 __device__ __forceinline__ void sum_chunk(const Params &p, int64_t h, int c, Shared &sh)
 {
     const int tid = threadIdx.x;
-    SeqState *st = p.state + h;
+    int32_t *mark = p.chunk_claim + h * (int64_t)p.nc + c;
     if (tid == 0) {
-        int32_t *claim = p.chunk_claim + h * (int64_t)p.nc + c;
-        sh.i0 = flag_load(&st->flag) == kDraw && flag_load(claim) == 0 && flag_swap(claim, 0, 1);
+        // The decision is read only after the flag says it is published
+        // (two device-scope loads from one thread are not ordered).
+        const int f = flag_load(&p.state[h].flag);
+        const int m = flag_load(mark);
+        sh.i0 = f == kDraw && m == 0;
         if (sh.i0)
             sh.dec = fetch_decision(p.decisions + h);
     }
@@ -1078,23 +1113,20 @@ __device__ __forceinline__ void sum_chunk(const Params &p, int64_t h, int c, Sha
         return;
     const Decision dec = sh.dec;
     chunk_weight_sums<D>(p, h, c, dec, sh);
-    if (tid == 0) {
-        drain_stores();  // chunk sums published before the count
-        if (counter_add(&st->sums_done, 1) == p.nc - 1)
-            flag_store(&st->flag, kSummed);
-    }
+    if (tid == 0)
+        flag_store(mark, 1);
     __syncthreads();
 }
 
-// Take the decision of sequence h if it is ready and nobody has taken it.
+// Take the decision of sequence h if it is ready. Each sequence has one
+// designated decider in k_verify and one in k_finish_decide, which runs
+// after it, so no claim is needed.
 template <class D>
 __device__ __forceinline__ void try_decide(const Params &p, int64_t h, Shared &sh)
 {
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        int32_t *flag = &p.state[h].flag;
-        sh.i1 = flag_load(flag) == kReady && flag_swap(flag, kReady, kDeciding);
-    }
+    if (tid == 0)
+        sh.i1 = flag_load(&p.state[h].flag) == kReady;
     __syncthreads();
     if (!sh.i1)
         return;
@@ -1226,11 +1258,11 @@ __global__ __launch_bounds__(kThreads) void k_finish_locate(Params p)
     const int64_t b = blockIdx.x;
     if (threadIdx.x == 0) {
         sh.flag = flag_load(&p.state[b].flag);
-        if (sh.flag == kSummed)
+        if (sh.flag == kDraw)
             sh.dec = fetch_decision(p.decisions + b);
     }
     __syncthreads();
-    if (sh.flag == kSummed) {
+    if (sh.flag == kDraw) {
         const Decision dec = sh.dec;
         locate<D>(p, b, dec, sh);
     }
