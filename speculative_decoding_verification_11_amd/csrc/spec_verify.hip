@@ -13,39 +13,38 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Launches per call, all stream-ordered, no host synchronisation:
+// Four launches per call, stream-ordered, no host synchronisation. Every
+// hand-over between workgroups crosses a launch boundary, so no workgroup
+// ever waits for another and nothing needs device-scope atomics:
 //
-//   k_reset          zeroes the per-sequence counters and chunk claims.
-//   k_verify         one workgroup per 32 KiB chunk of every logit row the
-//                    step needs (b-major). Each streams its chunk once with
-//                    16-byte loads and publishes an 8-byte partial: (max
-//                    logit, sum 2^((x - max) * log2(e)/tau)) for sampling
-//                    rows, (max logit, lowest index of it) for greedy rows.
-//                    These items carry ~all of the HBM traffic. The item that
-//                    completes a sequence only marks it ready. The items of
-//                    target row 0 then, by a fixed rule, take the decision
-//                    of an earlier sequence (fold the partials in chunk
-//                    order, gather p_i(g_i) and q_i(g_i), draw Philox, run
-//                    the left-to-right test, write the accepted prefix,
-//                    publish row j, kind and uniform v) and sum, in fp64,
-//                    one chunk of the draw weights w = max(0, p_j - q_j) (or
-//                    p_L for a bonus) of a still earlier sequence, whose rows
-//                    are still in the last-level cache.
-//   k_finish_decide  decisions nobody took during k_verify (the last
-//                    sequences, which have no later rows to help them);
-//   k_finish_sums    draw-weight chunks nobody summed;
-//   k_finish_locate  every sequence's token: the chunk where the cumulative
-//                    weight passes v * S, then the 2048-element tile, then
-//                    the lane, then the element, with coalesced loads and
-//                    fp64 block scans.
+//   k_rowstats  one workgroup per 32 KiB chunk of every logit row the step
+//               needs (b-major). Each streams its chunk once with 16-byte
+//               loads and stores an 8-byte partial: (max logit, sum
+//               2^((x - max) * log2(e)/tau)) for sampling rows, (max logit,
+//               lowest index of it) for greedy rows. This kernel carries
+//               all of the algorithmic HBM traffic and runs at copy speed.
+//   k_decide    one wave per sequence: fold the partials in chunk order,
+//               gather p_i(g_i) and q_i(g_i), draw Philox, run the
+//               left-to-right test, write the accepted prefix, and record
+//               the draw row j, its kind, the uniform v and the normalisers.
+//   k_draw      one workgroup per chunk of each sequence's draw row: fp64
+//               sum of the draw weights w = max(0, p_j - q_j) (or p_L for a
+//               bonus) over the chunk.
+//   k_locate    one workgroup per sequence: the chunk where the cumulative
+//               weight passes v * S, then the 2048-element tile, the group
+//               and the element, from one coalesced read of that chunk and
+//               fp64 block scans.
 //
-// Work is assigned statically, never to "whoever arrives first or last":
-// workgroup i runs on XCD i % 8, and any timing-driven hand-off would give
-// the work to whichever XCD lags and make it lag further.
+// k_draw re-reads the one or two draw rows of each sequence (about a fifth
+// of the bytes k_rowstats reads). Doing those sums inside k_rowstats while
+// the rows are still in the last-level cache was measured to cost more than
+// re-reading them afterwards: the sums wait on decisions, and the waiting
+// workgroups hold slots the streaming needs. Folding the locate into k_draw
+// (last workgroup of a sequence) costs more than its own launch: its
+// registers halve the occupancy of the latency-bound sums.
 //
 // Nothing here is a dense contraction, so there is no MFMA: the step is bound
-// by HBM bandwidth. No workgroup ever waits for another: work that is not
-// ready is left to the finishing launches.
+// by HBM bandwidth.
 
 #include <hip/hip_runtime.h>
 
@@ -63,11 +62,14 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunkBytes = 32768;  // one row-statistics item
 constexpr int kTiles = 8;           // 16-byte vectors per thread per chunk
-constexpr int kLagDecide = 32;      // target-row-0 items of sequence b decide b - kLagDecide
-constexpr int kLagSum = 80;         // ... and sum one draw chunk of b - kLagSum
-constexpr int kMaxLdsChunks = 256;  // chunk sums staged in LDS by the locate
+constexpr int kMaxLdsChunks = 256;  // chunk masses staged in LDS by the locate
+// Draw-weight segments of a chunk, in element order: the scalar head, then
+// one segment per (tile, wave) -- the 512 consecutive elements one wave
+// reads in one tile -- tile-major, then the scalar tail.
+constexpr int kSegs = kTiles * kWaves + 2;
+constexpr int kTrStride = 68;       // LDS row of 64 lanes, skewed across banks
 constexpr int kFoldBatch = 8;       // partial loads in flight per lane when folding
-constexpr int kDeviceVersion = 200;  // 0.2.0
+constexpr int kDeviceVersion = 300;  // 0.3.0
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 
@@ -297,17 +299,6 @@ struct __align__(16) Decision {
     float md, zd;  // draft row (residual draws only)
 };
 
-// Per-sequence synchronisation, zeroed by k_reset at the start of each call.
-struct __align__(16) SeqState {
-    int32_t rows_done;  // row-statistics chunks finished
-    int32_t flag;       // see below
-    int32_t unused0, unused1;
-};
-// Life of a sequence: kPending (row statistics running) -> kReady (every
-// partial published) -> kDraw (decision published; draw-weight chunks to
-// sum, then the locate) or kDone (greedy or error: finished).
-enum { kPending = 0, kReady = 1, kDraw = 2, kDone = 3 };
-
 struct AuxDev {
     float *p_g, *q_g, *resid_mass;
     int32_t *argmax, *seq_status, *draw_row, *draw_kind;
@@ -320,97 +311,24 @@ struct Params {
     int32_t k, V, nc, B;
     uint32_t key0, key1, seq_base;
     int64_t n_row_items;  // B * (2k+1) * nc
-    float2 *partials;     // [B][2k+1][nc]
-    Decision *decisions;  // [B]
-    double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the drawn row
-    SeqState *state;      // [B]
-    int32_t *chunk_claim; // [B][nc]: draw-weight chunk summed (0 / 1)
+    float2 *partials;     // [B][2k+1][nc], written by k_rowstats
+    Decision *decisions;  // [B], written by k_decide
+    double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the draw row
+    double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
     int32_t *out_tokens, *num_accepted;
     AuxDev aux;
 };
 
-// Cross-workgroup exchange. Published values are written with device-scope
-// (write-through) stores and read with device-scope loads, so no L2
-// write-back or invalidate is ever needed; a writer drains its stores
-// (s_waitcnt) before the relaxed device-scope counter or flag update that
-// tells readers to look. Agent-scope release/acquire would instead write
-// back / invalidate the whole L2 on every item, which costs more than the
-// streaming itself on this part.
-__device__ inline void publish64(void *ptr, uint64_t v)
-{
-    __hip_atomic_store(static_cast<uint64_t *>(ptr), v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t fetch64(const void *ptr)
-{
-    return __hip_atomic_load(static_cast<const uint64_t *>(ptr), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ inline int counter_add(int32_t *ptr, int32_t v)
-{
-    return __hip_atomic_fetch_add(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int flag_load(const int32_t *ptr)
-{
-    return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void flag_store(int32_t *ptr, int32_t v)
-{
-    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-
-__device__ inline void publish_pair(void *ptr, uint32_t lo, uint32_t hi)
-{
-    publish64(ptr, (uint64_t)lo | ((uint64_t)hi << 32));
-}
-__device__ inline float2 fetch_float2(const float2 *ptr)
-{
-    const uint64_t v = fetch64(ptr);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-__device__ inline double fetch_double(const double *ptr)
-{
-    return __longlong_as_double((long long)fetch64(ptr));
-}
-__device__ inline void publish_double(double *ptr, double v)
-{
-    publish64(ptr, (uint64_t)__double_as_longlong(v));
-}
-
-__device__ inline void publish_decision(Decision *dst, const Decision &d)
-{
-    publish_pair(reinterpret_cast<char *>(dst) + 0, (uint32_t)d.row, (uint32_t)d.kind);
-    publish_pair(reinterpret_cast<char *>(dst) + 8, __float_as_uint(d.v), __float_as_uint(d.scale));
-    publish_pair(reinterpret_cast<char *>(dst) + 16, __float_as_uint(d.mt), __float_as_uint(d.zt));
-    publish_pair(reinterpret_cast<char *>(dst) + 24, __float_as_uint(d.md), __float_as_uint(d.zd));
-}
-__device__ inline Decision fetch_decision(const Decision *src)
-{
-    const char *c = reinterpret_cast<const char *>(src);
-    const uint64_t a = fetch64(c), b = fetch64(c + 8), x = fetch64(c + 16), y = fetch64(c + 24);
-    Decision d;
-    d.row = (int32_t)(uint32_t)a;
-    d.kind = (int32_t)(uint32_t)(a >> 32);
-    d.v = __uint_as_float((uint32_t)b);
-    d.scale = __uint_as_float((uint32_t)(b >> 32));
-    d.mt = __uint_as_float((uint32_t)x);
-    d.zt = __uint_as_float((uint32_t)(x >> 32));
-    d.md = __uint_as_float((uint32_t)y);
-    d.zd = __uint_as_float((uint32_t)(y >> 32));
-    return d;
-}
-
-// LDS shared by the phases of k_verify (one phase at a time).
-struct Shared {
+// LDS of the kernels.
+struct RowShared {
     float a[kWaves], b[kWaves];
-    double wd[kWaves][kTiles], pd[kWaves], ht[2][kWaves];
-    double cm[kMaxLdsChunks];
-    Decision dec;
-    int i0, i1;
-    int flag;
-    int tok;
+};
+struct DrawShared {
+    float tr[kWaves][2 * kTiles][kTrStride];  // per-lane group sums, transposed
+    double seg[2][kSegs];                       // segment sums of w and p
+};
+struct LocateShared {
+    double cm[kMaxLdsChunks];  // chunk masses (w, p) of one sequence
 };
 
 // ===========================================================================
@@ -418,7 +336,7 @@ struct Shared {
 // ===========================================================================
 template <class D>
 __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64_t s, int64_t e, bool greedy,
-                              float scale, Shared &sh)
+                              float scale, RowShared &sh)
 {
     constexpr int NX = kTiles * D::kVec;
     const Span sp = make_span<D>(row, s, e);
@@ -515,16 +433,13 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
 }
 
 // ===========================================================================
-// Decision of one sequence (wave 0 of the deciding workgroup). Fills
-// sh.dec; writes the accepted prefix, num_accepted and diagnostics.
+// Decision of one sequence (one wave; `lane` in [0, 64)). Writes the
+// accepted prefix, num_accepted, diagnostics and the decision record.
 // ===========================================================================
 template <class D>
-__device__ __forceinline__ void decide(const Params &p, int64_t b, Shared &sh)
+__device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
 {
     using E = typename D::Elem;
-    const int lane = threadIdx.x;
-    if (lane >= kWave)
-        return;
     const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
     const E *target = static_cast<const E *>(p.target);
     const E *draft = static_cast<const E *>(p.draft);
@@ -560,7 +475,7 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, Shared &sh)
                 float2 t[kFoldBatch];
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? fetch_float2(pp + c0 + q)
+                    t[q] = c0 + q < nc ? pp[c0 + q]
                                        : make_float2(-INFINITY, __int_as_float(INT32_MAX));
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
@@ -586,7 +501,7 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, Shared &sh)
                 float2 t[kFoldBatch];
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? fetch_float2(pp + c0 + q) : make_float2(-INFINITY, 0.f);
+                    t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
                     ts = soft_merge(ts, Soft{t[q].x, t[q].y}, scale);
@@ -598,7 +513,7 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, Shared &sh)
                 float2 t[kFoldBatch];
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? fetch_float2(pp + c0 + q) : make_float2(-INFINITY, 0.f);
+                    t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
                     ds = soft_merge(ds, Soft{t[q].x, t[q].y}, scale);
@@ -651,13 +566,11 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, Shared &sh)
     if (aux.argmax && lane <= k)
         aux.argmax[b * (k + 1) + lane] = (lane <= L) ? amax : -1;
     if (lane == 0) {
-        publish_decision(p.decisions + b, dec);
-        sh.dec = dec;
+        p.decisions[b] = dec;
         if (aux.seq_status) aux.seq_status[b] = status;
         if (aux.draw_row) aux.draw_row[b] = dec.row;
-        // Each output address has exactly one writer (L2s of different XCDs
-        // write back independently): for a residual or bonus draw the
-        // locating workgroup owns draw_kind and resid_mass.
+        // For a residual or bonus draw the locating workgroup of k_draw
+        // writes draw_kind and resid_mass.
         if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS) {
             if (aux.draw_kind) aux.draw_kind[b] = dec.kind;
             if (aux.resid_mass) aux.resid_mass[b] = NAN;
@@ -749,22 +662,22 @@ __device__ inline void group_weight_sums(const DrawRows<D> &r, const Span &sp, i
 }
 
 // ===========================================================================
-// fp64 sums of the draw weights over one chunk of the decided row.
+// Sums of the draw weights over one chunk of the decided row: per segment
+// (fp64 sums of the fp32 pairwise group sums) and over the chunk, for w and
+// for p. The locate reads these instead of the chunk.
 // ===========================================================================
 template <class D>
-__device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, int c, const Decision &dec,
-                                  Shared &sh)
+__device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, int c,
+                                                  const Decision &dec, DrawShared &sh)
 {
     constexpr int64_t CH = chunk_elems<D>();
     const DrawRows<D> r = draw_rows<D>(p, b, dec);
     const int64_t s = (int64_t)c * CH, e = min64((int64_t)p.V, s + CH);
     const Span sp = make_span2<D>(r.t, r.d, s, e);
-    const int tid = threadIdx.x;
-    double aw = 0.0, ap = 0.0;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    float gw[kTiles], gp[kTiles];  // this lane's group sums, tile by tile
     if (sp.vec) {
-        // kBatch 16-byte loads per row in flight before their arithmetic,
-        // then one group of arithmetic at a time (the fp64 sums are one
-        // dependent chain; unfenced, the scheduler hoists every weight)
+        // kBatch 16-byte loads per row in flight before their arithmetic
         constexpr int kBatch = kTiles / 2;
         const u32x4 *vt = reinterpret_cast<const u32x4 *>(r.t + sp.a);
         const u32x4 *vd = reinterpret_cast<const u32x4 *>(r.d + sp.a);
@@ -780,409 +693,258 @@ __device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, in
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                if ((int64_t)(h + u) * kThreads + tid < sp.ngroups) {
-                    float ft[D::kVec], fd[D::kVec], w[D::kVec], pw[D::kVec];
-                    D::unpack(lt[u], ft);
-                    D::unpack(ld[u], fd);
+                float ft[D::kVec], fd[D::kVec], w[D::kVec], pw[D::kVec];
+                D::unpack(lt[u], ft);
+                D::unpack(ld[u], fd);
 #pragma unroll
-                    for (int j = 0; j < D::kVec; ++j) {
-                        const Weights x = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd,
-                                                       r.resid);
-                        w[j] = x.w;
-                        pw[j] = x.p;
-                    }
-                    aw += (double)pairwise(w);
-                    ap += (double)pairwise(pw);
+                for (int j = 0; j < D::kVec; ++j) {
+                    const Weights x = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd, r.resid);
+                    w[j] = x.w;
+                    pw[j] = x.p;
                 }
+                const bool in = (int64_t)(h + u) * kThreads + tid < sp.ngroups;
+                gw[h + u] = in ? pairwise(w) : 0.f;
+                gp[h + u] = in ? pairwise(pw) : 0.f;
             }
         }
     } else {
         int unused = -1;
-        for (int64_t gi = tid; gi < sp.ngroups; gi += kThreads) {
-            float gw, gp;
-            group_weight_sums<D>(r, sp, gi, dec, false, gw, gp, unused);
-            aw += (double)gw;
-            ap += (double)gp;
-        }
-    }
-    if (sp.s + tid < sp.a) {
-        const Weights x = elem_weight<D>(r, sp.s + tid, dec);
-        aw += (double)x.w;
-        ap += (double)x.p;
-    }
-    if (sp.z + tid < sp.e) {
-        const Weights x = elem_weight<D>(r, sp.z + tid, dec);
-        aw += (double)x.w;
-        ap += (double)x.p;
-    }
-    aw = wave_sum(aw);
-    ap = wave_sum(ap);
-    if ((tid & (kWave - 1)) == 0) {
-        sh.wd[tid / kWave][0] = aw;
-        sh.pd[tid / kWave] = ap;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        double w = 0.0, pp = 0.0;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            w += sh.wd[i][0];
-            pp += sh.pd[i];
+        for (int u = 0; u < kTiles; ++u) {
+            const int64_t gi = (int64_t)u * kThreads + tid;
+            gw[u] = gp[u] = 0.f;
+            if (gi < sp.ngroups)
+                group_weight_sums<D>(r, sp, gi, dec, false, gw[u], gp[u], unused);
         }
-        double *m = reinterpret_cast<double *>(p.masses + b * (int64_t)p.nc + c);
-        publish_double(m, w);
-        publish_double(m + 1, pp);
+    }
+    // Segment (tile u, this wave) = sum over the wave's 64 lanes. Transpose
+    // through LDS: row q * kTiles + u holds the 64 lanes' values; four lanes
+    // per row each add 16 of them (lane part, part + 4, ...), then combine.
+    float (*tr)[kTrStride] = sh.tr[wave];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+        tr[u][lane] = gw[u];
+        tr[kTiles + u][lane] = gp[u];
     }
     __syncthreads();
+    {
+        const int row = lane >> 2, part = lane & 3;
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < kWave / 4; ++i)
+            acc += (double)tr[row][part + 4 * i];
+        acc += __shfl_xor(acc, 1, kWave);
+        acc += __shfl_xor(acc, 2, kWave);
+        if (part == 0)
+            sh.seg[row / kTiles][1 + (row % kTiles) * kWaves + wave] = acc;
+    }
+    if (tid == 0) {  // head and tail: fewer than kVec elements each, in order
+        double hw = 0.0, hp = 0.0, tw = 0.0, tp = 0.0;
+        for (int64_t x = sp.s; x < sp.a; ++x) {
+            const Weights y = elem_weight<D>(r, x, dec);
+            hw += (double)y.w;
+            hp += (double)y.p;
+        }
+        for (int64_t x = sp.z; x < sp.e; ++x) {
+            const Weights y = elem_weight<D>(r, x, dec);
+            tw += (double)y.w;
+            tp += (double)y.p;
+        }
+        sh.seg[0][0] = hw;
+        sh.seg[1][0] = hp;
+        sh.seg[0][kSegs - 1] = tw;
+        sh.seg[1][kSegs - 1] = tp;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int64_t chunk = b * (int64_t)p.nc + c;
+        double *dst = p.segs + chunk * (2 * kSegs);
+        const double *src = &sh.seg[0][0];
+        for (int q = lane; q < 2 * kSegs; q += kWave)
+            dst[q] = src[q];
+        const double mw = wave_sum(lane < kSegs ? sh.seg[0][lane] : 0.0);
+        const double mp = wave_sum(lane < kSegs ? sh.seg[1][lane] : 0.0);
+        if (lane == 0)
+            p.masses[chunk] = make_double2(mw, mp);
+    }
 }
 
-// Inclusive prefix sum over the block (fixed order).
-__device__ inline double block_inclusive_scan(double v, Shared &sh)
+// Inclusive prefix sum over a wave (fixed order).
+__device__ inline double wave_inclusive_scan(double v, int lane)
 {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const double o = __shfl_up(v, off, kWave);
         if (lane >= off)
             v += o;
     }
-    if (lane == kWave - 1)
-        sh.pd[wave] = v;
-    __syncthreads();
-    double before = 0.0;
-    for (int w = 0; w < wave; ++w)
-        before += sh.pd[w];
-    __syncthreads();
-    return before + v;
+    return v;
 }
 
 // ===========================================================================
-// Inverse-CDF locate of one sequence's correction / bonus token.
+// Inverse-CDF locate of one sequence's correction / bonus token (one wave):
+// the smallest token x whose cumulative weight exceeds t = v * S, found
+// level by level -- the chunk (masses), the segment (segment sums), the
+// group of kVec tokens (one 16-byte load per lane), the token. The sums at
+// each level are those k_draw formed, so the levels agree up to fp64
+// rounding of the order of summation; where rounding leaves no crossing at
+// some level, the crossing is at the end of what that level covers, and the
+// locate takes the last token with weight there (also the rule when t
+// reaches S itself).
 // ===========================================================================
 template <class D>
-__device__ __forceinline__ void locate(const Params &p, int64_t b, const Decision &dec, Shared &sh)
+__device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, LocateShared &sh)
 {
     constexpr int64_t CH = chunk_elems<D>();
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nc = p.nc;
-    const double2 *mb = p.masses + b * (int64_t)nc;
+    const Decision dec = p.decisions[b];
+    if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
+        return;  // greedy or error: k_decide wrote everything
     const DrawRows<D> r = draw_rows<D>(p, b, dec);
-    int kind = dec.kind;
-
-    // The published chunk sums (device-scope loads, all in flight at once)
-    // go to LDS; thread 0 picks the chunk; the block shares its choice.
-    const double *mw = reinterpret_cast<const double *>(mb);  // (w, p) pairs
+    const double *mw = reinterpret_cast<const double *>(p.masses + b * (int64_t)nc);
     const bool staged = nc <= kMaxLdsChunks / 2;
     if (staged) {
-        for (int q = tid; q < 2 * nc; q += kThreads)
-            sh.cm[q] = fetch_double(mw + q);
+        for (int q = lane; q < 2 * nc; q += kWave)
+            sh.cm[q] = mw[q];
         __syncthreads();
     }
-    if (tid == 0) {
-        auto mass = [&](int q) { return staged ? sh.cm[q] : fetch_double(mw + q); };
-        double Sw = 0.0, Sp = 0.0;
-        for (int c = 0; c < nc; ++c) {
-            Sw += mass(2 * c);
-            Sp += mass(2 * c + 1);
+
+    // Chunk level (every lane runs the same scalar loop over LDS).
+    auto mass = [&](int q) { return staged ? sh.cm[q] : mw[q]; };
+    double Sw = 0.0, Sp = 0.0;
+    for (int c = 0; c < nc; ++c) {
+        Sw += mass(2 * c);
+        Sp += mass(2 * c + 1);
+    }
+    int kind = dec.kind;
+    bool use_p = !r.resid;
+    if (r.resid && !(Sw > 0.0)) {  // residual mass rounded away: draw from p
+        use_p = true;
+        kind = SPEC_DRAW_RESIDUAL_AS_P;
+    }
+    const int sel = use_p ? 1 : 0;
+    const double S = use_p ? Sp : Sw;
+    const double t = (double)dec.v * S;
+    double base = 0.0;
+    int cs = -1;
+    for (int c = 0; c < nc; ++c) {  // first chunk whose cumulative weight exceeds t
+        const double m = mass(2 * c + sel);
+        if (base + m > t) {
+            cs = c;
+            break;
         }
-        bool up = !r.resid;
-        int kd = dec.kind;
-        if (r.resid && !(Sw > 0.0)) {  // residual mass rounded away: draw from p
-            up = true;
-            kd = SPEC_DRAW_RESIDUAL_AS_P;
-        }
-        const double S_ = up ? Sp : Sw;
-        const double t_ = (double)dec.v * S_;
-        const int sel = up ? 1 : 0;
-        double cm = 0.0;
-        int c_star = -1;
-        for (int c = 0; c < nc; ++c) {  // first chunk whose cumulative weight exceeds t
-            const double m = mass(2 * c + sel);
-            if (cm + m > t_) {
-                c_star = c;
+        base += m;
+    }
+    bool fallback = cs < 0;
+    if (fallback) {  // no crossing: the last chunk with weight
+        cs = nc - 1;
+        for (int c = nc - 1; c >= 0; --c)
+            if (mass(2 * c + sel) > 0.0) {
+                cs = c;
                 break;
             }
-            cm += m;
-        }
-        const bool fb = c_star < 0;
-        if (fb) {  // rounding left no crossing: last chunk with weight
-            for (int c = nc - 1; c >= 0; --c)
-                if (mass(2 * c + sel) > 0.0) {
-                    c_star = c;
-                    break;
-                }
-            if (c_star < 0)
-                c_star = nc - 1;
-        }
-        sh.pd[0] = S_;
-        sh.pd[1] = t_;
-        sh.pd[2] = cm;
-        sh.i0 = c_star;
-        sh.i1 = (up ? 1 : 0) | (fb ? 2 : 0);
-        sh.flag = kd;
     }
-    __syncthreads();
-    const double S = sh.pd[0], t = sh.pd[1], cum = sh.pd[2];
-    const int cs = sh.i0;
-    const bool use_p = (sh.i1 & 1) != 0, fallback = (sh.i1 & 2) != 0;
-    kind = sh.flag;
-    __syncthreads();
-
     const int64_t s = (int64_t)cs * CH, e = min64((int64_t)p.V, s + CH);
     const Span sp = make_span2<D>(r.t, r.d, s, e);
 
-    // Element order inside the chunk: head [s, a), groups gi = 0..ngroups-1
-    // (tile u = gi / 256 holds lane tid at gi = u * 256 + tid), tail [z, e).
-    // Segment totals go to LDS: sh.wd[wave][u] for the tiles, sh.ht for
-    // head (0) and tail (1).
-    int last = -1;
-    if (sp.vec) {
-        // all of the chunk's 16-byte loads in flight at once
-        const u32x4 *vt = reinterpret_cast<const u32x4 *>(r.t + sp.a);
-        const u32x4 *vd = reinterpret_cast<const u32x4 *>(r.d + sp.a);
-        u32x4 lt[kTiles], ld[kTiles];
-#pragma unroll
-        for (int u = 0; u < kTiles; ++u) {
-            const int64_t gi = (int64_t)u * kThreads + tid;
-            const bool in = gi < sp.ngroups;
-            lt[u] = in ? vt[gi] : u32x4{0u, 0u, 0u, 0u};
-            ld[u] = in && r.resid ? vd[gi] : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < kTiles; ++u) {
-            const int64_t gi = (int64_t)u * kThreads + tid;
-            float sel = 0.f;
-            if (gi < sp.ngroups) {
-                float ft[D::kVec], fd[D::kVec], w[D::kVec];
-                D::unpack(lt[u], ft);
-                D::unpack(ld[u], fd);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j) {
-                    const Weights x = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd,
-                                                   r.resid);
-                    w[j] = use_p ? x.p : x.w;
-                    if (w[j] > 0.f)
-                        last = (int)(sp.a + gi * D::kVec + j);
-                }
-                sel = pairwise(w);
-            }
-            const double v = wave_sum((double)sel);
-            if (lane == 0)
-                sh.wd[wave][u] = v;
-        }
-    } else {
-#pragma unroll 1
-        for (int u = 0; u < kTiles; ++u) {
-            float gw = 0.f, gp = 0.f;
-            const int64_t gi = (int64_t)u * kThreads + tid;
-            if (gi < sp.ngroups)
-                group_weight_sums<D>(r, sp, gi, dec, use_p, gw, gp, last);
-            const double v = wave_sum((double)(use_p ? gp : gw));
-            if (lane == 0)
-                sh.wd[wave][u] = v;
-        }
-    }
-    double hv = 0.0, tv = 0.0;
-    if (sp.s + tid < sp.a) {
-        const Weights x = elem_weight<D>(r, sp.s + tid, dec);
-        hv = (double)(use_p ? x.p : x.w);
-        if (hv > 0.0)
-            last = max(last, (int)(sp.s + tid));
-    }
-    if (sp.z + tid < sp.e) {
-        const Weights x = elem_weight<D>(r, sp.z + tid, dec);
-        tv = (double)(use_p ? x.p : x.w);
-        if (tv > 0.0)
-            last = max(last, (int)(sp.z + tid));
-    }
-    hv = wave_sum(hv);
-    tv = wave_sum(tv);
-    if (lane == 0) {
-        sh.ht[0][wave] = hv;
-        sh.ht[1][wave] = tv;
-    }
-    if (tid == 0) {
-        sh.tok = -1;
-        sh.i1 = -1;
-        sh.i0 = kThreads;
-    }
-    __syncthreads();
-
-    // Which segment holds the crossing (same arithmetic on every thread):
-    // 0 = head, 1..kTiles = tiles, kTiles + 1 = tail.
-    int seg = -1;
-    double base = cum;
+    // Segment level: one segment sum per lane, scanned in order.
+    const double *segs = p.segs + (b * (int64_t)nc + cs) * (2 * kSegs) + sel * kSegs;
+    const double sv = lane < kSegs ? segs[lane] : 0.0;
+    const double sincl = wave_inclusive_scan(sv, lane);
+    int sg = -1;
     if (!fallback) {
-#pragma unroll 1
-        for (int u = 0; u < kTiles + 2; ++u) {
-            double tot = 0.0;
-            for (int w = 0; w < kWaves; ++w)
-                tot += u == 0 ? sh.ht[0][w] : (u == kTiles + 1 ? sh.ht[1][w] : sh.wd[w][u - 1]);
-            if (base + tot > t) {
-                seg = u;
-                break;
-            }
-            base += tot;
+        const uint64_t cross = __ballot(lane < kSegs && base + sincl > t);
+        if (cross) {
+            sg = __ffsll((unsigned long long)cross) - 1;
+            base += __shfl(sincl - sv, sg, kWave);
         }
     }
-    if (seg == 0 || seg == kTiles + 1) {
-        // head or tail: fewer than kVec elements, thread 0 walks them in order
-        if (tid == 0) {
-            const int64_t x0 = seg == 0 ? sp.s : sp.z, x1 = seg == 0 ? sp.a : sp.e;
-            double run = base;
-            for (int64_t x = x0; x < x1; ++x) {
-                const Weights wx = elem_weight<D>(r, x, dec);
-                run += (double)(use_p ? wx.p : wx.w);
-                if (run > t) {
-                    sh.tok = (int)x;
-                    break;
-                }
-            }
+    if (sg < 0) {  // no crossing: the last segment with weight
+        fallback = true;
+        const uint64_t pos = __ballot(lane < kSegs && sv > 0.0);
+        sg = pos ? 63 - __clzll((long long)pos) : 0;
+    }
+
+    int tok = -1;
+    if (sg == 0 || sg == kSegs - 1) {
+        // head or tail: fewer than kVec tokens, walked in order by every lane
+        const int64_t x0 = sg == 0 ? sp.s : sp.z, x1 = sg == 0 ? sp.a : sp.e;
+        double run = base;
+        int lastpos = -1;
+        for (int64_t x = x0; x < x1; ++x) {
+            const Weights y = elem_weight<D>(r, x, dec);
+            const float wx = use_p ? y.p : y.w;
+            run += (double)wx;
+            if (wx > 0.f)
+                lastpos = (int)x;
+            if (!fallback && tok < 0 && run > t)
+                tok = (int)x;
         }
-    } else if (seg > 0) {
-        const int64_t gi = (int64_t)(seg - 1) * kThreads + tid;
-        float gw = 0.f, gp = 0.f;
-        int unused = -1;
-        if (gi < sp.ngroups)
-            group_weight_sums<D>(r, sp, gi, dec, use_p, gw, gp, unused);
-        const double mine = (double)(use_p ? gp : gw);
-        const double incl = block_inclusive_scan(mine, sh);
-        if (base + incl > t)
-            atomicMin(&sh.i0, tid);
-        __syncthreads();
-        if (tid == sh.i0 && gi < sp.ngroups) {
-            float ft[D::kVec], fd[D::kVec];
+        if (tok < 0)
+            tok = lastpos;
+    } else {
+        // Segment (tile u, wave wv): lane l holds group u * 256 + wv * 64 + l.
+        const int u = (sg - 1) / kWaves, wv = (sg - 1) % kWaves;
+        const int64_t gi = (int64_t)u * kThreads + wv * kWave + lane;
+        const bool in = gi < sp.ngroups;
+        float ft[D::kVec], fd[D::kVec];
+#pragma unroll
+        for (int j = 0; j < D::kVec; ++j)
+            ft[j] = fd[j] = 0.f;
+        if (in) {
             load_group<D>(r.t, sp, gi, ft);
             if (r.resid)
                 load_group<D>(r.d, sp, gi, fd);
-            // Walk the group in id order. The group's total came from the
-            // pairwise sum; if rounding leaves the walk short of t, the
-            // crossing is still inside this group: take its last token
-            // with weight.
-            double run = base + (incl - mine);
-            int found = -1, lastpos = -1;
-            for (int j = 0; j < D::kVec; ++j) {
-                const Weights x = draw_weights(ft[j], r.resid ? fd[j] : 0.f, dec, r.inv_zt,
-                                               r.inv_zd, r.resid);
-                const float wj = use_p ? x.p : x.w;
-                run += (double)wj;
-                if (wj > 0.f)
-                    lastpos = (int)(sp.a + gi * D::kVec + j);
-                if (found < 0 && run > t)
-                    found = (int)(sp.a + gi * D::kVec + j);
-            }
-            sh.tok = found >= 0 ? found : lastpos;
         }
+        float w[D::kVec];
+#pragma unroll
+        for (int j = 0; j < D::kVec; ++j) {
+            const Weights y = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd, r.resid);
+            w[j] = in ? (use_p ? y.p : y.w) : 0.f;
+        }
+        const float gsum = pairwise(w);
+        const double gincl = wave_inclusive_scan((double)gsum, lane);
+        int gl = -1;
+        if (!fallback) {
+            const uint64_t cross = __ballot(base + gincl > t);
+            if (cross)
+                gl = __ffsll((unsigned long long)cross) - 1;
+        }
+        if (gl < 0) {  // no crossing: the last group with weight
+            fallback = true;
+            const uint64_t pos = __ballot(gsum > 0.f);
+            gl = pos ? 63 - __clzll((long long)pos) : 0;
+        }
+        // Lane gl walks its group in token order.
+        int found = -1, lastpos = -1;
+        double run = base + (gincl - (double)gsum);
+#pragma unroll
+        for (int j = 0; j < D::kVec; ++j) {
+            run += (double)w[j];
+            const int x = (int)(sp.a + gi * D::kVec + j);
+            if (w[j] > 0.f)
+                lastpos = x;
+            if (!fallback && found < 0 && run > t)
+                found = x;
+        }
+        tok = __shfl(found >= 0 ? found : lastpos, gl, kWave);
     }
-    // Rounding fallback: the last token with weight in the chunk.
-    if (last >= 0)
-        atomicMax(&sh.i1, last);
-    __syncthreads();
-    if (tid == 0) {
-        const int chosen = sh.tok >= 0 ? sh.tok : (sh.i1 >= 0 ? sh.i1 : (int)s);
-        p.out_tokens[b * (p.k + 1) + dec.row] = chosen;
+    if (lane == 0) {
+        p.out_tokens[b * (p.k + 1) + dec.row] = tok >= 0 ? tok : (int)s;
         if (p.aux.resid_mass) p.aux.resid_mass[b] = (float)S;
         if (p.aux.draw_kind) p.aux.draw_kind[b] = kind;
-    }
-    __syncthreads();
-}
-
-// ===========================================================================
-// Sum draw-weight chunk c of sequence h if its decision is published and
-// the chunk is not summed yet, then mark it summed. Each chunk has exactly
-// one designated workgroup in k_verify and one in k_finish_sums, which runs
-// after k_verify, so a chunk is never summed twice and nothing needs a
-// claim or a completion count: the launch boundary orders the marks.
-// ===========================================================================
-template <class D>
-__device__ __forceinline__ void sum_chunk(const Params &p, int64_t h, int c, Shared &sh)
-{
-    const int tid = threadIdx.x;
-    int32_t *mark = p.chunk_claim + h * (int64_t)p.nc + c;
-    if (tid == 0) {
-        // The decision is read only after the flag says it is published
-        // (two device-scope loads from one thread are not ordered).
-        const int f = flag_load(&p.state[h].flag);
-        const int m = flag_load(mark);
-        sh.i0 = f == kDraw && m == 0;
-        if (sh.i0)
-            sh.dec = fetch_decision(p.decisions + h);
-    }
-    __syncthreads();
-    if (!sh.i0)
-        return;
-    const Decision dec = sh.dec;
-    chunk_weight_sums<D>(p, h, c, dec, sh);
-    if (tid == 0)
-        flag_store(mark, 1);
-    __syncthreads();
-}
-
-// Take the decision of sequence h if it is ready. Each sequence has one
-// designated decider in k_verify and one in k_finish_decide, which runs
-// after it, so no claim is needed.
-template <class D>
-__device__ __forceinline__ void try_decide(const Params &p, int64_t h, Shared &sh)
-{
-    const int tid = threadIdx.x;
-    if (tid == 0)
-        sh.i1 = flag_load(&p.state[h].flag) == kReady;
-    __syncthreads();
-    if (!sh.i1)
-        return;
-    decide<D>(p, h, sh);
-    __syncthreads();
-    if (tid == 0) {
-        const bool draw = sh.dec.kind == SPEC_DRAW_RESIDUAL || sh.dec.kind == SPEC_DRAW_BONUS;
-        drain_stores();  // decision published before the flag
-        flag_store(&p.state[h].flag, draw ? kDraw : kDone);
-    }
-    __syncthreads();
-}
-
-// Error outputs of a sequence whose length or temperature is invalid (it
-// has no row items, so no decider).
-template <class D>
-__device__ __forceinline__ void invalid_sequence(const Params &p, int64_t b, int L, float tau)
-{
-    const int lane = threadIdx.x;
-    const int k = p.k;
-    if (lane <= k)
-        p.out_tokens[b * (k + 1) + lane] = -1;
-    if (p.aux.p_g && lane < k) p.aux.p_g[b * k + lane] = NAN;
-    if (p.aux.q_g && lane < k) p.aux.q_g[b * k + lane] = NAN;
-    if (p.aux.argmax && lane <= k) p.aux.argmax[b * (k + 1) + lane] = -1;
-    if (lane == 0) {
-        flag_store(&p.state[b].flag, kDone);
-        p.num_accepted[b] = 0;
-        if (p.aux.seq_status)
-            p.aux.seq_status[b] = !valid_len(L, k) ? SPEC_SEQ_BAD_LEN : SPEC_SEQ_BAD_TEMP;
-        if (p.aux.draw_row) p.aux.draw_row[b] = -1;
-        if (p.aux.draw_kind) p.aux.draw_kind[b] = SPEC_DRAW_NONE;
-        if (p.aux.resid_mass) p.aux.resid_mass[b] = NAN;
     }
 }
 
 // ===========================================================================
 // The step.
 // ===========================================================================
-__global__ __launch_bounds__(kThreads) void k_reset(SeqState *state, int32_t *chunk_claim,
-                                                    int32_t B, int32_t nc)
-{
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < B)
-        state[i] = SeqState{0, kPending, 0, 0};
-    if (i < (int64_t)B * nc)
-        chunk_claim[i] = 0;
-}
-
 template <class D>
-__global__ __launch_bounds__(kThreads) void k_verify(Params p)
+__global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
 {
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
-    __shared__ Shared sh;
-    const int tid = threadIdx.x;
+    __shared__ RowShared sh;
     const int64_t item = blockIdx.x;
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
 
@@ -1192,11 +954,8 @@ __global__ __launch_bounds__(kThreads) void k_verify(Params p)
     const int64_t b = rs / rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
-    if (!valid_len(L, k) || !valid_temp(tau)) {
-        if (slot == 0 && c == 0)
-            invalid_sequence<D>(p, b, L, tau);
-        return;
-    }
+    if (!valid_len(L, k) || !valid_temp(tau))
+        return;  // k_decide reports the sequence
     const bool greedy = tau == 0.f;
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
@@ -1208,64 +967,40 @@ __global__ __launch_bounds__(kThreads) void k_verify(Params p)
     const int64_t s = (int64_t)c * CH;
     const float2 part = chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy,
                                        greedy ? 0.f : temp_scale(tau), sh);
-    if (tid == 0) {
-        publish_pair(p.partials + item, __float_as_uint(part.x), __float_as_uint(part.y));
-        drain_stores();  // partial published before the count
-        const int items = nc * ((L + 1) + (greedy ? 0 : L));
-        if (counter_add(&p.state[b].rows_done, 1) == items - 1)
-            flag_store(&p.state[b].flag, kReady);
-    }
-    // The items of target row 0 (always read) take, by a fixed rule, the
-    // decision of sequence b - kLagDecide and one draw-weight chunk of
-    // sequence b - kLagSum, whose rows are still in the last-level cache.
-    // The assignment is static: who finishes first or last decides nothing,
-    // so an XCD that lags is never handed extra work (workgroup i runs on
-    // XCD i % 8, and chunk c of a row is workgroup ... * nc + c).
-    if (slot == 0) {
-        const int64_t h1 = b - kLagDecide, h2 = b - kLagSum;
-        if (h1 >= 0 && c == (int)(h1 % nc)) {
-            __syncthreads();
-            try_decide<D>(p, h1, sh);
-        }
-        if (h2 >= 0) {
-            __syncthreads();
-            sum_chunk<D>(p, h2, (int)((c + nc - h2 % nc) % nc), sh);
-        }
-    }
+    if (threadIdx.x == 0)
+        p.partials[item] = part;
 }
 
-// Work left when k_verify ends (in practice the last kLagSum sequences), in
-// three launches ordered by the stream, so nothing ever waits: decisions,
-// then chunk sums, then every locate.
+// One wave per sequence.
 template <class D>
-__global__ __launch_bounds__(kThreads) void k_finish_decide(Params p)
+__global__ __launch_bounds__(kThreads) void k_decide(Params p)
 {
-    __shared__ Shared sh;
-    try_decide<D>(p, blockIdx.x, sh);
+    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    if (b < p.B)
+        decide<D>(p, b, (int)(threadIdx.x % kWave));
 }
 
+// One workgroup per chunk of each sequence's draw row, sequences in reverse
+// order: the rows k_rowstats read last may still be in the last-level cache.
 template <class D>
-__global__ __launch_bounds__(kThreads) void k_finish_sums(Params p)
+__global__ __launch_bounds__(kThreads) void k_draw(Params p)
 {
-    __shared__ Shared sh;
-    sum_chunk<D>(p, blockIdx.x / p.nc, (int)(blockIdx.x % p.nc), sh);
+    __shared__ DrawShared sh;
+    const int nc = p.nc;
+    const int64_t b = (int64_t)p.B - 1 - (int64_t)(blockIdx.x / nc);
+    const int c = (int)(blockIdx.x % nc);
+    const Decision dec = p.decisions[b];  // uniform: one scalar load
+    if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
+        return;  // greedy or error: k_decide wrote everything
+    chunk_weight_sums<D>(p, b, c, dec, sh);
 }
 
+// One single-wave workgroup per sequence.
 template <class D>
-__global__ __launch_bounds__(kThreads) void k_finish_locate(Params p)
+__global__ __launch_bounds__(kWave) void k_locate(Params p)
 {
-    __shared__ Shared sh;
-    const int64_t b = blockIdx.x;
-    if (threadIdx.x == 0) {
-        sh.flag = flag_load(&p.state[b].flag);
-        if (sh.flag == kDraw)
-            sh.dec = fetch_decision(p.decisions + b);
-    }
-    __syncthreads();
-    if (sh.flag == kDraw) {
-        const Decision dec = sh.dec;
-        locate<D>(p, b, dec, sh);
-    }
+    __shared__ LocateShared sh;
+    locate<D>(p, blockIdx.x, (int)threadIdx.x, sh);
 }
 
 // ===========================================================================
@@ -1273,7 +1008,7 @@ __global__ __launch_bounds__(kThreads) void k_finish_locate(Params p)
 // ===========================================================================
 struct Layout {
     int nc;
-    size_t partials, decisions, masses, state, claims, total;
+    size_t partials, decisions, masses, segs, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1288,9 +1023,8 @@ bool layout_for(int32_t B, int32_t k, int32_t V, int32_t dtype, Layout *lay)
     lay->partials = 0;
     lay->decisions = align_up(nb * (size_t)(2 * k + 1) * (size_t)lay->nc * sizeof(float2), 256);
     lay->masses = lay->decisions + align_up(nb * sizeof(Decision), 256);
-    lay->state = lay->masses + align_up(nb * (size_t)lay->nc * sizeof(double2), 256);
-    lay->claims = lay->state + align_up(nb * sizeof(SeqState), 256);
-    lay->total = lay->claims + align_up(nb * (size_t)lay->nc * sizeof(int32_t), 256);
+    lay->segs = lay->masses + align_up(nb * (size_t)lay->nc * sizeof(double2), 256);
+    lay->total = lay->segs + align_up(nb * (size_t)lay->nc * 2 * kSegs * sizeof(double), 256);
     if (lay->total == 0)
         lay->total = 256;
     return true;
@@ -1325,8 +1059,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         p.partials = reinterpret_cast<float2 *>(ws + lay.partials) + b0 * per_seq_items;
         p.decisions = reinterpret_cast<Decision *>(ws + lay.decisions) + b0;
         p.masses = reinterpret_cast<double2 *>(ws + lay.masses) + b0 * nc;
-        p.state = reinterpret_cast<SeqState *>(ws + lay.state) + b0;
-        p.chunk_claim = reinterpret_cast<int32_t *>(ws + lay.claims) + b0 * nc;
+        p.segs = reinterpret_cast<double *>(ws + lay.segs) + b0 * nc * 2 * kSegs;
         p.out_tokens = base.out_tokens + b0 * (k + 1);
         p.num_accepted = base.num_accepted + b0;
         AuxDev &a = p.aux;
@@ -1339,18 +1072,17 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         if (a.draw_kind) a.draw_kind += b0;
         p.n_row_items = nb * per_seq_items;
 
-        hipLaunchKernelGGL(k_reset, dim3((unsigned)((nb * nc + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, p.state, p.chunk_claim, (int32_t)nb, nc);
+        // The events bracket k_rowstats of the first slice only.
         if (ev_begin && b0 == 0 && hipEventRecord(ev_begin, stream) != hipSuccess)
             return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(k_verify<D>, dim3((unsigned)p.n_row_items), dim3(kThreads), 0, stream,
-                           p);
-        hipLaunchKernelGGL(k_finish_decide<D>, dim3((unsigned)nb), dim3(kThreads), 0, stream, p);
-        hipLaunchKernelGGL(k_finish_sums<D>, dim3((unsigned)(nb * nc)), dim3(kThreads), 0, stream,
-                           p);
-        hipLaunchKernelGGL(k_finish_locate<D>, dim3((unsigned)nb), dim3(kThreads), 0, stream, p);
-        if (ev_end && b0 + nb >= B && hipEventRecord(ev_end, stream) != hipSuccess)
+        hipLaunchKernelGGL(k_rowstats<D>, dim3((unsigned)p.n_row_items), dim3(kThreads), 0,
+                           stream, p);
+        if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
             return SPEC_ELAUNCH;
+        hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
+                           dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_draw<D>, dim3((unsigned)(nb * nc)), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_locate<D>, dim3((unsigned)nb), dim3(kWave), 0, stream, p);
         if (hipGetLastError() != hipSuccess)
             return SPEC_ELAUNCH;
     }
