@@ -106,7 +106,10 @@ typedef struct {
     int32_t *draw_row;   /* [B]: row of the last emitted token (= num_accepted), -1 on error */
     int32_t *draw_kind;  /* [B]: SPEC_DRAW_*                                               */
     void *event_begin;   /* hipEvent_t or NULL: recorded on `stream` right before the     */
-    void *event_end;     /* main verification kernel, and right after it                   */
+    void *event_end;     /* row-statistics kernel (the one that reads every logit row),   */
+                         /* and right after it; when B is split into several launch      */
+                         /* slices (B * (2k+1) * ceil(V*e / 32 KiB) > 2^22), around the  */
+                         /* first slice's                                                */
 } spec_verify_aux_t;
 
 /* Bytes of scratch device memory one spec_verify call with these sizes
