@@ -127,6 +127,8 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=1024,
                     help="sequences of the batch the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-early-exit", action="store_true",
+                    help="skip timing the early-exit entry point on the same batch")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
 
@@ -177,10 +179,18 @@ def main() -> int:
     outs = [(torch.empty((w.B, w.k + 1), dtype=torch.int32, device="cuda:0"),
              torch.empty((w.B,), dtype=torch.int32, device="cuda:0")) for _ in copies]
 
-    def step(i: int, events=None):
+    def step(i: int, events=None, fn=sv.spec_verify):
         cb = copies[i % len(copies)]
-        sv.spec_verify(cb.target, cb.draft, cb.draft_tokens, cb.draft_len, cb.temperature, seed,
-                       workspace=ws, out=outs[i % len(copies)], events=events)
+        fn(cb.target, cb.draft, cb.draft_tokens, cb.draft_len, cb.temperature, seed,
+           workspace=ws, out=outs[i % len(copies)], events=events)
+
+    def event_ms():
+        ms = []
+        for a, b in ev:
+            m = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(m), a, b) == 0
+            ms.append(m.value)
+        return sorted(ms)
 
     log(f"[bench] settle {args.settle_ms:.0f} ms, then warmup {W} steps, {len(copies)} rotating copies")
     n_settle = 0
@@ -200,15 +210,7 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    k1_ms = []
-    for a, b in ev:
-        ms = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
-        k1_ms.append(ms.value)
-    for a, b in ev:
-        hip.hipEventDestroy(a)
-        hip.hipEventDestroy(b)
-    k1_ms.sort()
+    k1_ms = event_ms()
     k1_mean = sum(k1_ms) / len(k1_ms)
     k1_median = k1_ms[len(k1_ms) // 2]
     ms_per_step = elapsed * 1e3 / K
@@ -218,6 +220,45 @@ def main() -> int:
     log(f"[bench] {ms_per_step:.4f} ms/step; k_rowstats mean {k1_mean * 1e3:.1f} us "
         f"(median {k1_median * 1e3:.1f}, min {k1_ms[0] * 1e3:.1f}, max {k1_ms[-1] * 1e3:.1f}); "
         f"{achieved:.0f} GB/s")
+
+    early = None
+    if not args.no_early_exit:
+        # The same batch through the early-exit schedule (identical outputs;
+        # only the rows up to each sequence's first rejection are read).
+        log(f"[bench] early exit: warmup {W} steps, timing {K} steps")
+        for i in range(W):
+            step(i, fn=sv.spec_verify_early_exit)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i, events=(ev[i][0].value, ev[i][1].value), fn=sv.spec_verify_early_exit)
+        torch.cuda.synchronize()
+        ee_elapsed = time.perf_counter() - t0
+        loop_ms = event_ms()
+        loop_mean = sum(loop_ms) / len(loop_ms)
+        n_ee = outs[0][1].to(torch.int64).cpu()
+        L = copies[0].draft_len.to(torch.int64).cpu()
+        samp = (copies[0].temperature.cpu() > 0)
+        ee_t = int((n_ee + 1).sum())
+        ee_d = int(torch.minimum(n_ee + 1, L)[samp].sum())
+        ee_bytes = (ee_t + ee_d) * w.V * w.elem_bytes
+        ee_ms = ee_elapsed * 1e3 / K
+        early = {
+            "entry_point": "spec_verify_early_exit",
+            "value": positions / (ee_ms * 1e-3),
+            "unit": "positions/s",
+            "ms_per_step": ee_ms,
+            "rows_read": {"target": ee_t, "draft": ee_d},
+            "bytes_read_once": ee_bytes,
+            "position_loop_us_mean": loop_mean * 1e3,
+            "position_loop_GBps": ee_bytes / (loop_mean * 1e-3) / 1e9,
+            "outputs_identical": bool(torch.equal(n_ee, n_acc.cpu())),
+        }
+        log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
+            f"for {ee_bytes / 1e9:.3f} GB")
+    for a, b in ev:
+        hip.hipEventDestroy(a)
+        hip.hipEventDestroy(b)
 
     traffic = read_counter_traffic(w.name)
     result = {
@@ -257,6 +298,8 @@ def main() -> int:
             "kernel_us_median": k1_median * 1e3,
         },
     }
+    if early is not None:
+        result["early_exit"] = early
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences")
         result["cpu_baseline"] = cpu_baseline(batch, seed, args.cpu_seqs)

@@ -112,8 +112,8 @@ typedef struct {
                          /* first slice's                                                */
 } spec_verify_aux_t;
 
-/* Bytes of scratch device memory one spec_verify call with these sizes
- * needs. Returns 0 for invalid sizes. */
+/* Bytes of scratch device memory one spec_verify or spec_verify_early_exit
+ * call with these sizes needs. Returns 0 for invalid sizes. */
 size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int32_t dtype);
 
 /*
@@ -152,6 +152,36 @@ int spec_verify(const void *target_logits, const void *draft_logits, int32_t dty
                 uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
                 const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * Same step with an early-exit schedule: the draft positions are taken one
+ * at a time for the whole batch, and position i reads only the target and
+ * draft rows of the sequences that accepted every earlier drafted token.
+ * A round stops at its first rejection, and nothing after that position
+ * affects its outputs ("Speculative Decoding and the Art of Fast LLM
+ * Inference", "The Algorithm, Step by Step", step "Stop at the first
+ * rejection"; techaiinterview.com, "Core explanation", step 3), so rows past
+ * it need not be read at all.
+ *
+ * Arguments, layouts, ownership, RNG contract and host-side errors are those
+ * of spec_verify, and out_tokens, num_accepted, seq_status, draw_row,
+ * draw_kind and resid_mass are bit-identical to spec_verify's for the same
+ * inputs, seed and seq_base. The diagnostics of rows that are never read
+ * differ: p_g and q_g are written only for positions up to the stop (and
+ * are NaN after it), argmax only for greedy rows up to the stop (-1 after
+ * it). Enqueues k + 4 kernels (one row-statistics launch per position, in
+ * which the workgroup that completes a sequence's rows also decides it);
+ * event_begin / event_end bracket the per-position launches.
+ * Pays when rejections come early (few accepted tokens per round): it reads
+ * about (1 - a^L) / (1 - a) positions per sequence instead of L + 1, at a
+ * per-token acceptance rate a.
+ */
+int spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
+                           const int32_t *draft_tokens, const int32_t *draft_len,
+                           const float *temperature, int32_t B, int32_t k, int32_t V,
+                           uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                           int32_t *num_accepted, const spec_verify_aux_t *aux,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a spec_status_t value. */
 const char *spec_verify_strerror(int status);

@@ -1,11 +1,12 @@
 """Speculative-sampling verification on AMD Instinct MI355X (gfx950).
 
 The hot path is the C-ABI HIP library declared in include/spec_verify.h;
-``spec_verify`` below is its thin Python binding. ``workloads`` draws the
-seeded synthetic inputs.
+``spec_verify`` and ``spec_verify_early_exit`` below are its thin Python
+binding. ``workloads`` draws the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
-    BF16, F32, MAX_K, SpecVerifyError, spec_verify, strerror, workspace_size, library,
+    BF16, F32, MAX_K, SpecVerifyError, spec_verify, spec_verify_early_exit, strerror,
+    workspace_size, library,
     SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO,
     DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P,
 )

@@ -26,8 +26,8 @@ DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
 
-EXPORTED = ("spec_verify", "spec_verify_workspace_size", "spec_verify_strerror",
-            "spec_verify_version")
+EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_workspace_size",
+            "spec_verify_strerror", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -72,9 +72,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         i32, u32, u64 = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
         lib.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.spec_verify_workspace_size.restype = ctypes.c_size_t
-        lib.spec_verify.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
-                                    ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
-        lib.spec_verify.restype = ctypes.c_int
+        for fn in (lib.spec_verify, lib.spec_verify_early_exit):
+            fn.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
+                           ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
+            fn.restype = ctypes.c_int
         lib.spec_verify_strerror.argtypes = [ctypes.c_int]
         lib.spec_verify_strerror.restype = ctypes.c_char_p
         lib.spec_verify_version.argtypes = []
@@ -109,6 +110,29 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor],
                 temperature: Union[float, torch.Tensor] = 1.0, seed: int = 0, *,
                 seq_base: int = 0, aux: bool = False, workspace: Optional[torch.Tensor] = None,
                 out: Optional[tuple] = None, events: Optional[tuple] = None):
+    """Verify B drafted continuations on the GPU (C entry point spec_verify).
+    See _verify for the arguments."""
+    return _verify("spec_verify", target, draft, draft_tokens, draft_len, temperature, seed,
+                   seq_base, aux, workspace, out, events)
+
+
+def spec_verify_early_exit(target: torch.Tensor, draft: Optional[torch.Tensor],
+                           draft_tokens: Optional[torch.Tensor],
+                           draft_len: Optional[torch.Tensor] = None,
+                           temperature: Union[float, torch.Tensor] = 1.0, seed: int = 0, *,
+                           seq_base: int = 0, aux: bool = False,
+                           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None,
+                           events: Optional[tuple] = None):
+    """Same outputs as spec_verify, reading only the rows up to each
+    sequence's first rejection (C entry point spec_verify_early_exit). The
+    p_g / q_g / argmax diagnostics past the stop are NaN / -1. ``events``
+    bracket the per-position launches."""
+    return _verify("spec_verify_early_exit", target, draft, draft_tokens, draft_len, temperature,
+                   seed, seq_base, aux, workspace, out, events)
+
+
+def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, seq_base, aux,
+            workspace, out, events):
     """Verify B drafted continuations on the GPU.
 
     target [B, k+1, V] and draft [B, k, V]: float32 or bfloat16, contiguous,
@@ -183,7 +207,7 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor],
 
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        rc = lib.spec_verify(
+        rc = getattr(lib, entry)(
             target.data_ptr(), _ptr(draft) if k > 0 else None, dt,
             _ptr(draft_tokens) if k > 0 else None, _ptr(draft_len), temp.data_ptr(),
             B, k, V, ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint32(seq_base & 0xFFFFFFFF),
