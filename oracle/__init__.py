@@ -15,6 +15,9 @@ Parity status of each function (what pins it is in the tests):
   round_greedy         pinned: worked rounds, argmax agreement by hand
   spec_verify_ref      pinned: chi-square of emitted tokens against p, accepted
                        length against the closed form, worked rounds
+  tree_greedy          pinned: chain trees equal round_greedy; brute-force path
+                       enumeration; a hand-worked tree; planted mistakes
+  spec_tree_ref        pinned: argmax_row per node + tree_greedy, statuses
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ _LIB = os.path.join(_HERE, "_build", "libspecverify_oracle.so")
 F32 = 0
 BF16 = 1
 
-SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO = range(5)
+SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE = range(6)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 _lock = threading.Lock()
@@ -81,6 +84,11 @@ def _load():
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                         ctypes.c_uint32] + [P] * 11
         lib.spec_verify_ref.restype = ctypes.c_int
+        lib.ref_tree_greedy.argtypes = [P, P, P, ctypes.c_int, P, P]
+        lib.ref_tree_greedy.restype = ctypes.c_int
+        lib.spec_tree_ref.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int64, P, P, P, P, P]
+        lib.spec_tree_ref.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -238,4 +246,52 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
             rcs = list(ex.map(lambda b0: run(b0, min(B, b0 + step)), range(0, B, step)))
         if any(rcs):
             raise MemoryError("oracle scratch allocation failed")
+    return res
+
+
+def tree_greedy(amax, parents, tokens):
+    """Greedy verification of one candidate tree from per-node argmaxes.
+    Returns (d, out[0..d], path[0..d-1])."""
+    amax = np.ascontiguousarray(np.asarray(amax, dtype=np.int64))
+    n = amax.shape[0]
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(n))
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(n))
+    out = np.full(n, -1, dtype=np.int32)
+    path = np.full(n, -1, dtype=np.int32)
+    d = _load().ref_tree_greedy(_ptr(amax), _ptr(par), _ptr(tok), n, _ptr(out), _ptr(path))
+    if d < 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return int(d), out[:d + 1].copy(), path[:d].copy()
+
+
+def spec_tree_ref(target: np.ndarray, parents: np.ndarray, tokens: np.ndarray, n_nodes,
+                  nthreads: int = 1) -> dict:
+    """Greedy tree verification of a batch on host arrays (see spec_tree_ref
+    in spec_verify_ref.c). target [B, N, V] float32 or uint16 (bf16 bits)."""
+    target, dt = _logits(target)
+    B, N, V = target.shape
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(B, N))
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(B, N))
+    nn = np.ascontiguousarray(np.asarray(n_nodes, dtype=np.int32).reshape(B))
+    res = dict(out_tokens=np.full((B, N), -1, dtype=np.int32),
+               path_nodes=np.full((B, N), -1, dtype=np.int32),
+               num_accepted=np.zeros(B, dtype=np.int32),
+               seq_status=np.zeros(B, dtype=np.int32),
+               argmax=np.full((B, N), -1, dtype=np.int32))
+    lib = _load()
+
+    def run(b0: int, b1: int) -> int:
+        if b1 <= b0:
+            return 0
+        sl = slice(b0, b1)
+        return lib.spec_tree_ref(_ptr(target[sl]), dt, _ptr(par[sl]), _ptr(tok[sl]), _ptr(nn[sl]),
+                                 b1 - b0, N, V, *[_ptr(res[k][sl]) for k in (
+                                     "out_tokens", "path_nodes", "num_accepted", "seq_status",
+                                     "argmax")])
+
+    step = max(1, (B + max(1, nthreads) - 1) // max(1, nthreads))
+    with ThreadPoolExecutor(max_workers=max(1, nthreads)) as ex:
+        rcs = list(ex.map(lambda b0: run(b0, min(B, b0 + step)), range(0, B, step)))
+    if any(rcs):
+        raise MemoryError("oracle scratch allocation failed")
     return res

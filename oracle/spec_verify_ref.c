@@ -39,6 +39,12 @@
  *       on ties); the correction/bonus is that argmax.
  *   R6  row alignment: target row i and draft row i score draft position i
  *       (0-based); the bonus is target row L (L = the sequence's draft length).
+ *   T1  candidate trees: greedy acceptance only (the pages give no sampling
+ *       rule for trees). Node 0 is the root; node n >= 1 holds a drafted
+ *       token and a parent with a smaller index; the target row of node n
+ *       scores the token that follows node n's path.
+ *   T2  a tree round keeps the deepest accepted node, the lowest node index
+ *       among equally deep ones.
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,7 +58,8 @@ enum {
     REF_SEQ_BAD_TOKEN = 1,
     REF_SEQ_BAD_LEN = 2,
     REF_SEQ_BAD_TEMP = 3,
-    REF_SEQ_QZERO = 4
+    REF_SEQ_QZERO = 4,
+    REF_SEQ_BAD_TREE = 5  /* a parent index outside [0, n) for node n */
 };
 
 enum {
@@ -410,5 +417,116 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
     }
 
     free(p), free(q), free(w), free(u), free(v), free(amax), free(macc);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Greedy verification of one candidate tree ([ART] "EAGLE: drafting in */
+/* feature space": a tree of candidate continuations verified together; */
+/* [TAI] "Drafts and limits": tree verification checks several          */
+/* candidate continuations in one target pass; readings T1, T2, R5).    */
+/*                                                                      */
+/*   amax[n]: target argmax of node n's row (n < n_nodes)               */
+/*   par[n], tok[n]: parent and drafted token of node n >= 1            */
+/* Node 0 (the root) is accepted; node n >= 1 is accepted iff its parent */
+/* is accepted and tok[n] equals the parent's argmax -- the linear      */
+/* greedy rule applied along every branch. The round keeps the deepest  */
+/* accepted node b, emits the tokens on the path root -> b and then     */
+/* amax[b]. out[0..d-1] = path tokens, out[d] = amax[b],                */
+/* path[0..d-1] = path nodes (root excluded). Returns d.                */
+/* ------------------------------------------------------------------ */
+int ref_tree_greedy(const int64_t *amax, const int32_t *par, const int32_t *tok, int n_nodes,
+                    int32_t *out, int32_t *path)
+{
+    char *acc = malloc((size_t)n_nodes);
+    int *depth = malloc(sizeof(int) * (size_t)n_nodes);
+    if (!acc || !depth) {
+        free(acc), free(depth);
+        return -1;
+    }
+    acc[0] = 1;
+    depth[0] = 0;
+    for (int n = 1; n < n_nodes; n++) {
+        acc[n] = acc[par[n]] && (int64_t)tok[n] == amax[par[n]];
+        depth[n] = depth[par[n]] + 1;
+    }
+    int best = 0;
+    for (int n = 1; n < n_nodes; n++)  /* ascending: the first of the deepest wins */
+        if (acc[n] && depth[n] > depth[best])
+            best = n;
+    const int d = depth[best];
+    int x = best;
+    for (int j = d - 1; j >= 0; j--) {
+        path[j] = x;
+        out[j] = tok[x];
+        x = par[x];
+    }
+    out[d] = (int32_t)amax[best];
+    free(acc), free(depth);
+    return d;
+}
+
+/* ------------------------------------------------------------------ */
+/* Greedy tree verification for a batch of B sequences.                 */
+/*                                                                      */
+/* target [B, N, V] (dtype REF_F32 or REF_BF16 as raw bits): row n of    */
+/* sequence b is scored at node n. parents [B, N], tokens [B, N] (entry */
+/* 0 of each is ignored), n_nodes [B] in [1, N].                        */
+/* Outputs: out_tokens [B, N]: path tokens, then the bonus, then -1;    */
+/* path_nodes [B, N]: path nodes, then -1; num_accepted [B];            */
+/* seq_status [B] (REF_SEQ_BAD_LEN: n_nodes outside [1, N];             */
+/* REF_SEQ_BAD_TREE: a parent outside [0, n); REF_SEQ_BAD_TOKEN: a token */
+/* outside [0, V)); argmax [B, N] (may be NULL): argmax of the rows of  */
+/* nodes < n_nodes, -1 elsewhere. Returns 0, or -1 on allocation failure.*/
+/* ------------------------------------------------------------------ */
+int spec_tree_ref(const void *target, int dtype, const int32_t *parents, const int32_t *tokens,
+                  const int32_t *n_nodes, int32_t B, int32_t N, int64_t V, int32_t *out_tokens,
+                  int32_t *path_nodes, int32_t *num_accepted, int32_t *seq_status,
+                  int32_t *argmax)
+{
+    const size_t esz = dtype == REF_F32 ? 4 : 2;
+    int64_t *amax = malloc(sizeof(int64_t) * (size_t)N);
+    if (!amax)
+        return -1;
+    for (int32_t b = 0; b < B; b++) {
+        int32_t *out = out_tokens + (size_t)b * N;
+        int32_t *path = path_nodes + (size_t)b * N;
+        const int32_t *par = parents + (size_t)b * N;
+        const int32_t *tok = tokens + (size_t)b * N;
+        const int nn = n_nodes[b];
+        for (int n = 0; n < N; n++) {
+            out[n] = -1;
+            path[n] = -1;
+            if (argmax) argmax[(size_t)b * N + n] = -1;
+        }
+        num_accepted[b] = 0;
+        int status = REF_SEQ_OK;
+        if (nn < 1 || nn > N) {
+            status = REF_SEQ_BAD_LEN;
+        } else {
+            for (int n = 1; n < nn; n++)
+                if (par[n] < 0 || par[n] >= n)
+                    status = REF_SEQ_BAD_TREE;
+            if (status == REF_SEQ_OK)
+                for (int n = 1; n < nn; n++)
+                    if (tok[n] < 0 || (int64_t)tok[n] >= V)
+                        status = REF_SEQ_BAD_TOKEN;
+        }
+        seq_status[b] = status;
+        if (status != REF_SEQ_OK)
+            continue;
+        const char *rows = (const char *)target + (size_t)b * N * V * esz;
+        for (int n = 0; n < nn; n++) {
+            amax[n] = ref_argmax_row(rows + (size_t)n * V * esz, dtype, V);
+            if (argmax) argmax[(size_t)b * N + n] = (int32_t)amax[n];
+        }
+        const int d = ref_tree_greedy(amax, par, tok, nn, out, path);
+        if (d < 0) {
+            free(amax);
+            return -1;
+        }
+        num_accepted[b] = d;
+    }
+    free(amax);
     return 0;
 }
