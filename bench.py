@@ -113,6 +113,54 @@ def cpu_baseline(batch, seed: int, nseq: int) -> dict:
                       f"{dt:.2f} s wall"}
 
 
+def bench_tree(hip, ev, K: int, W: int) -> dict:
+    """Greedy tree verification on workload t3: nodes per second, and the
+    node-row kernel's bandwidth (each node row read once, HIP events)."""
+    import torch
+    import speculative_decoding_verification_11_amd as sv
+    from speculative_decoding_verification_11_amd import workloads as wl
+
+    tw = wl.TREE_WORKLOADS["t3"]
+    log(f"[bench] tree: generating {tw.name}: {tw.description}")
+    tb = wl.generate_tree(tw, "cuda:0")
+    ws = torch.empty(sv.tree_workspace_size(tw.B, tw.N, tw.V, tw.dtype_code), dtype=torch.uint8,
+                     device="cuda:0")
+    out = (torch.empty((tw.B, tw.N), dtype=torch.int32, device="cuda:0"),
+           torch.empty((tw.B, tw.N), dtype=torch.int32, device="cuda:0"),
+           torch.empty((tw.B,), dtype=torch.int32, device="cuda:0"))
+
+    def step(events=None):
+        sv.spec_verify_tree(tb.target, tb.parents, tb.tokens, tb.n_nodes, workspace=ws, out=out,
+                            events=events)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events=(ev[i][0].value, ev[i][1].value))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = []
+    for a, b in ev:
+        m = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(m), a, b) == 0
+        ms.append(m.value)
+    row_mean = sum(ms) / len(ms)
+    nodes = int(tb.n_nodes.sum())
+    nbytes = tb.bytes_read()
+    ms_step = elapsed * 1e3 / K
+    res = {"entry_point": "spec_verify_tree", "workload": f"{tw.name}: {tw.description}",
+           "value": nodes / (ms_step * 1e-3), "unit": "nodes/s", "ms_per_step": ms_step,
+           "bytes_read_once": nbytes, "row_kernel": "k_tree_rowstats",
+           "row_kernel_us_mean": row_mean * 1e3,
+           "row_kernel_GBps": nbytes / (row_mean * 1e-3) / 1e9,
+           "mean_accepted_depth": float(out[2].float().mean())}
+    log(f"[bench] tree {ms_step:.4f} ms/step; rows {row_mean * 1e3:.1f} us "
+        f"({res['row_kernel_GBps']:.0f} GB/s)")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +177,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-early-exit", action="store_true",
                     help="skip timing the early-exit entry point on the same batch")
+    ap.add_argument("--no-tree", action="store_true",
+                    help="skip timing greedy tree verification (workload t3)")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
 
@@ -256,6 +306,9 @@ def main() -> int:
         }
         log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
             f"for {ee_bytes / 1e9:.3f} GB")
+    tree = None
+    if not args.no_tree:
+        tree = bench_tree(hip, ev, K, W)
     for a, b in ev:
         hip.hipEventDestroy(a)
         hip.hipEventDestroy(b)
@@ -300,6 +353,8 @@ def main() -> int:
     }
     if early is not None:
         result["early_exit"] = early
+    if tree is not None:
+        result["tree"] = tree
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences")
         result["cpu_baseline"] = cpu_baseline(batch, seed, args.cpu_seqs)

@@ -76,10 +76,12 @@ enum {
     SPEC_SEQ_BAD_LEN = 2,   /* draft length outside [0, k]                   */
     SPEC_SEQ_BAD_TEMP = 3,  /* temperature NaN, infinite, negative, or       */
                             /* positive but below FLT_MIN                    */
-    SPEC_SEQ_QZERO = 4      /* the scan reached a drafted token whose fp32   */
+    SPEC_SEQ_QZERO = 4,     /* the scan reached a drafted token whose fp32   */
                             /* draft probability is 0 (the acceptance ratio  */
                             /* is undefined; thelatentsource.com accept_token */
                             /* raises in this case)                          */
+    SPEC_SEQ_BAD_TREE = 5   /* spec_verify_tree: a parent index outside      */
+                            /* [0, n) for node n                             */
 };
 
 /* How the last emitted token of a sequence was produced (aux->draw_kind). */
@@ -182,6 +184,58 @@ int spec_verify_early_exit(const void *target_logits, const void *draft_logits, 
                            uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
                            int32_t *num_accepted, const spec_verify_aux_t *aux,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy verification of candidate trees.
+ *
+ * A draft may be a tree of candidate continuations verified in one target
+ * pass ("Speculative Decoding and the Art of Fast LLM Inference", "EAGLE:
+ * drafting in feature space"; techaiinterview.com, "Drafts and limits",
+ * tree verification). Node 0 of a sequence's tree is the root (the last
+ * committed position); node n >= 1 holds a drafted token tokens[n] and hangs
+ * below parents[n] < n. Target row n scores the token that follows node n's
+ * path. The pages give no sampling rule for trees, so the rule is greedy:
+ * node n >= 1 is accepted iff its parent is accepted and tokens[n] equals
+ * the argmax of the parent's row (lowest token id on ties); the round keeps
+ * the deepest accepted node (the lowest node index among equally deep ones)
+ * and emits the tokens on its path, then the argmax of its row. A chain tree
+ * (parents[n] = n - 1) is exactly spec_verify's greedy rule.
+ * ---------------------------------------------------------------------- */
+
+/* Largest supported number of nodes per tree (one wave lane per node). */
+#define SPEC_MAX_TREE 64
+
+/* Optional outputs of spec_verify_tree. Every member may be NULL. */
+typedef struct {
+    int32_t *seq_status; /* [B]: SPEC_SEQ_OK, _BAD_LEN (n_nodes outside [1, N]),          */
+                         /*      _BAD_TREE, or _BAD_TOKEN (a token outside [0, V))        */
+    int32_t *argmax;     /* [B, N]: argmax of the rows of nodes < n_nodes; -1 elsewhere    */
+    void *event_begin;   /* hipEvent_t or NULL: recorded right before and right after the  */
+    void *event_end;     /* row kernel (of the first launch slice)                        */
+} spec_tree_aux_t;
+
+/* Workspace bytes one spec_verify_tree call needs; 0 for invalid sizes. */
+size_t spec_verify_tree_workspace_size(int32_t B, int32_t N, int32_t V, int32_t dtype);
+
+/*
+ *   target_logits [B, N, V] row-major, dtype; rows of nodes >= n_nodes[b] are
+ *                 never read.
+ *   parents, tokens [B, N] int32; entry 0 (the root) of each is ignored.
+ *   n_nodes       [B] int32, in [1, N].
+ *   B, N, V       B >= 0, 1 <= N <= SPEC_MAX_TREE, V >= 1.
+ *   out_tokens    [B, N] out: the d accepted tokens along the path, then the
+ *                 argmax after the path, then -1.
+ *   path_nodes    [B, N] out: the d node indices of the path (root excluded),
+ *                 then -1.
+ *   num_accepted  [B] out: d, the depth of the kept node.
+ * Memory, errors, alignment and streams as for spec_verify: a sequence with a
+ * bad status gets num_accepted = 0 and out_tokens / path_nodes all -1.
+ */
+int spec_verify_tree(const void *target_logits, int32_t dtype, const int32_t *parents,
+                     const int32_t *tokens, const int32_t *n_nodes, int32_t B, int32_t N,
+                     int32_t V, int32_t *out_tokens, int32_t *path_nodes, int32_t *num_accepted,
+                     const spec_tree_aux_t *aux, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /* Static, human-readable text for a spec_status_t value. */
 const char *spec_verify_strerror(int status);

@@ -20,14 +20,16 @@ from .build import LIB as LIB_PATH
 F32 = 0
 BF16 = 1
 MAX_K = 63
+MAX_TREE = 64
 
-SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO = range(5)
+SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE = range(6)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
 
 EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_workspace_size",
-            "spec_verify_strerror", "spec_verify_version")
+            "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_verify_strerror",
+            "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -47,6 +49,17 @@ class Aux(ctypes.Structure):
         ("seq_status", ctypes.c_void_p),
         ("draw_row", ctypes.c_void_p),
         ("draw_kind", ctypes.c_void_p),
+        ("event_begin", ctypes.c_void_p),
+        ("event_end", ctypes.c_void_p),
+    ]
+
+
+class TreeAux(ctypes.Structure):
+    """Mirror of spec_tree_aux_t."""
+
+    _fields_ = [
+        ("seq_status", ctypes.c_void_p),
+        ("argmax", ctypes.c_void_p),
         ("event_begin", ctypes.c_void_p),
         ("event_end", ctypes.c_void_p),
     ]
@@ -76,6 +89,11 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
                            ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
             fn.restype = ctypes.c_int
+        lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.spec_verify_tree_workspace_size.restype = ctypes.c_size_t
+        lib.spec_verify_tree.argtypes = [P, i32, P, P, P, i32, i32, i32, P, P, P,
+                                         ctypes.POINTER(TreeAux), P, ctypes.c_size_t, P]
+        lib.spec_verify_tree.restype = ctypes.c_int
         lib.spec_verify_strerror.argtypes = [ctypes.c_int]
         lib.spec_verify_strerror.restype = ctypes.c_char_p
         lib.spec_verify_version.argtypes = []
@@ -219,3 +237,69 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
     if aux:
         return out_tokens, num_acc, aux_out
     return out_tokens, num_acc
+
+
+def tree_workspace_size(B: int, N: int, V: int, dtype: int) -> int:
+    return int(library().spec_verify_tree_workspace_size(B, N, V, dtype))
+
+
+def spec_verify_tree(target: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                     n_nodes: torch.Tensor, *, aux: bool = False,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None,
+                     events: Optional[tuple] = None):
+    """Greedy verification of B candidate trees (C entry point spec_verify_tree).
+
+    target [B, N, V] float32 or bfloat16 (row n scored at node n); parents,
+    tokens [B, N] int32 (entry 0 ignored); n_nodes [B] int32. Returns
+    (out_tokens [B, N], path_nodes [B, N], num_accepted [B]), plus a dict with
+    seq_status and argmax when ``aux`` is true. ``events`` = (begin, end) raw
+    hipEvent_t handles recorded around the row kernel.
+    """
+    if target.dim() != 3:
+        raise ValueError("target must be [B, N, V]")
+    B, N, V = target.shape
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    dt = _dtype_code(target)
+    if not target.is_contiguous():
+        raise ValueError("target must be contiguous")
+    for name, t, shape in (("parents", parents, (B, N)), ("tokens", tokens, (B, N)),
+                           ("n_nodes", n_nodes, (B,))):
+        if (tuple(t.shape) != shape or t.dtype != torch.int32 or t.device != dev
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous {list(shape)} int32 on {dev}")
+    lib = library()
+    if out is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+        path_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        num_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        out_tokens, path_nodes, num_acc = out
+    need = int(lib.spec_verify_tree_workspace_size(B, N, V, dt))
+    if need == 0:
+        raise SpecVerifyError(1, "invalid sizes for the tree workspace query")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    aux_t, aux_out = None, None
+    if aux or events is not None:
+        aux_t = TreeAux()
+        if aux:
+            aux_out = dict(seq_status=torch.empty((B,), dtype=torch.int32, device=dev),
+                           argmax=torch.empty((B, N), dtype=torch.int32, device=dev))
+            aux_t.seq_status = aux_out["seq_status"].data_ptr()
+            aux_t.argmax = aux_out["argmax"].data_ptr()
+        if events is not None:
+            aux_t.event_begin, aux_t.event_end = events
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_tree(target.data_ptr(), dt, parents.data_ptr(), tokens.data_ptr(),
+                                  n_nodes.data_ptr(), B, N, V, out_tokens.data_ptr(),
+                                  path_nodes.data_ptr(), num_acc.data_ptr(),
+                                  ctypes.byref(aux_t) if aux_t is not None else None,
+                                  workspace.data_ptr(), need, stream)
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    if aux:
+        return out_tokens, path_nodes, num_acc, aux_out
+    return out_tokens, path_nodes, num_acc

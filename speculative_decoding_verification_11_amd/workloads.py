@@ -284,7 +284,142 @@ def to_host_arrays(batch: Batch) -> dict:
     }
 
 
+# ---------------------------------------------------------------------------
+# Candidate trees (greedy tree verification).
+#
+# Recipe: level widths are fixed per workload (level d holds widths[d-1]
+# nodes, numbered breadth first after the root); each node of level d picks
+# its parent uniformly from level d-1. Target rows are drawn as for the
+# linear workloads (N(0, sigma^2) plus the Zipf-ranked bias, rounded to the
+# storage dtype). A node's children carry the best-ranked distinct tokens of
+# a draft row at that node (target row + N(0, sigma_d^2), never stored): the
+# first child the draft's top token, the second its runner-up, and so on, as
+# a tree drafter expands its most likely candidates. The draft noise sets
+# how often a child hits the target's argmax.
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class TreeWorkload:
+    name: str
+    B: int
+    V: int
+    dtype: str
+    widths: Tuple[int, ...]  # nodes per level below the root
+    target_sigma: float = 3.0
+    draft_sigma: float = 1.0
+    zipf_s: Optional[float] = 1.1
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def N(self) -> int:
+        return 1 + sum(self.widths)
+
+    @property
+    def dtype_code(self) -> int:
+        return _DTYPE_CODE[self.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        return _ELEM_BYTES[self.dtype]
+
+
+TREE_WORKLOADS = {
+    "t1": TreeWorkload("t1", B=4, V=1024, dtype="f32", widths=(3, 4, 4, 3, 1),
+                       target_sigma=2.0, draft_sigma=0.7, zipf_s=None, seed=7001,
+                       description="B=4 N=16 V=1024 fp32 trees, widths 3-4-4-3-1"),
+    "t2": TreeWorkload("t2", B=16, V=32000, dtype="f32", widths=(4, 8, 12, 12, 10, 8, 6, 3),
+                       draft_sigma=1.0, seed=7002,
+                       description="B=16 N=64 V=32000 fp32 trees, 8 levels"),
+    "t3": TreeWorkload("t3", B=128, V=128256, dtype="bf16", widths=(4, 8, 12, 12, 10, 8, 6, 3),
+                       draft_sigma=1.0, seed=7003,
+                       description="B=128 N=64 V=128256 bf16 trees, 8 levels (widths "
+                                   "4-8-12-12-10-8-6-3)"),
+}
+
+
+@dataclass
+class TreeBatch:
+    workload: TreeWorkload
+    target: torch.Tensor  # [B, N, V]
+    parents: torch.Tensor  # [B, N] int32, -1 at the root
+    tokens: torch.Tensor  # [B, N] int32, 0 at the root
+    n_nodes: torch.Tensor  # [B] int32
+
+    def bytes_read(self) -> int:
+        """Each node row once."""
+        return int(self.n_nodes.to(torch.int64).sum()) * self.workload.V * self.workload.elem_bytes
+
+
+def generate_tree(w: TreeWorkload, device: Union[str, torch.device] = "cpu",
+                  seq_block: int = 16) -> TreeBatch:
+    """Draw one batch of candidate trees for ``w`` on ``device``. Draw order:
+    Zipf permutation, parents (level by level), then per block of sequences
+    target noise and draft noise."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    B, N, V = w.B, w.N, w.V
+    sdt = _TORCH_DTYPE[w.dtype]
+    bias = None
+    if w.zipf_s is not None:
+        perm = torch.randperm(V, generator=gen, device=device)
+        bias = -w.zipf_s * torch.log((perm + 1).to(torch.float32))
+    parents = torch.full((B, N), -1, dtype=torch.int64, device=device)
+    first = [1]
+    for d, width in enumerate(w.widths):
+        first.append(first[-1] + width)
+    for d, width in enumerate(w.widths):
+        lo, hi = first[d], first[d + 1]
+        plo, phi = (0, 1) if d == 0 else (first[d - 1], first[d])
+        parents[:, lo:hi] = torch.randint(plo, phi, (B, width), generator=gen, device=device)
+    par_cpu = parents.cpu()
+    # rank of each node among its siblings (by node index)
+    rank = torch.zeros((B, N), dtype=torch.int64)
+    for b in range(B):
+        seen = {}
+        for n in range(1, N):
+            pnode = int(par_cpu[b, n])
+            rank[b, n] = seen.get(pnode, 0)
+            seen[pnode] = int(rank[b, n]) + 1
+    kmax = int(rank.max()) + 1 if N > 1 else 1
+    rank = rank.to(device)
+    target = torch.empty((B, N, V), dtype=sdt, device=device)
+    tokens = torch.zeros((B, N), dtype=torch.int64, device=device)
+    for b0 in range(0, B, seq_block):
+        b1 = min(B, b0 + seq_block)
+        nb = b1 - b0
+        t = torch.randn((nb, N, V), generator=gen, device=device) * w.target_sigma
+        if bias is not None:
+            t += bias
+        target[b0:b1] = t.to(sdt)
+        d = target[b0:b1].to(torch.float32) + \
+            torch.randn((nb, N, V), generator=gen, device=device) * w.draft_sigma
+        top = d.topk(kmax, dim=-1).indices  # [nb, N, kmax]
+        del t, d
+        par = parents[b0:b1].clamp(min=0)
+        cand = torch.gather(top, 1, par[:, :, None].expand(nb, N, kmax))  # parent's list
+        tokens[b0:b1] = torch.gather(cand, 2, rank[b0:b1, :, None]).squeeze(2)
+    tokens[:, 0] = 0
+    return TreeBatch(w, target.contiguous(), parents.to(torch.int32).contiguous(),
+                     tokens.to(torch.int32).contiguous(),
+                     torch.full((B,), N, dtype=torch.int32, device=device))
+
+
+def tree_to_host_arrays(batch: TreeBatch) -> dict:
+    import numpy as np
+
+    t = batch.target.detach().cpu().contiguous()
+    target = t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    return {"target": target,
+            "parents": batch.parents.cpu().numpy().astype(np.int32),
+            "tokens": batch.tokens.cpu().numpy().astype(np.int32),
+            "n_nodes": batch.n_nodes.cpu().numpy().astype(np.int32)}
+
+
 __all__ = [
+    "TreeWorkload", "TreeBatch", "TREE_WORKLOADS", "generate_tree", "tree_to_host_arrays",
     "Workload", "Batch", "WORKLOADS", "generate", "philox_seeds", "to_host_arrays",
     "DTYPE_F32", "DTYPE_BF16",
 ]

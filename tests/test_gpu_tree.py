@@ -1,0 +1,164 @@
+"""GPU parity of greedy tree verification (spec_verify_tree) against the oracle.
+
+Tree verification is integer and index work (row argmaxes, then a walk), so
+every output must match the oracle exactly: path tokens, path nodes, accepted
+depth, statuses and the per-node argmaxes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import bf16_bits
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+import speculative_decoding_verification_11_amd as sv  # noqa: E402
+from speculative_decoding_verification_11_amd import workloads as wl  # noqa: E402
+import oracle  # noqa: E402
+from oracle import parity  # noqa: E402
+
+DEV = "cuda:0"
+NTH = parity.host_threads()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_tree(target, parents, tokens, n_nodes):
+    out, path, n, aux = sv.spec_verify_tree(target, parents, tokens, n_nodes, aux=True)
+    torch.cuda.synchronize()
+    return dict(out_tokens=out.cpu().numpy(), path_nodes=path.cpu().numpy(),
+                num_accepted=n.cpu().numpy(), seq_status=aux["seq_status"].cpu().numpy(),
+                argmax=aux["argmax"].cpu().numpy())
+
+
+def to_dev(a):
+    if isinstance(a, np.ndarray) and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV).contiguous()
+    return torch.as_tensor(a).to(DEV).contiguous()
+
+
+def assert_tree_parity(g, r, label):
+    for key in ("seq_status", "num_accepted", "out_tokens", "path_nodes", "argmax"):
+        np.testing.assert_array_equal(g[key], r[key], err_msg=f"{label}: {key}")
+
+
+@pytest.mark.parametrize("name", ["t1", "t2", "t3"])
+def test_tree_parity_workloads(name):
+    w = wl.TREE_WORKLOADS[name]
+    tb = wl.generate_tree(w, DEV if name == "t3" else "cpu")
+    h = wl.tree_to_host_arrays(tb)
+    say(f"[case] tree {name} B={w.B} N={w.N} V={w.V} {w.dtype}")
+    g = run_tree(to_dev(tb.target), to_dev(tb.parents), to_dev(tb.tokens), to_dev(tb.n_nodes))
+    r = oracle.spec_tree_ref(h["target"], h["parents"], h["tokens"], h["n_nodes"], nthreads=NTH)
+    assert_tree_parity(g, r, name)
+    say(f"[parity] tree {name}: mean depth {g['num_accepted'].mean():.2f}")
+
+
+def _random_trees(rng, B, N, V, dtype, nn=None):
+    t = (rng.standard_normal((B, N, V)) * 2).astype(np.float32)
+    if dtype == "bf16":
+        t = bf16_bits(t)
+        tv = t.astype(np.uint32) << 16
+        tv = tv.view(np.float32)
+    else:
+        tv = t
+    amax = tv.argmax(axis=2)
+    par = np.full((B, N), -1, np.int32)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for n in range(1, N):
+            par[b, n] = rng.integers(max(0, n - 6), n)
+            tok[b, n] = amax[b, par[b, n]] if rng.random() < 0.7 else rng.integers(0, V)
+    nn = np.full(B, N, np.int32) if nn is None else np.asarray(nn, np.int32)
+    return t, par, tok, nn
+
+
+@pytest.mark.parametrize("V,dtype,N", [(1, "bf16", 5), (7, "f32", 9), (1001, "bf16", 17),
+                                       (16385, "bf16", 64), (8193, "f32", 33),
+                                       (50257, "bf16", 64)])
+def test_tree_odd_sizes_and_ragged_counts(V, dtype, N):
+    rng = np.random.default_rng(V + N)
+    B = 9
+    nn = rng.integers(1, N + 1, size=B)
+    t, par, tok, nn = _random_trees(rng, B, N, V, dtype, nn)
+    say(f"[case] tree V={V} {dtype} N={N}")
+    g = run_tree(to_dev(t), to_dev(par), to_dev(tok), to_dev(nn))
+    r = oracle.spec_tree_ref(t, par, tok, nn)
+    assert_tree_parity(g, r, f"V={V} N={N}")
+
+
+def test_tree_statuses():
+    rng = np.random.default_rng(4)
+    B, N, V = 6, 8, 64
+    t, par, tok, nn = _random_trees(rng, B, N, V, "f32")
+    nn[1] = 0
+    nn[2] = N + 1
+    par[3, 5] = 5  # a node cannot hang below itself
+    par[4, 2] = -1
+    tok[5, 7] = V + 1
+    g = run_tree(to_dev(t), to_dev(par), to_dev(tok), to_dev(nn))
+    assert list(g["seq_status"]) == [0, 2, 2, 5, 5, 1]
+    r = oracle.spec_tree_ref(t, par, tok, nn)
+    assert_tree_parity(g, r, "statuses")
+
+
+def test_chain_tree_equals_linear_greedy_path():
+    """A chain tree is a linear draft: spec_verify_tree and spec_verify at
+    temperature 0 must agree on every sequence."""
+    w = wl.WORKLOADS["c3"]
+    cb = wl.generate(w, "cpu")
+    B, k, V = w.B, w.k, w.V
+    h = wl.to_host_arrays(cb)
+    # plant argmax-matching drafts so that paths get long
+    tv = (h["target"].astype(np.uint32) << 16).view(np.float32)
+    am = tv.argmax(axis=2)
+    rng = np.random.default_rng(5)
+    g = np.where(rng.random((B, k)) < 0.8, am[:, :k], rng.integers(0, V, size=(B, k))).astype(np.int32)
+    L = h["draft_len"]
+    lin_out, lin_n = sv.spec_verify(cb.target.to(DEV), cb.draft.to(DEV),
+                                    torch.from_numpy(g).to(DEV),
+                                    torch.from_numpy(L).to(DEV),
+                                    torch.zeros(B, dtype=torch.float32, device=DEV), 0)
+    par = np.tile(np.arange(-1, k, dtype=np.int32), (B, 1))
+    tok = np.concatenate([np.zeros((B, 1), np.int32), g], axis=1)
+    gt = run_tree(cb.target.to(DEV), to_dev(par), to_dev(tok), to_dev((L + 1).astype(np.int32)))
+    np.testing.assert_array_equal(gt["num_accepted"], lin_n.cpu().numpy())
+    np.testing.assert_array_equal(gt["out_tokens"], lin_out.cpu().numpy())
+
+
+def test_tree_argmax_ties_bf16_and_single_node():
+    rng = np.random.default_rng(6)
+    B, N, V = 8, 12, 40000
+    t = bf16_bits((rng.standard_normal((B, N, V)) * 3).astype(np.float32))
+    tv = (t.astype(np.uint32) << 16).view(np.float32)
+    for b in range(B):
+        for n in range(N):
+            top = t[b, n, int(np.argmax(tv[b, n]))]
+            t[b, n, rng.choice(V, 1 + (b + n) % 4, replace=False)] = top
+    tv = (t.astype(np.uint32) << 16).view(np.float32)
+    am = tv.argmax(axis=2)
+    par = np.tile(np.array([-1, 0, 0, 1, 1, 2, 3, 3, 4, 6, 7, 9], np.int32), (B, 1))
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for n in range(1, N):
+            tok[b, n] = am[b, par[b, n]] if rng.random() < 0.75 else (am[b, par[b, n]] + 1) % V
+    nn = np.full(B, N, np.int32)
+    nn[0] = 1
+    g = run_tree(to_dev(t), to_dev(par), to_dev(tok), to_dev(nn))
+    r = oracle.spec_tree_ref(t, par, tok, nn)
+    assert_tree_parity(g, r, "ties")
+    assert g["num_accepted"][0] == 0 and g["out_tokens"][0, 0] == am[0, 0]
+
+
+def test_tree_deterministic():
+    w = wl.TREE_WORKLOADS["t2"]
+    tb = wl.generate_tree(w, DEV)
+    args = (tb.target, tb.parents, tb.tokens, tb.n_nodes)
+    first = run_tree(*args)
+    for _ in range(3):
+        again = run_tree(*args)
+        for key in first:
+            assert np.array_equal(first[key], again[key]), key
