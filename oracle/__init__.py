@@ -18,6 +18,8 @@ Parity status of each function (what pins it is in the tests):
   tree_greedy          pinned: chain trees equal round_greedy; brute-force path
                        enumeration; a hand-worked tree; planted mistakes
   spec_tree_ref        pinned: argmax_row per node + tree_greedy, statuses
+  prompt_lookup        pinned: brute force over all windows, hand-worked
+                       contexts, invariants, planted mistakes
 """
 from __future__ import annotations
 
@@ -89,6 +91,13 @@ def _load():
         lib.spec_tree_ref.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int64, P, P, P, P, P]
         lib.spec_tree_ref.restype = ctypes.c_int
+        lib.ref_prompt_lookup.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, P, P, P]
+        lib.ref_prompt_lookup.restype = ctypes.c_int
+        lib.spec_prompt_lookup_ref.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               P, P, P, P]
+        lib.spec_prompt_lookup_ref.restype = None
         _lib = lib
         return lib
 
@@ -294,4 +303,34 @@ def spec_tree_ref(target: np.ndarray, parents: np.ndarray, tokens: np.ndarray, n
         rcs = list(ex.map(lambda b0: run(b0, min(B, b0 + step)), range(0, B, step)))
     if any(rcs):
         raise MemoryError("oracle scratch allocation failed")
+    return res
+
+
+def prompt_lookup(ctx, n_min: int, n_max: int, k: int):
+    """Prompt-lookup proposal for one context. Returns (tokens, match_n, match_s)."""
+    c = np.ascontiguousarray(np.asarray(ctx, dtype=np.int32).reshape(-1))
+    T = c.shape[0]
+    buf = c if T else np.zeros(1, dtype=np.int32)
+    d = np.full(max(k, 1), -1, dtype=np.int32)
+    mn = ctypes.c_int(0)
+    ms = ctypes.c_int(-1)
+    n = _load().ref_prompt_lookup(_ptr(buf), T, n_min, n_max, k, _ptr(d), ctypes.byref(mn),
+                                  ctypes.byref(ms))
+    return d[:n].copy(), int(mn.value), int(ms.value)
+
+
+def spec_prompt_lookup_ref(contexts: np.ndarray, ctx_len, n_min: int, n_max: int, k: int) -> dict:
+    """Prompt lookup for a batch: contexts [B, T_max] int32, ctx_len [B]."""
+    c = np.ascontiguousarray(np.asarray(contexts, dtype=np.int32))
+    B, T_max = c.shape
+    lens = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int32).reshape(B))
+    res = dict(draft_tokens=np.full((B, max(k, 0)), -1, dtype=np.int32),
+               draft_len=np.zeros(B, dtype=np.int32), match_n=np.zeros(B, dtype=np.int32),
+               match_s=np.full(B, -1, dtype=np.int32))
+    if B == 0:
+        return res
+    dt = res["draft_tokens"] if k > 0 else np.zeros((B, 1), dtype=np.int32)
+    _load().spec_prompt_lookup_ref(_ptr(c), _ptr(lens), B, T_max, n_min, n_max, k, _ptr(dt),
+                                   _ptr(res["draft_len"]), _ptr(res["match_n"]),
+                                   _ptr(res["match_s"]))
     return res

@@ -45,6 +45,11 @@
  *       scores the token that follows node n's path.
  *   T2  a tree round keeps the deepest accepted node, the lowest node index
  *       among equally deep ones.
+ *   P1  prompt lookup: n-gram sizes are tried from n_max down to n_min; for
+ *       a size n the match is the most recent occurrence of the context's
+ *       last n tokens that ends before the last token; the proposal is the
+ *       (up to k) tokens that followed it, cut at the end of the context.
+ *       No match at any size proposes nothing.
  */
 #include <math.h>
 #include <stdint.h>
@@ -529,4 +534,70 @@ int spec_tree_ref(const void *target, int dtype, const int32_t *parents, const i
     }
     free(amax);
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Prompt-lookup drafting for one context ([ART] "n-gram and prompt     */
+/* lookup: no model at all": search the existing context for a recent   */
+/* matching n-gram and propose the tokens that followed it last time;   */
+/* [TAI] "Drafts and limits", n-gram / prompt lookup; reading P1).      */
+/*                                                                      */
+/*   ctx[0..T-1]: the context. For n = n_max down to n_min, and for     */
+/*   start s = T-n-1 down to 0 (latest first), the window ctx[s..s+n-1] */
+/*   matches if it equals the last n tokens ctx[T-n..T-1]; the first    */
+/*   match proposes ctx[s+n .. min(s+n+k, T) - 1].                      */
+/* Writes the proposal to draft[0..len-1] and returns len (0 if none);  */
+/* *match_n and *match_s get the n-gram size and start (0 and -1 when   */
+/* nothing matched).                                                    */
+/* ------------------------------------------------------------------ */
+int ref_prompt_lookup(const int32_t *ctx, int T, int n_min, int n_max, int k, int32_t *draft,
+                      int *match_n, int *match_s)
+{
+    *match_n = 0;
+    *match_s = -1;
+    for (int n = n_max; n >= n_min; n--) {
+        if (n > T - 1)
+            continue;  /* no window of this size ends before the last token */
+        for (int s = T - n - 1; s >= 0; s--) {
+            int same = 1;
+            for (int j = 0; j < n; j++)
+                if (ctx[s + j] != ctx[T - n + j]) {
+                    same = 0;
+                    break;
+                }
+            if (!same)
+                continue;
+            int len = 0;
+            for (int j = s + n; j < T && len < k; j++)
+                draft[len++] = ctx[j];
+            *match_n = n;
+            *match_s = s;
+            return len;
+        }
+    }
+    return 0;
+}
+
+/* Prompt lookup for a batch: contexts [B, T_max] (row b holds ctx_len[b]  */
+/* tokens; a length outside [0, T_max] proposes nothing); draft_tokens    */
+/* [B, k] (-1 after the proposal), draft_len [B], match_n [B],            */
+/* match_s [B] (may be NULL).                                            */
+void spec_prompt_lookup_ref(const int32_t *contexts, const int32_t *ctx_len, int32_t B,
+                            int32_t T_max, int32_t n_min, int32_t n_max, int32_t k,
+                            int32_t *draft_tokens, int32_t *draft_len, int32_t *match_n,
+                            int32_t *match_s)
+{
+    for (int32_t b = 0; b < B; b++) {
+        int32_t *d = draft_tokens + (size_t)b * k;
+        for (int j = 0; j < k; j++)
+            d[j] = -1;
+        const int T = ctx_len[b];
+        int mn = 0, ms = -1, len = 0;
+        if (T >= 0 && T <= T_max)
+            len = ref_prompt_lookup(contexts + (size_t)b * T_max, T, n_min, n_max, k, d, &mn,
+                                    &ms);
+        draft_len[b] = len;
+        if (match_n) match_n[b] = mn;
+        if (match_s) match_s[b] = ms;
+    }
 }
