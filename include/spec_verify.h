@@ -237,6 +237,44 @@ int spec_verify_tree(const void *target_logits, int32_t dtype, const int32_t *pa
                      const spec_tree_aux_t *aux, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* ------------------------------------------------------------------------
+ * Prompt-lookup drafting.
+ *
+ * The model-free drafter that precedes verification on copy-heavy tasks:
+ * search the existing context for a recent occurrence of its own last n
+ * tokens and propose the tokens that followed it ("Speculative Decoding and
+ * the Art of Fast LLM Inference", "n-gram and prompt lookup: no model at
+ * all"; techaiinterview.com, "Drafts and limits", n-gram / prompt lookup).
+ * Sizes are tried from n_max down to n_min; for a size, the most recent
+ * occurrence that ends before the context's last token wins, and up to k of
+ * the tokens after it are proposed (fewer if the context ends first). No
+ * occurrence at any size proposes nothing.
+ * ---------------------------------------------------------------------- */
+
+/* Largest supported n-gram size. */
+#define SPEC_MAX_NGRAM 16
+
+/*
+ *   contexts      [B, T_max] int32 row-major device memory; row b holds
+ *                 context_len[b] tokens (any int32 values), the rest is
+ *                 never read.
+ *   context_len   [B] int32; a length outside [0, T_max] proposes nothing.
+ *   n_min, n_max  1 <= n_min <= n_max <= SPEC_MAX_NGRAM.
+ *   k             0 <= k <= SPEC_MAX_K: most tokens proposed.
+ *   draft_tokens  [B, k] out: the proposal, then -1 (ready for spec_verify's
+ *                 draft_tokens); may be NULL when k == 0.
+ *   draft_len     [B] out: proposal length in [0, k] (spec_verify's
+ *                 draft_len).
+ *   match_n       [B] out or NULL: matched n-gram size, 0 if none.
+ *   match_start   [B] out or NULL: start of the matched occurrence, -1 if
+ *                 none.
+ * One kernel, no workspace; errors and streams as for spec_verify.
+ */
+int spec_prompt_lookup(const int32_t *contexts, const int32_t *context_len, int32_t B,
+                       int32_t T_max, int32_t n_min, int32_t n_max, int32_t k,
+                       int32_t *draft_tokens, int32_t *draft_len, int32_t *match_n,
+                       int32_t *match_start, void *stream);
+
 /* Static, human-readable text for a spec_status_t value. */
 const char *spec_verify_strerror(int status);
 

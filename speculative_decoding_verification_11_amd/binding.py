@@ -21,6 +21,7 @@ F32 = 0
 BF16 = 1
 MAX_K = 63
 MAX_TREE = 64
+MAX_NGRAM = 16
 
 SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE = range(6)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
@@ -28,8 +29,8 @@ DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
 
 EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_workspace_size",
-            "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_verify_strerror",
-            "spec_verify_version")
+            "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_prompt_lookup",
+            "spec_verify_strerror", "spec_verify_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -94,6 +95,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.spec_verify_tree.argtypes = [P, i32, P, P, P, i32, i32, i32, P, P, P,
                                          ctypes.POINTER(TreeAux), P, ctypes.c_size_t, P]
         lib.spec_verify_tree.restype = ctypes.c_int
+        lib.spec_prompt_lookup.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P]
+        lib.spec_prompt_lookup.restype = ctypes.c_int
         lib.spec_verify_strerror.argtypes = [ctypes.c_int]
         lib.spec_verify_strerror.restype = ctypes.c_char_p
         lib.spec_verify_version.argtypes = []
@@ -303,3 +306,43 @@ def spec_verify_tree(target: torch.Tensor, parents: torch.Tensor, tokens: torch.
     if aux:
         return out_tokens, path_nodes, num_acc, aux_out
     return out_tokens, path_nodes, num_acc
+
+
+def spec_prompt_lookup(contexts: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int,
+                       k: int, *, match: bool = False, out: Optional[tuple] = None):
+    """Prompt-lookup drafting (C entry point spec_prompt_lookup).
+
+    contexts [B, T_max] int32 (row b holds context_len[b] tokens), context_len
+    [B] int32. Returns (draft_tokens [B, k], draft_len [B]), plus (match_n,
+    match_start) when ``match`` is true.
+    """
+    if contexts.dim() != 2:
+        raise ValueError("contexts must be [B, T_max]")
+    B, T_max = contexts.shape
+    dev = contexts.device
+    if dev.type != "cuda":
+        raise ValueError("contexts must be a GPU tensor")
+    for name, t, shape in (("contexts", contexts, (B, T_max)), ("context_len", context_len, (B,))):
+        if (tuple(t.shape) != shape or t.dtype != torch.int32 or t.device != dev
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous {list(shape)} int32 on {dev}")
+    if out is None:  # sizes are checked by the library
+        draft = torch.empty((B, max(k, 0)), dtype=torch.int32, device=dev)
+        dlen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        draft, dlen = out
+    mn = ms = None
+    if match:
+        mn = torch.empty((B,), dtype=torch.int32, device=dev)
+        ms = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = library().spec_prompt_lookup(
+            contexts.data_ptr(), context_len.data_ptr(), B, T_max, n_min, n_max, k,
+            draft.data_ptr() if k > 0 else None, dlen.data_ptr(),
+            _ptr(mn), _ptr(ms), stream)
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    if match:
+        return draft, dlen, mn, ms
+    return draft, dlen

@@ -418,7 +418,79 @@ def tree_to_host_arrays(batch: TreeBatch) -> dict:
             "n_nodes": batch.n_nodes.cpu().numpy().astype(np.int32)}
 
 
+# ---------------------------------------------------------------------------
+# Contexts for prompt lookup.
+#
+# Recipe (copy-heavy text, as in summarisation, code editing or RAG): a
+# context is a run of segments; each is, with probability copy_p, a copy of
+# an earlier stretch of the same context (start uniform, length geometric
+# with mean copy_len), else fresh tokens uniform in [0, vocab) (length
+# geometric with mean fresh_len). The context then ends part-way through one
+# more copied stretch, so its last tokens have occurred before. Lengths are
+# U{T_max/2..T_max} per sequence. numpy Generator seeded per workload.
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class LookupWorkload:
+    name: str
+    B: int
+    T_max: int
+    vocab: int
+    n_min: int
+    n_max: int
+    k: int
+    copy_p: float = 0.3
+    copy_len: int = 32
+    fresh_len: int = 64
+    seed: int = 0
+    description: str = ""
+
+
+LOOKUP_WORKLOADS = {
+    "p1": LookupWorkload("p1", B=8, T_max=256, vocab=50, n_min=1, n_max=3, k=5, copy_len=8,
+                         fresh_len=16, seed=8001,
+                         description="B=8 T<=256 vocab 50, n 1..3, k 5"),
+    "p2": LookupWorkload("p2", B=64, T_max=4096, vocab=32000, n_min=1, n_max=4, k=7, seed=8002,
+                         description="B=64 T<=4096 vocab 32000, n 1..4, k 7"),
+    "p3": LookupWorkload("p3", B=1024, T_max=32768, vocab=128256, n_min=1, n_max=4, k=7,
+                         seed=8003,
+                         description="B=1024 T<=32768 vocab 128256, n 1..4, k 7, copy-heavy"),
+}
+
+
+def generate_contexts(w: LookupWorkload):
+    """(contexts [B, T_max] int32, context_len [B] int32) as numpy arrays; the
+    unused tail of a row holds -7 (never read)."""
+    import numpy as np
+
+    rng = np.random.default_rng(w.seed)
+    ctx = np.full((w.B, w.T_max), -7, dtype=np.int32)
+    lens = rng.integers(w.T_max // 2, w.T_max + 1, size=w.B).astype(np.int32)
+    for b in range(w.B):
+        T = int(lens[b])
+        row = ctx[b]
+        pos = 0
+        while pos < T:
+            if pos > 8 and rng.random() < w.copy_p:
+                ln = min(int(rng.geometric(1.0 / w.copy_len)), T - pos)
+                src = int(rng.integers(0, pos))
+                for j in range(ln):  # may overlap itself: copy token by token
+                    row[pos + j] = row[src + j]
+            else:
+                ln = min(int(rng.geometric(1.0 / w.fresh_len)), T - pos)
+                row[pos:pos + ln] = rng.integers(0, w.vocab, size=ln)
+            pos += ln
+        # end inside a copied stretch: overwrite the last few tokens by a copy
+        if T > 16:
+            ln = int(rng.integers(2, min(12, T // 4) + 1))
+            src = int(rng.integers(0, T - ln - 1))
+            row[T - ln:T] = row[src:src + ln].copy()
+    return ctx, lens
+
+
 __all__ = [
+    "LookupWorkload", "LOOKUP_WORKLOADS", "generate_contexts",
     "TreeWorkload", "TreeBatch", "TREE_WORKLOADS", "generate_tree", "tree_to_host_arrays",
     "Workload", "Batch", "WORKLOADS", "generate", "philox_seeds", "to_host_arrays",
     "DTYPE_F32", "DTYPE_BF16",
