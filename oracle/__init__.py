@@ -15,6 +15,9 @@ Parity status of each function (what pins it is in the tests):
   round_greedy         pinned: worked rounds, argmax agreement by hand
   spec_verify_ref      pinned: chi-square of emitted tokens against p, accepted
                        length against the closed form, worked rounds
+  nucleus_row          pinned: brute force over level prefixes, closed forms
+                       (uniform and two-level rows), top_p = 1 is the identity,
+                       planted mistakes
   tree_greedy          pinned: chain trees equal round_greedy; brute-force path
                        enumeration; a hand-worked tree; planted mistakes
   spec_tree_ref        pinned: argmax_row per node + tree_greedy, statuses
@@ -86,6 +89,12 @@ def _load():
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                         ctypes.c_uint32] + [P] * 11
         lib.spec_verify_ref.restype = ctypes.c_int
+        lib.ref_nucleus_row.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_double, P, P, P]
+        lib.ref_nucleus_row.restype = ctypes.c_double
+        lib.spec_verify_topp_ref.argtypes = [P, P, ctypes.c_int, P, P, P, P, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                             ctypes.c_uint32] + [P] * 12
+        lib.spec_verify_topp_ref.restype = ctypes.c_int
         lib.ref_tree_greedy.argtypes = [P, P, P, ctypes.c_int, P, P]
         lib.ref_tree_greedy.restype = ctypes.c_int
         lib.spec_tree_ref.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int32, ctypes.c_int32,
@@ -148,6 +157,18 @@ def draw_inverse_cdf(w: np.ndarray, v: float):
     return int(x), float(S[0]), float(m[0]), bool(fb[0])
 
 
+def nucleus_row(row: np.ndarray, p: np.ndarray, top_p: float):
+    """Nucleus filter of one row (reading TP1). row: the logits; p: their
+    softmax. Returns (filtered p, kept mass, threshold logit, margin)."""
+    row, dt = _logits(row)
+    q = np.ascontiguousarray(np.asarray(p, dtype=np.float64)).copy()
+    thr = np.zeros(1)
+    mg = np.zeros(1)
+    kept = _load().ref_nucleus_row(_ptr(row), dt, row.shape[-1], float(top_p), _ptr(q), _ptr(thr),
+                                   _ptr(mg))
+    return q, float(kept), float(thr[0]), float(mg[0])
+
+
 def round_sampling(p: np.ndarray, q: np.ndarray, g, u, v):
     """One sampling round from explicit probabilities and uniforms.
 
@@ -196,7 +217,7 @@ def round_greedy(amax, g):
 
 def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
                     draft_len, temperature, seed: int, seq_base: int = 0,
-                    nthreads: int = 1) -> dict:
+                    nthreads: int = 1, top_p=None) -> dict:
     """The whole step on host arrays (see spec_verify_ref.c for the contract).
 
     target [B, k+1, V] and draft [B, k, V] are float32 or uint16 (bf16 bits).
@@ -216,6 +237,9 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         lens = np.ascontiguousarray(np.asarray(draft_len, dtype=np.int32).reshape(B))
     temp = np.asarray(temperature, dtype=np.float32)
     temp = np.ascontiguousarray(np.broadcast_to(temp, (B,)).copy())
+    tp = None
+    if top_p is not None:
+        tp = np.ascontiguousarray(np.broadcast_to(np.asarray(top_p, dtype=np.float32), (B,)).copy())
 
     res = dict(
         out_tokens=np.full((B, k + 1), -1, dtype=np.int32),
@@ -230,18 +254,29 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         draw_row=np.full(B, -1, dtype=np.int32),
         draw_kind=np.zeros(B, dtype=np.int32),
     )
+    if tp is not None:
+        res["margin_nucleus"] = np.full((B, 2 * k + 1), np.nan)
     lib = _load()
 
     def run(b0: int, b1: int) -> int:
         if b1 <= b0:
             return 0
         sl = slice(b0, b1)
+        if tp is None:
+            outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
+                                         "argmax", "resid_mass", "margin_accept", "margin_draw",
+                                         "draw_row", "draw_kind")]
+            return lib.spec_verify_ref(
+                _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
+                _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]),
+                b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
+                ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs])
         outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
                                      "argmax", "resid_mass", "margin_accept", "margin_draw",
-                                     "draw_row", "draw_kind")]
-        return lib.spec_verify_ref(
+                                     "margin_nucleus", "draw_row", "draw_kind")]
+        return lib.spec_verify_topp_ref(
             _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
-            _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]),
+            _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]), _ptr(tp[sl]),
             b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
             ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs])
 

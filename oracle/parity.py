@@ -36,18 +36,20 @@ def host_threads(cap: int = 16) -> int:
     return max(1, min(cap, n))
 
 
-def oracle_on(host: dict, seed: int, seqs=None, nthreads: int = 1) -> dict:
+def oracle_on(host: dict, seed: int, seqs=None, nthreads: int = 1, top_p=None) -> dict:
     """Run the oracle on all sequences, or on the listed ones (each with its
-    own global index as the Philox sequence index)."""
+    own global index as the Philox sequence index). ``top_p``: None, or [B]
+    nucleus parameters."""
     t, d, g, L, tau = (host["target"], host["draft"], host["draft_tokens"], host["draft_len"],
                        host["temperature"])
+    tp = None if top_p is None else np.broadcast_to(np.asarray(top_p, np.float32), (len(L),))
     if seqs is None:
-        return spec_verify_ref(t, d, g, L, tau, seed, seq_base=0, nthreads=nthreads)
+        return spec_verify_ref(t, d, g, L, tau, seed, seq_base=0, nthreads=nthreads, top_p=tp)
     seqs = [int(b) for b in seqs]
 
     def one(b):
         return spec_verify_ref(t[b:b + 1], d[b:b + 1], g[b:b + 1], L[b:b + 1], tau[b:b + 1], seed,
-                               seq_base=b)
+                               seq_base=b, top_p=None if tp is None else tp[b:b + 1])
 
     if nthreads > 1:
         with ThreadPoolExecutor(max_workers=nthreads) as ex:
@@ -170,6 +172,17 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
                 rep.mismatches.append(f"{tag}: greedy draw_kind {gpu['draw_kind'][b]}")
             rep.compared_tokens += r_n + 1
             continue
+        # a nucleus boundary within the band on a row the round depends on
+        # (target rows 0..n, draft rows 0..min(n, L-1)) may legitimately
+        # differ: the whole sequence counts as one flagged draw
+        if "margin_nucleus" in ref:
+            mn = ref["margin_nucleus"][j]
+            rows = list(range(min(r_n, L) + 1)) + [k + 1 + i for i in range(min(r_n + 1, L))]
+            near = [mn[x] for x in rows if not np.isnan(mn[x]) and mn[x] < band]
+            if near:
+                agree = (g_n == r_n and np.array_equal(g_out, r_out))
+                draw(min(near), agree, f"{tag}: nucleus boundary")
+                continue
         # sampling: gathered probabilities at every valid position
         for i in range(L):
             for key in ("p_g", "q_g"):

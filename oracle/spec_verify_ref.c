@@ -45,6 +45,13 @@
  *       scores the token that follows node n's path.
  *   T2  a tree round keeps the deepest accepted node, the lowest node index
  *       among equally deep ones.
+ *   TP1 top-p ([ART] "Why It Stays Exact", key limitation: verification
+ *       must use the target's own sampling parameters, temperature and
+ *       top-p): after the temperature softmax, keep whole probability
+ *       levels -- tokens of equal logit -- from the top until their mass
+ *       reaches top_p times the row's mass; ties at the boundary are all
+ *       kept. The kept tokens are renormalised and the rest get 0. The
+ *       draft row is filtered with the same top_p. top_p >= 1 keeps all.
  *   P1  prompt lookup: n-gram sizes are tried from n_max down to n_min; for
  *       a size n the match is the most recent occurrence of the context's
  *       last n tokens that ends before the last token; the proposal is the
@@ -125,6 +132,76 @@ int64_t ref_argmax_row(const void *row, int dtype, int64_t V)
         }
     }
     return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* Nucleus (top-p) filter of one probability row (reading TP1).          */
+/*   row: the logits (for the levels), p: the row's softmax, filtered    */
+/*   in place. Levels are visited from the largest logit down; each      */
+/*   level's mass is added to the running total until it reaches        */
+/*   top_p * (sum of p); that level and all above it are kept.           */
+/* Returns the kept mass before renormalisation; *thr = the boundary     */
+/* logit (keep x >= *thr); *margin = distance of top_p * total to the    */
+/* running mass just before and just after the boundary level, relative */
+/* to total (small: the boundary is a near tie).                        */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    double x;
+    int64_t i;
+} ref_level_item;
+
+static int ref_level_desc(const void *a, const void *b)
+{
+    const ref_level_item *u = a, *v = b;
+    if (u->x != v->x)
+        return u->x > v->x ? -1 : 1;
+    return u->i < v->i ? -1 : (u->i > v->i);
+}
+
+double ref_nucleus_row(const void *row, int dtype, int64_t V, double top_p, double *p, double *thr,
+                       double *margin)
+{
+    double total = 0.0;
+    for (int64_t x = 0; x < V; x++)
+        total += p[x];
+    *thr = -INFINITY;
+    *margin = NAN;
+    if (!(top_p < 1.0))
+        return total;
+    ref_level_item *it = malloc(sizeof(ref_level_item) * (size_t)V);
+    if (!it)
+        return NAN;
+    for (int64_t x = 0; x < V; x++) {
+        it[x].x = ref_logit(row, dtype, (size_t)x);
+        if (it[x].x == 0.0)
+            it[x].x = 0.0; /* -0 and +0 are one level */
+        it[x].i = x;
+    }
+    qsort(it, (size_t)V, sizeof(ref_level_item), ref_level_desc);
+    const double target = top_p * total;
+    double cum = 0.0, kept = total;
+    for (int64_t a = 0; a < V;) {
+        int64_t b = a;
+        double level = 0.0;
+        while (b < V && it[b].x == it[a].x)
+            level += p[it[b++].i];
+        const double before = cum;
+        cum += level;
+        if (cum >= target) {
+            *thr = it[a].x;
+            kept = cum;
+            const double m1 = (cum - target) / total, m2 = (target - before) / total;
+            *margin = m1 < m2 ? m1 : m2;
+            break;
+        }
+        a = b;
+    }
+    free(it);
+    for (int64_t x = 0; x < V; x++) {
+        double lx = ref_logit(row, dtype, (size_t)x);
+        p[x] = lx >= *thr ? p[x] / kept : 0.0;
+    }
+    return kept;
 }
 
 /* ------------------------------------------------------------------ */
@@ -318,13 +395,14 @@ int ref_round_greedy(const int64_t *amax, const int32_t *g, int L, int32_t *out)
 /*   draw_row [B], draw_kind [B]: row of the final token and REF_DRAW_*  */
 /* Returns 0, or -1 if a scratch allocation failed.                     */
 /* ------------------------------------------------------------------ */
-int spec_verify_ref(const void *target, const void *draft, int dtype,
-                    const int32_t *draft_tokens, const int32_t *draft_len,
-                    const float *temperature, int32_t B, int32_t k, int64_t V, uint64_t seed,
-                    uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
-                    int32_t *seq_status, double *p_g, double *q_g, int32_t *argmax,
-                    double *resid_mass, double *margin_accept, double *margin_draw,
-                    int32_t *draw_row, int32_t *draw_kind)
+static int verify_batch(const void *target, const void *draft, int dtype,
+                        const int32_t *draft_tokens, const int32_t *draft_len,
+                        const float *temperature, const float *top_p, int32_t B, int32_t k,
+                        int64_t V, uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                        int32_t *num_accepted, int32_t *seq_status, double *p_g, double *q_g,
+                        int32_t *argmax, double *resid_mass, double *margin_accept,
+                        double *margin_draw, double *margin_nucleus, int32_t *draw_row,
+                        int32_t *draw_kind)
 {
     const size_t esz = dtype == REF_F32 ? 4 : 2;
     double *p = malloc(sizeof(double) * (size_t)(k + 1) * (size_t)V);
@@ -356,6 +434,8 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
         }
         for (int i = 0; i <= k; i++)
             if (argmax) argmax[(size_t)b * (k + 1) + i] = -1;
+        for (int i = 0; i < 2 * k + 1; i++)
+            if (margin_nucleus) margin_nucleus[(size_t)b * (2 * k + 1) + i] = NAN;
         if (resid_mass) resid_mass[b] = NAN;
         if (margin_draw) margin_draw[b] = NAN;
         if (draw_row) draw_row[b] = -1;
@@ -392,6 +472,21 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
                 ref_softmax_row(trow0 + (size_t)i * V * esz, dtype, V, tau, p + (size_t)i * V);
             for (int i = 0; i < L; i++)
                 ref_softmax_row(drow0 + (size_t)i * V * esz, dtype, V, tau, q + (size_t)i * V);
+            if (top_p && top_p[b] < 1.0f) {
+                /* the same nucleus rule on every target and draft row */
+                const double tp = (double)top_p[b];
+                double thr, mg;
+                for (int i = 0; i <= L; i++) {
+                    ref_nucleus_row(trow0 + (size_t)i * V * esz, dtype, V, tp, p + (size_t)i * V,
+                                    &thr, &mg);
+                    if (margin_nucleus) margin_nucleus[(size_t)b * (2 * k + 1) + i] = mg;
+                }
+                for (int i = 0; i < L; i++) {
+                    ref_nucleus_row(drow0 + (size_t)i * V * esz, dtype, V, tp, q + (size_t)i * V,
+                                    &thr, &mg);
+                    if (margin_nucleus) margin_nucleus[(size_t)b * (2 * k + 1) + k + 1 + i] = mg;
+                }
+            }
             for (int i = 0; i < L; i++) {
                 if (p_g) p_g[(size_t)b * k + i] = p[(size_t)i * V + g[i]];
                 if (q_g) q_g[(size_t)b * k + i] = q[(size_t)i * V + g[i]];
@@ -423,6 +518,39 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
 
     free(p), free(q), free(w), free(u), free(v), free(amax), free(macc);
     return 0;
+}
+
+int spec_verify_ref(const void *target, const void *draft, int dtype,
+                    const int32_t *draft_tokens, const int32_t *draft_len,
+                    const float *temperature, int32_t B, int32_t k, int64_t V, uint64_t seed,
+                    uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
+                    int32_t *seq_status, double *p_g, double *q_g, int32_t *argmax,
+                    double *resid_mass, double *margin_accept, double *margin_draw,
+                    int32_t *draw_row, int32_t *draw_kind)
+{
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, B, k,
+                        V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+                        argmax, resid_mass, margin_accept, margin_draw, NULL, draw_row,
+                        draw_kind);
+}
+
+/* The whole step with nucleus filtering (reading TP1): top_p [B] fp32, 1  */
+/* or more (or a greedy sequence) filters nothing. margin_nucleus          */
+/* [B, 2k+1] (may be NULL): the nucleus margin of target row i (index i)   */
+/* and draft row i (index k+1+i), NaN where no filter was applied.         */
+int spec_verify_topp_ref(const void *target, const void *draft, int dtype,
+                         const int32_t *draft_tokens, const int32_t *draft_len,
+                         const float *temperature, const float *top_p, int32_t B, int32_t k,
+                         int64_t V, uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                         int32_t *num_accepted, int32_t *seq_status, double *p_g, double *q_g,
+                         int32_t *argmax, double *resid_mass, double *margin_accept,
+                         double *margin_draw, double *margin_nucleus, int32_t *draw_row,
+                         int32_t *draw_kind)
+{
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_p, B, k,
+                        V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+                        argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
+                        draw_row, draw_kind);
 }
 
 /* ------------------------------------------------------------------ */
