@@ -221,6 +221,8 @@ def main() -> int:
                     help="skip timing greedy tree verification (workload t3)")
     ap.add_argument("--no-lookup", action="store_true",
                     help="skip timing prompt-lookup drafting (workload p3)")
+    ap.add_argument("--no-top-p", action="store_true",
+                    help="skip timing the top-p entry point on the same batch")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
 
@@ -348,6 +350,30 @@ def main() -> int:
         }
         log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
             f"for {ee_bytes / 1e9:.3f} GB")
+    topp = None
+    if not args.no_top_p:
+        # The same batch with top-p 0.95 on every row (the drafted tokens were
+        # sampled without it, so a few land outside the draft's nucleus and
+        # end their sequence with status QZERO, as the contract says).
+        log(f"[bench] top-p 0.95: warmup {W} steps, timing {K} steps")
+        tp = torch.full((w.B,), 0.95, dtype=torch.float32, device="cuda:0")
+        for i in range(W):
+            step(i, fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i, fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
+        torch.cuda.synchronize()
+        tp_ms = (time.perf_counter() - t0) * 1e3 / K
+        _, _, aux_tp = sv.spec_verify_top_p(copies[0].target, copies[0].draft,
+                                            copies[0].draft_tokens, copies[0].draft_len,
+                                            copies[0].temperature, tp, seed, aux=True)
+        st = aux_tp["seq_status"].cpu()
+        topp = {"entry_point": "spec_verify_top_p", "top_p": 0.95,
+                "value": positions / (tp_ms * 1e-3), "unit": "positions/s", "ms_per_step": tp_ms,
+                "rows_filtered": t_rows + d_rows,
+                "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum())}
+        log(f"[bench] top-p {tp_ms:.4f} ms/step")
     tree = None
     if not args.no_tree:
         tree = bench_tree(hip, ev, K, W)
@@ -398,6 +424,8 @@ def main() -> int:
     }
     if early is not None:
         result["early_exit"] = early
+    if topp is not None:
+        result["top_p"] = topp
     if tree is not None:
         result["tree"] = tree
     if lookup is not None:

@@ -80,8 +80,9 @@ enum {
                             /* draft probability is 0 (the acceptance ratio  */
                             /* is undefined; thelatentsource.com accept_token */
                             /* raises in this case)                          */
-    SPEC_SEQ_BAD_TREE = 5   /* spec_verify_tree: a parent index outside      */
+    SPEC_SEQ_BAD_TREE = 5,  /* spec_verify_tree: a parent index outside      */
                             /* [0, n) for node n                             */
+    SPEC_SEQ_BAD_TOP_P = 6  /* spec_verify_top_p: top_p NaN or not positive  */
 };
 
 /* How the last emitted token of a sequence was produced (aux->draw_kind). */
@@ -184,6 +185,34 @@ int spec_verify_early_exit(const void *target_logits, const void *draft_logits, 
                            uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
                            int32_t *num_accepted, const spec_verify_aux_t *aux,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The step with top-p (nucleus) sampling parameters. Verification must use
+ * the target's own sampling parameters, temperature and top-p, for the
+ * output to follow the target ("Speculative Decoding and the Art of Fast
+ * LLM Inference", "Why It Stays Exact", key limitation). For a sampling
+ * sequence with 0 < top_p[b] < 1, every target row i <= L and draft row
+ * i < L is filtered after the temperature softmax: whole probability levels
+ * (tokens of equal logit) are kept from the largest logit down until their
+ * mass reaches top_p of the row's mass (tokens tied at the boundary are all
+ * kept), and the kept tokens are renormalised. The acceptance test, the
+ * residual max(0, p - q) and the bonus draw then use the filtered p and q;
+ * a drafted token outside the draft row's nucleus has q(g) = 0 and gives
+ * SPEC_SEQ_QZERO. top_p[b] >= 1 filters nothing; greedy sequences ignore
+ * it; NaN or top_p[b] <= 0 gives SPEC_SEQ_BAD_TOP_P (checked after the
+ * temperature, before the tokens). top_p is [B] fp32 device memory and
+ * must not be NULL; everything else is as for spec_verify, with aux->q_g
+ * and p_g the filtered probabilities and resid_mass the filtered mass.
+ * The nucleus of a row is found exactly (a radix select over the logits,
+ * with the row masses summed in 64-bit fixed point), at the cost of
+ * reading each filtered row two more times (three for fp32 logits).
+ */
+int spec_verify_top_p(const void *target_logits, const void *draft_logits, int32_t dtype,
+                      const int32_t *draft_tokens, const int32_t *draft_len,
+                      const float *temperature, const float *top_p, int32_t B, int32_t k,
+                      int32_t V, uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                      int32_t *num_accepted, const spec_verify_aux_t *aux, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Greedy verification of candidate trees.

@@ -41,7 +41,7 @@ _LIB = os.path.join(_HERE, "_build", "libspecverify_oracle.so")
 F32 = 0
 BF16 = 1
 
-SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE = range(6)
+SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE, SEQ_BAD_TOP_P = range(7)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 _lock = threading.Lock()

@@ -71,7 +71,8 @@ enum {
     REF_SEQ_BAD_LEN = 2,
     REF_SEQ_BAD_TEMP = 3,
     REF_SEQ_QZERO = 4,
-    REF_SEQ_BAD_TREE = 5  /* a parent index outside [0, n) for node n */
+    REF_SEQ_BAD_TREE = 5, /* a parent index outside [0, n) for node n */
+    REF_SEQ_BAD_TOP_P = 6 /* top_p NaN or not positive                */
 };
 
 enum {
@@ -442,13 +443,15 @@ static int verify_batch(const void *target, const void *draft, int dtype,
         if (draw_kind) draw_kind[b] = REF_DRAW_NONE;
         num_accepted[b] = 0;
 
-        /* Input checks, in this order: length, temperature, tokens. A
-         * temperature must be 0 (greedy) or a normal positive fp32. */
+        /* Input checks, in this order: length, temperature, top-p, tokens.
+         * A temperature must be 0 (greedy) or a normal positive fp32. */
         int status = REF_SEQ_OK;
         if (L < 0 || L > k)
             status = REF_SEQ_BAD_LEN;
         else if (!(tau == 0.0 || (tau >= (double)1.17549435e-38f && isfinite(tau))))
             status = REF_SEQ_BAD_TEMP;
+        else if (top_p && !(top_p[b] > 0.0f))
+            status = REF_SEQ_BAD_TOP_P;
         else
             for (int i = 0; i < L; i++)
                 if (g[i] < 0 || (int64_t)g[i] >= V)

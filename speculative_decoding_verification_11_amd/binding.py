@@ -23,12 +23,13 @@ MAX_K = 63
 MAX_TREE = 64
 MAX_NGRAM = 16
 
-SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE = range(6)
+SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE, SEQ_BAD_TOP_P = range(7)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
 
-EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_workspace_size",
+EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_top_p",
+            "spec_verify_workspace_size",
             "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_prompt_lookup",
             "spec_verify_strerror", "spec_verify_version")
 
@@ -90,6 +91,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
                            ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
             fn.restype = ctypes.c_int
+        lib.spec_verify_top_p.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, u64, u32, P, P,
+                                          ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
+        lib.spec_verify_top_p.restype = ctypes.c_int
         lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.spec_verify_tree_workspace_size.restype = ctypes.c_size_t
         lib.spec_verify_tree.argtypes = [P, i32, P, P, P, i32, i32, i32, P, P, P,
@@ -152,8 +156,29 @@ def spec_verify_early_exit(target: torch.Tensor, draft: Optional[torch.Tensor],
                    seed, seq_base, aux, workspace, out, events)
 
 
+def spec_verify_top_p(target: torch.Tensor, draft: Optional[torch.Tensor],
+                      draft_tokens: Optional[torch.Tensor], draft_len: Optional[torch.Tensor] = None,
+                      temperature: Union[float, torch.Tensor] = 1.0,
+                      top_p: Union[float, torch.Tensor] = 1.0, seed: int = 0, *,
+                      seq_base: int = 0, aux: bool = False,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None,
+                      events: Optional[tuple] = None):
+    """spec_verify with top-p (nucleus) filtering of every target and draft
+    row (C entry point spec_verify_top_p). top_p: float or [B] float32."""
+    B = target.shape[0]
+    if isinstance(top_p, torch.Tensor):
+        tp = top_p
+        if (tuple(tp.shape) != (B,) or tp.dtype != torch.float32 or tp.device != target.device
+                or not tp.is_contiguous()):
+            raise ValueError(f"top_p must be contiguous [{B}] float32 on {target.device}")
+    else:
+        tp = torch.full((B,), float(top_p), dtype=torch.float32, device=target.device)
+    return _verify("spec_verify_top_p", target, draft, draft_tokens, draft_len, temperature, seed,
+                   seq_base, aux, workspace, out, events, top_p=tp)
+
+
 def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, seq_base, aux,
-            workspace, out, events):
+            workspace, out, events, top_p=None):
     """Verify B drafted continuations on the GPU.
 
     target [B, k+1, V] and draft [B, k, V]: float32 or bfloat16, contiguous,
@@ -228,9 +253,10 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
 
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
+        extra = (top_p.data_ptr(),) if top_p is not None else ()
         rc = getattr(lib, entry)(
             target.data_ptr(), _ptr(draft) if k > 0 else None, dt,
-            _ptr(draft_tokens) if k > 0 else None, _ptr(draft_len), temp.data_ptr(),
+            _ptr(draft_tokens) if k > 0 else None, _ptr(draft_len), temp.data_ptr(), *extra,
             B, k, V, ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint32(seq_base & 0xFFFFFFFF),
             out_tokens.data_ptr(), num_acc.data_ptr(),
             ctypes.byref(aux_t) if aux_t is not None else None,

@@ -82,6 +82,7 @@ __host__ __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? 
 struct F32 {
     using Elem = float;
     static constexpr int kVec = 4;
+    static constexpr int kKeyBits = 32;  // order-preserving key of a logit (top-p)
     static constexpr uint32_t kNegInfWord = 0xff800000u;  // -inf
     __device__ static inline void unpack(const u32x4 v, float (&f)[kVec])
     {
@@ -96,6 +97,7 @@ struct F32 {
 struct BF16 {
     using Elem = uint16_t;  // raw bf16 bits; widening to fp32 is exact
     static constexpr int kVec = 8;
+    static constexpr int kKeyBits = 16;
     static constexpr uint32_t kNegInfWord = 0xff80ff80u;  // two bf16 -inf
     __device__ static inline void unpack(const u32x4 v, float (&f)[kVec])
     {
@@ -292,13 +294,24 @@ __device__ inline float temp_scale(float tau)
 // Workspace records.
 // ---------------------------------------------------------------------------
 struct __align__(16) Decision {
-    int32_t row;   // row of the final draw
-    int32_t kind;  // SPEC_DRAW_*
-    float v;       // draw uniform
-    float scale;   // log2(e) / tau
-    float mt, zt;  // target row: max logit, normaliser
-    float md, zd;  // draft row (residual draws only)
+    int32_t row;     // row of the final draw
+    int32_t kind;    // SPEC_DRAW_*
+    float v;         // draw uniform
+    float scale;     // log2(e) / tau
+    float mt, zt;    // target row: max logit, normaliser (kept mass under top-p)
+    float md, zd;    // draft row (residual draws only)
+    float tht, thd;  // top-p: smallest kept logit of the target / draft row (-inf: all)
 };
+
+__device__ inline Decision no_decision()
+{
+    Decision d;
+    d.row = -1;
+    d.kind = SPEC_DRAW_NONE;
+    d.v = d.scale = d.mt = d.zt = d.md = d.zd = 0.f;
+    d.tht = d.thd = -INFINITY;
+    return d;
+}
 
 struct AuxDev {
     float *p_g, *q_g, *resid_mass;
@@ -316,6 +329,9 @@ struct Params {
     Decision *decisions;  // [B], written by k_decide
     double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the draw row
     double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
+    const float *top_p;   // [B] or null: nucleus parameter per sequence
+    float2 *nucleus;      // [B][2k+1]: top-p (threshold logit, kept mass) per row
+    int32_t fix_bits;     // top-p: fixed-point fraction bits of the row masses
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
     int32_t *ee_done;     // [k+1][B]: early exit: chunks finished per position
@@ -457,16 +473,15 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
         status = SPEC_SEQ_BAD_LEN;
     } else if (!valid_temp(tau)) {
         status = SPEC_SEQ_BAD_TEMP;
+    } else if (p.top_p && !(p.top_p[b] > 0.f)) {
+        status = SPEC_SEQ_BAD_TOP_P;
     } else {
         g = lane < L ? p.draft_tokens[b * k + lane] : -1;
         if (__any(lane < L && (g < 0 || g >= V)))
             status = SPEC_SEQ_BAD_TOKEN;
     }
 
-    Decision dec;
-    dec.row = -1;
-    dec.kind = SPEC_DRAW_NONE;
-    dec.v = dec.scale = dec.mt = dec.zt = dec.md = dec.zd = 0.f;
+    Decision dec = no_decision();
     float pg = NAN, qg = NAN;
     int amax = -1;
 
@@ -522,10 +537,27 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
                 for (int q = 0; q < kFoldBatch; ++q)
                     ds = soft_merge(ds, Soft{t[q].x, t[q].y}, scale);
             }
+        }
+        // Top-p: each row keeps its logits >= its threshold, normalised by
+        // the kept mass (k_nucleus); otherwise the whole row and Z.
+        float tz = ts.z, tth = -INFINITY, dz = ds.z, dth = -INFINITY;
+        if (p.top_p && p.top_p[b] < 1.f) {
+            if (lane <= L) {
+                const float2 n = p.nucleus[b * rows + lane];
+                tth = n.x;
+                tz = n.y;
+            }
+            if (lane < L) {
+                const float2 n = p.nucleus[b * rows + k + 1 + lane];
+                dth = n.x;
+                dz = n.y;
+            }
+        }
+        if (lane < L) {
             const float xt = D::at(target + (b * (k + 1) + lane) * (int64_t)V, g);
             const float xd = D::at(draft + (b * k + lane) * (int64_t)V, g);
-            pg = exp2_fast((xt - ts.m) * scale) / ts.z;
-            qg = exp2_fast((xd - ds.m) * scale) / ds.z;
+            pg = xt >= tth ? exp2_fast((xt - ts.m) * scale) / tz : 0.f;
+            qg = xd >= dth ? exp2_fast((xd - ds.m) * scale) / dz : 0.f;
         }
         const uint4 w = philox4x32_10(
             make_uint4((uint32_t)lane, p.seq_base + (uint32_t)b, 0u, 0u), p.key0, p.key1);
@@ -544,9 +576,11 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
             dec.v = __shfl(v, j, kWave);
             dec.scale = scale;
             dec.mt = __shfl(ts.m, j, kWave);
-            dec.zt = __shfl(ts.z, j, kWave);
+            dec.zt = __shfl(tz, j, kWave);
             dec.md = __shfl(ds.m, j, kWave);
-            dec.zd = __shfl(ds.z, j, kWave);
+            dec.zd = __shfl(dz, j, kWave);
+            dec.tht = __shfl(tth, j, kWave);
+            dec.thd = __shfl(dth, j, kWave);
             if (lane == 0)
                 p.num_accepted[b] = j;
         }
@@ -594,10 +628,12 @@ struct Weights {
 __device__ inline Weights draw_weights(float xt, float xd, const Decision &dec, float inv_zt,
                                        float inv_zd, bool resid)
 {
-    const float pt = exp2_fast((xt - dec.mt) * dec.scale) * inv_zt;
+    const float et = exp2_fast((xt - dec.mt) * dec.scale) * inv_zt;
+    const float pt = xt >= dec.tht ? et : 0.f;  // outside the target's nucleus: 0
     if (!resid)
         return {pt, pt};
-    const float pd = exp2_fast((xd - dec.md) * dec.scale) * inv_zd;
+    const float ed = exp2_fast((xd - dec.md) * dec.scale) * inv_zd;
+    const float pd = xd >= dec.thd ? ed : 0.f;
     return {fmaxf(pt - pd, 0.f), pt};
 }
 
@@ -941,6 +977,226 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 }
 
 // ===========================================================================
+// Top-p. The pages require verification to use the target's own sampling
+// parameters, temperature and top-p ("Speculative Decoding and the Art of
+// Fast LLM Inference", "Why It Stays Exact", key limitation). Each row keeps
+// whole probability levels (equal logits) from the top until their mass
+// reaches top_p of the row's mass, and is renormalised over them; the draft
+// rows get the same rule. k_nucleus finds, per row, the smallest kept logit
+// and the kept mass by an exact radix select over an order-preserving key of
+// the logit: digits of 12 bits (then the rest), most significant first.
+// Each pass streams the row and adds every element's weight 2^((x-m)s), in
+// fixed point (fix_bits fraction bits), to a 4096-bin LDS histogram of the
+// next digit among the elements that match the digits found so far; 64-bit
+// integer sums make the result independent of the order of the adds. The
+// crossing is found by an integer scan from the top bin; the target mass
+// ceil(top_p * total) is formed exactly in 128 bits.
+// ===========================================================================
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+
+template <class D>
+__device__ inline uint32_t order_key(float x)
+{
+    uint32_t u = x == 0.f ? 0u : __float_as_uint(x);  // -0 and +0: one level
+    if (D::kKeyBits == 16)
+        u >>= 16;  // a widened bf16 has 16 low zero bits
+    const uint32_t top = 1u << (D::kKeyBits - 1);
+    const uint32_t mask = D::kKeyBits == 32 ? 0xffffffffu : 0xffffu;
+    return (u & top) ? (~u & mask) : (u | top);
+}
+
+template <class D>
+__device__ inline float key_value(uint32_t key)
+{
+    const uint32_t top = 1u << (D::kKeyBits - 1);
+    const uint32_t mask = D::kKeyBits == 32 ? 0xffffffffu : 0xffffu;
+    uint32_t u = (key & top) ? (key & ~top) : (~key & mask);
+    if (D::kKeyBits == 16)
+        u <<= 16;
+    return __uint_as_float(u);
+}
+
+// ceil(top_p * total) for 0 < top_p < 1, exactly.
+__device__ inline uint64_t mass_target(uint64_t total, float top_p)
+{
+    int e;
+    const float fr = frexpf(top_p, &e);  // top_p = fr * 2^e, fr in [0.5, 1)
+    const uint64_t mant = (uint64_t)(fr * 16777216.0f);  // 24-bit integer, exact
+    const uint64_t lo = total * mant, hi = __umul64hi(total, mant);
+    const int sh = 24 - e;  // top_p = mant * 2^-sh, sh >= 24
+    if (sh >= 128)
+        return (hi | lo) ? 1 : 0;
+    if (sh >= 64) {
+        const int r = sh - 64;
+        const uint64_t q = r == 0 ? hi : hi >> r;
+        const bool rem = lo != 0 || (r > 0 && (hi & ((1ull << r) - 1)) != 0);
+        return q + (rem ? 1 : 0);
+    }
+    const uint64_t q = (hi << (64 - sh)) | (lo >> sh);
+    return q + ((lo & ((1ull << sh) - 1)) != 0 ? 1 : 0);
+}
+
+struct NucleusShared {
+    unsigned long long hist[kBins];
+    unsigned long long wsum[kWaves];
+    unsigned long long above;
+    int digit;
+    float rs;  // row max
+};
+
+// Visits every element of row[0, V) as fp32 (16-byte loads where aligned).
+template <class D, class F>
+__device__ __forceinline__ void for_each_logit(const typename D::Elem *row, int64_t V, F &&f)
+{
+    const Span sp = make_span<D>(row, 0, V);
+    const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
+    const int tid = threadIdx.x;
+    for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
+        u32x4 r[kTiles];
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            const int64_t vi = base + u * kThreads + tid;
+            r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kTiles; ++u) {
+            if (base + u * kThreads + tid < sp.ngroups) {
+                float x[D::kVec];
+                D::unpack(r[u], x);
+#pragma unroll
+                for (int j = 0; j < D::kVec; ++j)
+                    f(x[j]);
+            }
+        }
+    }
+    if (sp.s + tid < sp.a)
+        f(D::at(row, sp.s + tid));
+    if (sp.z + tid < sp.e)
+        f(D::at(row, sp.z + tid));
+}
+
+// One workgroup per row of every sequence with 0 < top_p < 1.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
+{
+    using E = typename D::Elem;
+    constexpr int KB = D::kKeyBits;
+    __shared__ NucleusShared sh;
+    const int k = p.k, nc = p.nc, rows = 2 * k + 1;
+    const int64_t rb = blockIdx.x;
+    const int slot = (int)(rb % rows);
+    const int64_t b = rb / rows;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    const float top_p = p.top_p[b];
+    if (!valid_len(L, k) || !valid_temp(tau) || tau == 0.f || !(top_p > 0.f) || !(top_p < 1.f))
+        return;
+    const bool is_target = slot <= k;
+    const int i = is_target ? slot : slot - (k + 1);
+    if (is_target ? i > L : i >= L)
+        return;
+    const E *row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
+                             : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
+    const float scale = temp_scale(tau);
+    const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
+    if (tid == 0) {
+        float m = -INFINITY;  // the row max: the largest chunk max
+        for (int c = 0; c < nc; ++c)
+            m = fmaxf(m, p.partials[(b * rows + slot) * (int64_t)nc + c].x);
+        sh.rs = m;
+        sh.above = 0;
+    }
+    __syncthreads();
+    const float m = sh.rs;
+    auto fixed = [&](float x) {
+        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
+    };
+
+    uint64_t target = 0, above = 0;
+    uint32_t prefix = 0;
+    int done = 0;
+    while (done < KB) {
+        const int w = min(kDigitBits, KB - done);
+        const int nb = 1 << w;
+        for (int q = tid; q < nb; q += kThreads)
+            sh.hist[q] = 0;
+        __syncthreads();
+        unsigned long long mine = 0;
+        for_each_logit<D>(row, p.V, [&](float x) {
+            const uint32_t key = order_key<D>(x);
+            if (done == 0 || (key >> (KB - done)) == prefix) {
+                const unsigned long long wf = fixed(x);
+                atomicAdd(&sh.hist[(key >> (KB - done - w)) & (uint32_t)(nb - 1)], wf);
+                mine += wf;
+            }
+        });
+        if (done == 0) {  // the row's total mass sets the target
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1)
+                mine += __shfl_xor(mine, off, kWave);
+            if (lane == 0)
+                sh.wsum[wave] = mine;
+        }
+        __syncthreads();
+        if (done == 0) {
+            uint64_t total = 0;
+            for (int q = 0; q < kWaves; ++q)
+                total += sh.wsum[q];
+            target = mass_target(total, top_p);
+        }
+        // Crossing: thread t owns bins [nb - (t+1)*per, nb - t*per), scanned
+        // from the top; an exclusive scan over threads in that order.
+        const uint64_t need = target - above;
+        const int per = nb >= kThreads ? nb / kThreads : 1;
+        const bool owns = tid * per < nb;
+        uint64_t loc = 0;
+        if (owns)
+            for (int q = 0; q < per; ++q)
+                loc += sh.hist[nb - 1 - tid * per - q];
+        uint64_t incl = loc;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint64_t o = __shfl_up(incl, off, kWave);
+            if (lane >= off)
+                incl += o;
+        }
+        __syncthreads();  // everyone has read the histogram sums; wsum is free
+        if (lane == kWave - 1)
+            sh.wsum[wave] = incl;
+        __syncthreads();
+        uint64_t before = 0;
+        for (int q = 0; q < wave; ++q)
+            before += sh.wsum[q];
+        const uint64_t excl = before + incl - loc;
+        if (owns && excl < need && need <= excl + loc) {
+            uint64_t cum = excl;
+            for (int q = 0; q < per; ++q) {
+                const int bin = nb - 1 - tid * per - q;
+                if (cum + sh.hist[bin] >= need) {
+                    sh.digit = bin;
+                    sh.above = cum;
+                    break;
+                }
+                cum += sh.hist[bin];
+            }
+        }
+        __syncthreads();
+        const int d = sh.digit;
+        above += sh.above;
+        prefix = (prefix << w) | (uint32_t)d;
+        done += w;
+        if (done == KB && tid == 0) {
+            const uint64_t kept = above + sh.hist[d];
+            p.nucleus[b * rows + slot] =
+                make_float2(key_value<D>(prefix), (float)kept / fscale);
+        }
+        __syncthreads();  // sh.hist is cleared next pass
+    }
+}
+
+// ===========================================================================
 // The step.
 // ===========================================================================
 template <class D>
@@ -1097,10 +1353,7 @@ __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float
 {
     using E = typename D::Elem;
     const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
-    Decision dec;
-    dec.row = -1;
-    dec.kind = SPEC_DRAW_NONE;
-    dec.v = dec.scale = dec.mt = dec.zt = dec.md = dec.zd = 0.f;
+    Decision dec = no_decision();
     auto partial = [&](const float2 *q) { return published ? fetch_float2(q) : *q; };
 
     const E *target = static_cast<const E *>(p.target);
@@ -1249,10 +1502,7 @@ __global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p)
             }
         }
         if (status != SPEC_SEQ_OK) {
-            Decision dec;
-            dec.row = -1;
-            dec.kind = SPEC_DRAW_NONE;
-            dec.v = dec.scale = dec.mt = dec.zt = dec.md = dec.zd = 0.f;
+            const Decision dec = no_decision();
             ee_stop(p, b, 0, status, dec, false, 0, 0, 0);
         } else {
             go = ee_decide<D>(p, b, 0, L, tau, false);
@@ -1577,7 +1827,7 @@ __global__ __launch_bounds__(kThreads) void k_prompt_lookup(
 // ===========================================================================
 struct Layout {
     int nc;
-    size_t partials, decisions, masses, segs, ee_count, ee_list, ee_done, total;
+    size_t partials, decisions, masses, segs, nucleus, ee_count, ee_list, ee_done, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1593,7 +1843,8 @@ bool layout_for(int32_t B, int32_t k, int32_t V, int32_t dtype, Layout *lay)
     lay->decisions = align_up(nb * (size_t)(2 * k + 1) * (size_t)lay->nc * sizeof(float2), 256);
     lay->masses = lay->decisions + align_up(nb * sizeof(Decision), 256);
     lay->segs = lay->masses + align_up(nb * (size_t)lay->nc * sizeof(double2), 256);
-    lay->ee_count = lay->segs + align_up(nb * (size_t)lay->nc * 2 * kSegs * sizeof(double), 256);
+    lay->nucleus = lay->segs + align_up(nb * (size_t)lay->nc * 2 * kSegs * sizeof(double), 256);
+    lay->ee_count = lay->nucleus + align_up(nb * (size_t)(2 * k + 1) * sizeof(float2), 256);
     lay->ee_list = lay->ee_count + align_up((size_t)(k + 2) * sizeof(int32_t), 256);
     lay->ee_done = lay->ee_list + align_up((size_t)(k + 1) * nb * sizeof(int32_t), 256);
     lay->total = lay->ee_done + align_up((size_t)(k + 1) * nb * sizeof(int32_t), 256);
@@ -1632,6 +1883,8 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         p.decisions = reinterpret_cast<Decision *>(ws + lay.decisions) + b0;
         p.masses = reinterpret_cast<double2 *>(ws + lay.masses) + b0 * nc;
         p.segs = reinterpret_cast<double *>(ws + lay.segs) + b0 * nc * 2 * kSegs;
+        p.nucleus = reinterpret_cast<float2 *>(ws + lay.nucleus) + b0 * rows;
+        if (p.top_p) p.top_p += b0;
         // Early-exit lists and counters are per slice (indexed by the
         // slice's own B), so each slice uses the arrays from their start.
         p.ee_count = reinterpret_cast<int32_t *>(ws + lay.ee_count);
@@ -1658,6 +1911,9 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                                stream, p);
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
+            if (p.top_p)
+                hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kThreads), 0,
+                                   stream, p);
             hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
                                dim3(kThreads), 0, stream, p);
         } else {
@@ -1684,9 +1940,10 @@ bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 int verify_entry(const void *target_logits, const void *draft_logits, int32_t dtype,
                  const int32_t *draft_tokens, const int32_t *draft_len, const float *temperature,
-                 int32_t B, int32_t k, int32_t V, uint64_t seed, uint32_t seq_base,
-                 int32_t *out_tokens, int32_t *num_accepted, const spec_verify_aux_t *aux,
-                 void *workspace, size_t workspace_bytes, void *stream, bool early_exit)
+                 const float *top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                 uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
+                 const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
+                 void *stream, bool early_exit)
 {
     Layout lay;
     if (!layout_for(B, k, V, dtype, &lay))
@@ -1700,7 +1957,8 @@ int verify_entry(const void *target_logits, const void *draft_logits, int32_t dt
         return SPEC_EINVAL;
     if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)) ||
         !aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(num_accepted, 4) ||
-        (draft_tokens && !aligned(draft_tokens, 4)) || (draft_len && !aligned(draft_len, 4)))
+        (draft_tokens && !aligned(draft_tokens, 4)) || (draft_len && !aligned(draft_len, 4)) ||
+        !aligned(top_p, 4))
         return SPEC_EINVAL;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
         return SPEC_EWORKSPACE;
@@ -1719,6 +1977,15 @@ int verify_entry(const void *target_logits, const void *draft_logits, int32_t dt
     p.seq_base = seq_base;
     p.out_tokens = out_tokens;
     p.num_accepted = num_accepted;
+    p.top_p = top_p;
+    {
+        // fixed-point masses of a row: V elements of at most 2^F each must
+        // sum below 2^62
+        int lv = 0;
+        while (lv < 31 && (1ll << lv) < (int64_t)V)
+            ++lv;
+        p.fix_bits = std::min(40, 62 - lv);
+    }
     if (aux) {
         p.aux.p_g = aux->p_g;
         p.aux.q_g = aux->q_g;
@@ -1745,7 +2012,22 @@ extern "C" int spec_verify(const void *target_logits, const void *draft_logits, 
                            size_t workspace_bytes, void *stream)
 {
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
-                        B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
+                        nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
+                        workspace_bytes, stream, false);
+}
+
+extern "C" int spec_verify_top_p(const void *target_logits, const void *draft_logits,
+                                 int32_t dtype, const int32_t *draft_tokens,
+                                 const int32_t *draft_len, const float *temperature,
+                                 const float *top_p, int32_t B, int32_t k, int32_t V,
+                                 uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                                 int32_t *num_accepted, const spec_verify_aux_t *aux,
+                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!top_p && B > 0)
+        return SPEC_EINVAL;
+    return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
+                        top_p, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
                         workspace_bytes, stream, false);
 }
 
@@ -1758,7 +2040,7 @@ extern "C" int spec_verify_early_exit(const void *target_logits, const void *dra
                                       void *workspace, size_t workspace_bytes, void *stream)
 {
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
-                        B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
+                        nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
                         workspace_bytes, stream, true);
 }
 
