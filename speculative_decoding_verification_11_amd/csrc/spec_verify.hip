@@ -62,6 +62,9 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunkBytes = 32768;  // one row-statistics item
 constexpr int kTiles = 8;           // 16-byte vectors per thread per chunk
+// A chunk is exactly kTiles tiles of one 16-byte vector per lane: the draw
+// sums and the locate walk it tile by tile without a loop.
+static_assert(kChunkBytes == kTiles * 256 * 16, "chunk geometry");
 constexpr int kMaxLdsChunks = 256;  // chunk masses staged in LDS by the locate
 // Draw-weight segments of a chunk, in element order: the scalar head, then
 // one segment per (tile, wave) -- the 512 consecutive elements one wave
