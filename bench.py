@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -59,8 +58,9 @@ def hip_runtime():
 
 
 def kernel_source_digest() -> str:
-    src = os.path.join(ROOT, "speculative_decoding_verification_11_amd", "csrc", "spec_verify.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    from speculative_decoding_verification_11_amd.build import source_digest
+
+    return source_digest()
 
 
 def read_counter_traffic(workload: str):

@@ -13,7 +13,11 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "spec_verify.hip")
+CSRC = os.path.join(PKG, "csrc")
+# verify.hip: spec_verify, spec_verify_top_p, spec_verify_early_exit;
+# tree.hip: spec_verify_tree; lookup.hip: spec_prompt_lookup (common.h is
+# their shared device header).
+SRCS = [os.path.join(CSRC, f) for f in ("verify.hip", "tree.hip", "lookup.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "_build", "libspecverify.so")
 ARCH = "gfx950"
@@ -34,16 +38,29 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+def source_digest() -> str:
+    """sha256[:16] over every kernel source file (name and bytes, sorted):
+    the key that ties a committed profile to the code it measured."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def build_library(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {SRC}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {' '.join(SRCS)}")
     os.replace(tmp, out)
     return out
 

@@ -1,5 +1,6 @@
-// spec_verify.hip -- HIP kernels and C ABI for the speculative-sampling
-// verification step on MI355X (gfx950).
+// verify.hip -- HIP kernels and C ABI of the speculative-sampling
+// verification step on MI355X (gfx950): spec_verify, spec_verify_top_p and
+// spec_verify_early_exit.
 //
 // The step, per sequence b with draft length L and temperature tau
 // ("Speculative Decoding and the Art of Fast LLM Inference", "The Algorithm,
@@ -46,252 +47,9 @@
 // Nothing here is a dense contraction, so there is no MFMA: the step is bound
 // by HBM bandwidth.
 
-#include <hip/hip_runtime.h>
-
-#include <algorithm>
-#include <float.h>
-#include <math.h>
-#include <stdint.h>
-
-#include "spec_verify.h"
+#include "common.h"
 
 namespace {
-
-constexpr int kThreads = 256;       // 4 waves of 64 lanes
-constexpr int kWave = 64;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kChunkBytes = 32768;  // one row-statistics item
-constexpr int kTiles = 8;           // 16-byte vectors per thread per chunk
-// A chunk is exactly kTiles tiles of one 16-byte vector per lane: the draw
-// sums and the locate walk it tile by tile without a loop.
-static_assert(kChunkBytes == kTiles * 256 * 16, "chunk geometry");
-constexpr int kMaxLdsChunks = 256;  // chunk masses staged in LDS by the locate
-// Draw-weight segments of a chunk, in element order: the scalar head, then
-// one segment per (tile, wave) -- the 512 consecutive elements one wave
-// reads in one tile -- tile-major, then the scalar tail.
-constexpr int kSegs = kTiles * kWaves + 2;
-constexpr int kTrStride = 68;       // LDS row of 64 lanes, skewed across banks
-constexpr int kMaxNgram = SPEC_MAX_NGRAM;
-constexpr int kFoldBatch = 8;       // partial loads in flight per lane when folding
-constexpr int kDeviceVersion = 300;  // 0.3.0
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
-
-__host__ __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
-
-// ---------------------------------------------------------------------------
-// Storage types: 16 bytes hold 4 fp32 or 8 bf16 logits.
-// ---------------------------------------------------------------------------
-struct F32 {
-    using Elem = float;
-    static constexpr int kVec = 4;
-    static constexpr int kKeyBits = 32;  // order-preserving key of a logit (top-p)
-    static constexpr uint32_t kNegInfWord = 0xff800000u;  // -inf
-    __device__ static inline void unpack(const u32x4 v, float (&f)[kVec])
-    {
-        f[0] = __uint_as_float(v.x);
-        f[1] = __uint_as_float(v.y);
-        f[2] = __uint_as_float(v.z);
-        f[3] = __uint_as_float(v.w);
-    }
-    __device__ static inline float at(const Elem *p, int64_t i) { return p[i]; }
-};
-
-struct BF16 {
-    using Elem = uint16_t;  // raw bf16 bits; widening to fp32 is exact
-    static constexpr int kVec = 8;
-    static constexpr int kKeyBits = 16;
-    static constexpr uint32_t kNegInfWord = 0xff80ff80u;  // two bf16 -inf
-    __device__ static inline void unpack(const u32x4 v, float (&f)[kVec])
-    {
-        f[0] = __uint_as_float(v.x << 16);
-        f[1] = __uint_as_float(v.x & 0xffff0000u);
-        f[2] = __uint_as_float(v.y << 16);
-        f[3] = __uint_as_float(v.y & 0xffff0000u);
-        f[4] = __uint_as_float(v.z << 16);
-        f[5] = __uint_as_float(v.z & 0xffff0000u);
-        f[6] = __uint_as_float(v.w << 16);
-        f[7] = __uint_as_float(v.w & 0xffff0000u);
-    }
-    __device__ static inline float at(const Elem *p, int64_t i)
-    {
-        return __uint_as_float((uint32_t)p[i] << 16);
-    }
-};
-
-template <class D>
-constexpr int64_t chunk_elems()
-{
-    return kChunkBytes / (int64_t)sizeof(typename D::Elem);
-}
-
-// Element range [s, e) of a row chunk split into a scalar head [s, a),
-// groups of kVec elements [a, z) and a scalar tail [z, e). With `vec` the
-// groups are 16-byte aligned and loaded as vectors.
-struct Span {
-    int64_t s, a, z, e, ngroups;
-    bool vec;
-};
-
-template <class D>
-__device__ inline Span make_span(const typename D::Elem *row, int64_t s, int64_t e)
-{
-    using E = typename D::Elem;
-    const uintptr_t addr = (uintptr_t)(row + s);
-    const int64_t head = (int64_t)(((16u - (addr & 15u)) & 15u) / sizeof(E));
-    Span sp;
-    sp.s = s;
-    sp.e = e;
-    sp.a = min64(e, s + head);
-    sp.ngroups = (e - sp.a) / D::kVec;
-    sp.z = sp.a + sp.ngroups * D::kVec;
-    sp.vec = true;
-    return sp;
-}
-
-// Span for reading two rows at once: vectors only if both share alignment.
-template <class D>
-__device__ inline Span make_span2(const typename D::Elem *r1, const typename D::Elem *r2,
-                                  int64_t s, int64_t e)
-{
-    Span sp = make_span<D>(r1, s, e);
-    if (((uintptr_t)(r1 + s) & 15u) != ((uintptr_t)(r2 + s) & 15u)) {
-        sp.a = s;
-        sp.ngroups = (e - s) / D::kVec;
-        sp.z = s + sp.ngroups * D::kVec;
-        sp.vec = false;
-    }
-    return sp;
-}
-
-template <class D>
-__device__ inline void load_group(const typename D::Elem *row, const Span &sp, int64_t gi,
-                                  float (&f)[D::kVec])
-{
-    if (sp.vec) {
-        D::unpack(reinterpret_cast<const u32x4 *>(row + sp.a)[gi], f);
-    } else {
-#pragma unroll
-        for (int j = 0; j < D::kVec; ++j)
-            f[j] = D::at(row, sp.a + gi * D::kVec + j);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Online softmax statistics (Milakov & Gimelshein, "Online normalizer
-// calculation for softmax", 2018): running max m of the raw logits and
-// z = sum 2^((x - m) * scale), scale = log2(e) / tau.
-// ---------------------------------------------------------------------------
-struct Soft {
-    float m, z;
-};
-
-__device__ inline float exp2_fast(float x)
-{
-    return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
-}
-
-__device__ inline Soft soft_merge(Soft a, Soft b, float scale)
-{
-    const float m = fmaxf(a.m, b.m);
-    if (m == -INFINITY)
-        return {m, 0.f};
-    return {m, a.z * exp2_fast((a.m - m) * scale) + b.z * exp2_fast((b.m - m) * scale)};
-}
-
-template <int N>
-__device__ inline void soft_update(Soft &st, const float (&x)[N], float scale)
-{
-    float bm = x[0];
-#pragma unroll
-    for (int j = 1; j < N; ++j)
-        bm = fmaxf(bm, x[j]);
-    const float m = fmaxf(st.m, bm);
-    const float base = m == -INFINITY ? 0.f : m;  // a thread that saw only padding
-    float z = st.z * exp2_fast((st.m - base) * scale);
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        z += exp2_fast((x[j] - base) * scale);
-    st.m = m;
-    st.z = z;
-}
-
-struct ArgMax {
-    float v;
-    int32_t i;
-};
-
-__device__ inline ArgMax argmax_merge(ArgMax a, ArgMax b)
-{
-    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
-}
-
-// ---------------------------------------------------------------------------
-// Wave and block reductions (fixed order, independent of timing).
-// ---------------------------------------------------------------------------
-__device__ inline Soft wave_soft(Soft s, float scale)
-{
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        Soft o{__shfl_xor(s.m, off, kWave), __shfl_xor(s.z, off, kWave)};
-        s = soft_merge(s, o, scale);
-    }
-    return s;
-}
-
-__device__ inline ArgMax wave_argmax(ArgMax a)
-{
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        ArgMax o{__shfl_xor(a.v, off, kWave), __shfl_xor(a.i, off, kWave)};
-        a = argmax_merge(a, o);
-    }
-    return a;
-}
-
-__device__ inline double wave_sum(double v)
-{
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
-// ---------------------------------------------------------------------------
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each round
-// multiplies counter words 0 and 2 by the Philox multipliers, keeps both
-// halves of the products and mixes the high halves with words 1 and 3 and
-// the round key; the key advances by the Weyl constants between rounds.
-// ---------------------------------------------------------------------------
-__device__ inline uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1)
-{
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    return c;
-}
-
-__device__ inline float uniform24(uint32_t w)
-{
-    return (float)(w >> 8) * 0x1p-24f;  // exact: 24-bit integer times 2^-24
-}
-
-__host__ __device__ inline bool valid_len(int L, int k) { return L >= 0 && L <= k; }
-
-__host__ __device__ inline bool valid_temp(float tau)
-{
-    return tau == 0.f || (tau >= FLT_MIN && tau <= FLT_MAX);  // NaN fails both
-}
-
-__device__ inline float temp_scale(float tau)
-{
-    return (float)(1.4426950408889634 / (double)tau);  // log2(e) / tau, rounded once
-}
 
 // ---------------------------------------------------------------------------
 // Workspace records.
@@ -342,10 +100,6 @@ struct Params {
     AuxDev aux;
 };
 
-// LDS of the kernels.
-struct RowShared {
-    float a[kWaves], b[kWaves];
-};
 struct DrawShared {
     float tr[kWaves][2 * kTiles][kTrStride];  // per-lane group sums, transposed
     double seg[2][kSegs];                       // segment sums of w and p
@@ -353,107 +107,6 @@ struct DrawShared {
 struct LocateShared {
     double cm[kMaxLdsChunks];  // chunk masses (w, p) of one sequence
 };
-
-// ===========================================================================
-// Row statistics of one chunk: returns the block's partial in thread 0.
-// ===========================================================================
-template <class D>
-__device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64_t s, int64_t e, bool greedy,
-                              float scale, RowShared &sh)
-{
-    constexpr int NX = kTiles * D::kVec;
-    const Span sp = make_span<D>(row, s, e);
-    const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
-    const int tid = threadIdx.x;
-    const u32x4 pad = {D::kNegInfWord, D::kNegInfWord, D::kNegInfWord, D::kNegInfWord};
-    float2 out = make_float2(0.f, 0.f);
-
-    if (!greedy) {
-        Soft st{-INFINITY, 0.f};
-        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
-            u32x4 r[kTiles];
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                const int64_t vi = base + u * kThreads + tid;
-                r[u] = vi < sp.ngroups ? vrow[vi] : pad;
-            }
-            float x[NX];
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                float f[D::kVec];
-                D::unpack(r[u], f);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j)
-                    x[u * D::kVec + j] = f[j];
-            }
-            soft_update(st, x, scale);
-        }
-        {
-            float x[2];
-            const int64_t hi = sp.s + tid, ti = sp.z + tid;
-            x[0] = hi < sp.a ? D::at(row, hi) : -INFINITY;
-            x[1] = ti < sp.e ? D::at(row, ti) : -INFINITY;
-            if (x[0] != -INFINITY || x[1] != -INFINITY)
-                soft_update(st, x, scale);
-        }
-        st = wave_soft(st, scale);
-        if ((tid & (kWave - 1)) == 0) {
-            sh.a[tid / kWave] = st.m;
-            sh.b[tid / kWave] = st.z;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            Soft acc{sh.a[0], sh.b[0]};
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                acc = soft_merge(acc, Soft{sh.a[w], sh.b[w]}, scale);
-            out = make_float2(acc.m, acc.z);
-        }
-    } else {
-        ArgMax am{-INFINITY, INT32_MAX};
-        // head, vectors, tail: each thread sees ascending ids
-        if (sp.s + tid < sp.a) {
-            const float x = D::at(row, sp.s + tid);
-            if (x > am.v) am = ArgMax{x, (int32_t)(sp.s + tid)};
-        }
-        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
-            u32x4 r[kTiles];
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                const int64_t vi = base + u * kThreads + tid;
-                r[u] = vi < sp.ngroups ? vrow[vi] : pad;
-            }
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                float f[D::kVec];
-                D::unpack(r[u], f);
-                const int32_t i0 = (int32_t)(sp.a + (base + u * kThreads + tid) * D::kVec);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j)
-                    if (f[j] > am.v) am = ArgMax{f[j], i0 + j};
-            }
-        }
-        if (sp.z + tid < sp.e) {
-            const float x = D::at(row, sp.z + tid);
-            if (x > am.v) am = ArgMax{x, (int32_t)(sp.z + tid)};
-        }
-        am = wave_argmax(am);
-        if ((tid & (kWave - 1)) == 0) {
-            sh.a[tid / kWave] = am.v;
-            sh.b[tid / kWave] = __int_as_float(am.i);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            ArgMax acc{sh.a[0], __float_as_int(sh.b[0])};
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                acc = argmax_merge(acc, ArgMax{sh.a[w], __float_as_int(sh.b[w])});
-            out = make_float2(acc.v, __int_as_float(acc.i));
-        }
-    }
-    __syncthreads();  // sh is reused by the caller
-    return out;
-}
 
 // ===========================================================================
 // Decision of one sequence (one wave; `lane` in [0, 64)). Writes the
@@ -1547,293 +1200,12 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
 }
 
 // ===========================================================================
-// Greedy verification of candidate trees. A tree's node 0 is the root (the
-// last committed position); node n >= 1 holds a drafted token and a parent
-// with a smaller index; the target row of node n scores the token after
-// node n's path ("Speculative Decoding and the Art of Fast LLM Inference",
-// "EAGLE: drafting in feature space": a tree of candidate continuations
-// verified together; techaiinterview.com, "Drafts and limits"). The pages
-// give no sampling rule for trees, so the rule is greedy: a node is
-// accepted when its parent is and its token equals the parent's target
-// argmax; the round keeps the deepest accepted node (lowest index among
-// equals) and emits its path, then its argmax.
-// ===========================================================================
-struct TreeParams {
-    const void *target;
-    const int32_t *parents, *tokens, *n_nodes;
-    int32_t N, V, nc, B;
-    float2 *partials;  // [B][N][nc]: (max logit, lowest index of it)
-    int32_t *out_tokens, *path_nodes, *num_accepted, *seq_status, *argmax;
-};
-
-// One workgroup per 32 KiB chunk of each node's row.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_tree_rowstats(TreeParams p)
-{
-    using E = typename D::Elem;
-    constexpr int64_t CH = chunk_elems<D>();
-    __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
-    const int nc = p.nc, N = p.N;
-    const int c = (int)(item % nc);
-    const int64_t rn = item / nc;
-    const int n = (int)(rn % N);
-    const int64_t b = rn / N;
-    const int nn = p.n_nodes[b];
-    if (nn < 1 || nn > N || n >= nn)
-        return;  // k_tree_decide reports a bad node count
-    const E *row = static_cast<const E *>(p.target) + (b * N + n) * (int64_t)p.V;
-    const int64_t s = (int64_t)c * CH;
-    const float2 part = chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), true, 0.f, sh);
-    if (threadIdx.x == 0)
-        p.partials[item] = part;
-}
-
-// One wave per sequence, lane n = node n.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_tree_decide(TreeParams p)
-{
-    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-    const int lane = (int)(threadIdx.x % kWave);
-    if (b >= p.B)
-        return;
-    const int N = p.N, V = p.V, nc = p.nc;
-    const int nn = p.n_nodes[b];
-    const bool node = lane < nn && lane < N;
-    int status = SPEC_SEQ_OK;
-    int par = -1, tok = -1;
-    if (nn < 1 || nn > N) {
-        status = SPEC_SEQ_BAD_LEN;
-    } else {
-        if (node && lane > 0) {
-            par = p.parents[b * N + lane];
-            tok = p.tokens[b * N + lane];
-        }
-        if (__any(node && lane > 0 && (par < 0 || par >= lane)))
-            status = SPEC_SEQ_BAD_TREE;
-        else if (__any(node && lane > 0 && (tok < 0 || tok >= V)))
-            status = SPEC_SEQ_BAD_TOKEN;
-    }
-    int amax = -1;
-    if (status == SPEC_SEQ_OK && node) {
-        const float2 *pp = p.partials + (b * N + lane) * (int64_t)nc;
-        ArgMax acc{-INFINITY, INT32_MAX};
-        for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
-            float2 t[kFoldBatch];
-#pragma unroll
-            for (int q = 0; q < kFoldBatch; ++q)
-                t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, __int_as_float(INT32_MAX));
-#pragma unroll
-            for (int q = 0; q < kFoldBatch; ++q)
-                acc = argmax_merge(acc, ArgMax{t[q].x, __float_as_int(t[q].y)});
-        }
-        amax = acc.i;
-    }
-    int32_t *out = p.out_tokens + b * N;
-    int32_t *path = p.path_nodes + b * N;
-    if (status != SPEC_SEQ_OK) {
-        if (lane < N) {
-            out[lane] = -1;
-            path[lane] = -1;
-            if (p.argmax) p.argmax[b * N + lane] = -1;
-        }
-        if (lane == 0) {
-            p.num_accepted[b] = 0;
-            if (p.seq_status) p.seq_status[b] = status;
-        }
-        return;
-    }
-    // Acceptance and depth flow down from the root; a parent's index is
-    // smaller than its child's, so nn rounds always settle them.
-    // (every lane takes part in each shuffle: a lane that skips one leaves
-    // nothing for the lanes that read from it)
-    const int pl = par < 0 ? 0 : par;
-    const int parent_amax = __shfl(amax, pl, kWave);
-    const bool match = node && lane > 0 && tok == parent_amax;
-    bool acc = lane == 0;
-    int depth = 0;
-    for (int r = 1; r < nn; ++r) {
-        const bool pa = __shfl((int)acc, pl, kWave) != 0;
-        const int pd = __shfl(depth, pl, kWave);
-        if (lane > 0 && node) {
-            acc = match && pa;
-            depth = pd + 1;
-        }
-    }
-    // The deepest accepted node, the lowest index among equals.
-    int key = acc ? (depth << 8) | (255 - lane) : -1;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1)
-        key = max(key, __shfl_xor(key, off, kWave));
-    const int best = 255 - (key & 255), d = key >> 8;
-    // Walk the path from the deepest node up; lane j keeps position j.
-    int x = best, mine_tok = -1, mine_node = -1;
-    for (int j = d - 1; j >= 0; --j) {
-        const int tx = __shfl(tok, x, kWave);
-        const int px = __shfl(par, x, kWave);
-        if (lane == j) {
-            mine_tok = tx;
-            mine_node = x;
-        }
-        x = px;
-    }
-    const int bonus = __shfl(amax, best, kWave);
-    if (lane < N) {
-        out[lane] = lane < d ? mine_tok : (lane == d ? bonus : -1);
-        path[lane] = lane < d ? mine_node : -1;
-        if (p.argmax) p.argmax[b * N + lane] = node ? amax : -1;
-    }
-    if (lane == 0) {
-        p.num_accepted[b] = d;
-        if (p.seq_status) p.seq_status[b] = SPEC_SEQ_OK;
-    }
-}
-
-template <class D>
-int launch_tree(const TreeParams &base, const spec_tree_aux_t *aux, char *ws, int nc,
-                hipStream_t stream)
-{
-    const int B = base.B, N = base.N;
-    const int64_t per_seq_items = (int64_t)N * nc;
-    const int64_t max_items = (int64_t)1 << 22;
-    const int64_t slice = std::max<int64_t>(1, max_items / per_seq_items);
-    hipEvent_t ev_begin = aux ? static_cast<hipEvent_t>(aux->event_begin) : nullptr;
-    hipEvent_t ev_end = aux ? static_cast<hipEvent_t>(aux->event_end) : nullptr;
-    for (int64_t b0 = 0; b0 < B; b0 += slice) {
-        const int64_t nb = std::min<int64_t>((int64_t)B - b0, slice);
-        TreeParams p = base;
-        p.B = (int32_t)nb;
-        p.nc = nc;
-        p.target = static_cast<const typename D::Elem *>(base.target) + b0 * N * (int64_t)base.V;
-        p.parents = base.parents + b0 * N;
-        p.tokens = base.tokens + b0 * N;
-        p.n_nodes = base.n_nodes + b0;
-        p.partials = reinterpret_cast<float2 *>(ws);
-        p.out_tokens = base.out_tokens + b0 * N;
-        p.path_nodes = base.path_nodes + b0 * N;
-        p.num_accepted = base.num_accepted + b0;
-        if (p.seq_status) p.seq_status += b0;
-        if (p.argmax) p.argmax += b0 * N;
-        if (ev_begin && b0 == 0 && hipEventRecord(ev_begin, stream) != hipSuccess)
-            return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(k_tree_rowstats<D>, dim3((unsigned)(nb * per_seq_items)),
-                           dim3(kThreads), 0, stream, p);
-        if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
-            return SPEC_ELAUNCH;
-        hipLaunchKernelGGL(k_tree_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
-                           dim3(kThreads), 0, stream, p);
-        if (hipGetLastError() != hipSuccess)
-            return SPEC_ELAUNCH;
-    }
-    return SPEC_OK;
-}
-
-int tree_nc(int32_t V, int32_t dtype)
-{
-    const int64_t ch = kChunkBytes / (dtype == SPEC_F32 ? 4 : 2);
-    return (int)((V + ch - 1) / ch);
-}
-
-bool tree_sizes_ok(int32_t B, int32_t N, int32_t V, int32_t dtype)
-{
-    return B >= 0 && N >= 1 && N <= SPEC_MAX_TREE && V >= 1 &&
-           (dtype == SPEC_F32 || dtype == SPEC_BF16);
-}
-
-// ===========================================================================
-// Prompt-lookup drafting: search the context for a recent occurrence of its
-// own last n tokens and propose the tokens that followed it ("Speculative
-// Decoding and the Art of Fast LLM Inference", "n-gram and prompt lookup: no
-// model at all"; techaiinterview.com, "Drafts and limits"). Sizes are tried
-// from n_max down to n_min; for a size the most recent occurrence ending
-// before the last token wins.
-//
-// One workgroup per context. For every candidate end position e < T - 1 the
-// lane finds m(e), the number of tokens ending at e that equal the
-// context's last tokens (capped at n_max). The answer is the largest
-// (min(m(e), n_max), e) with m(e) >= n_min: the largest size that matches
-// anywhere, then its latest end.
-// ===========================================================================
-constexpr int kLookupUnroll = 16;  // context loads in flight per lane
-
-__global__ __launch_bounds__(kThreads) void k_prompt_lookup(
-    const int32_t *__restrict__ contexts, const int32_t *__restrict__ ctx_len, int32_t T_max,
-    int32_t n_min, int32_t n_max, int32_t k, int32_t *__restrict__ draft_tokens,
-    int32_t *__restrict__ draft_len, int32_t *__restrict__ match_n,
-    int32_t *__restrict__ match_start)
-{
-    __shared__ uint64_t best_w[kWaves];
-    __shared__ int32_t tail[kMaxNgram];  // tail[j] = ctx[T - 1 - j]
-    const int64_t b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int T = ctx_len[b];
-    const bool valid = T >= 0 && T <= T_max;
-    const int32_t *ctx = contexts + b * (int64_t)T_max;
-
-    if (tid < kMaxNgram)
-        tail[tid] = valid && tid < n_max && tid < T ? ctx[T - 1 - tid] : 0;
-    __syncthreads();
-    const int32_t last = tail[0];
-
-    // Candidate ends e in [0, T - 2]; key = (size << 32) | e, 0 = none.
-    uint64_t key = 0;
-    const int e_end = valid ? T - 1 : 0;
-    for (int base = 0; base < e_end; base += kThreads * kLookupUnroll) {
-        int32_t c[kLookupUnroll];
-#pragma unroll
-        for (int u = 0; u < kLookupUnroll; ++u) {
-            const int e = base + u * kThreads + tid;
-            c[u] = e < e_end ? ctx[e] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kLookupUnroll; ++u) {
-            const int e = base + u * kThreads + tid;
-            if (e < e_end && c[u] == last) {
-                int m = 1;
-                const int cap = min(n_max, e + 1);
-                while (m < cap && ctx[e - m] == tail[m])
-                    ++m;
-                if (m >= n_min) {
-                    const uint64_t kk = ((uint64_t)m << 32) | (uint32_t)e;
-                    key = kk > key ? kk : key;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const uint64_t o = __shfl_xor(key, off, kWave);
-        key = o > key ? o : key;
-    }
-    if (lane == 0)
-        best_w[wave] = key;
-    __syncthreads();
-    key = best_w[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        key = best_w[w] > key ? best_w[w] : key;
-
-    const int n = (int)(key >> 32);
-    const int e = (int)(uint32_t)key;
-    const int len = n > 0 ? min(k, T - 1 - e) : 0;
-    for (int j = tid; j < k; j += kThreads)
-        draft_tokens[b * (int64_t)k + j] = j < len ? ctx[e + 1 + j] : -1;
-    if (tid == 0) {
-        draft_len[b] = len;
-        if (match_n) match_n[b] = n;
-        if (match_start) match_start[b] = n > 0 ? e - n + 1 : -1;
-    }
-}
-
-// ===========================================================================
 // Host side.
 // ===========================================================================
 struct Layout {
     int nc;
     size_t partials, decisions, masses, segs, nucleus, ee_count, ee_list, ee_done, total;
 };
-
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool layout_for(int32_t B, int32_t k, int32_t V, int32_t dtype, Layout *lay)
 {
@@ -1937,8 +1309,6 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
     }
     return SPEC_OK;
 }
-
-bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 
 int verify_entry(const void *target_logits, const void *draft_logits, int32_t dtype,
@@ -2045,86 +1415,6 @@ extern "C" int spec_verify_early_exit(const void *target_logits, const void *dra
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
                         nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
                         workspace_bytes, stream, true);
-}
-
-extern "C" size_t spec_verify_tree_workspace_size(int32_t B, int32_t N, int32_t V, int32_t dtype)
-{
-    if (!tree_sizes_ok(B, N, V, dtype))
-        return 0;
-    const size_t bytes = (size_t)B * (size_t)N * (size_t)tree_nc(V, dtype) * sizeof(float2);
-    return bytes == 0 ? 256 : align_up(bytes, 256);
-}
-
-extern "C" int spec_verify_tree(const void *target_logits, int32_t dtype, const int32_t *parents,
-                                const int32_t *tokens, const int32_t *n_nodes, int32_t B,
-                                int32_t N, int32_t V, int32_t *out_tokens, int32_t *path_nodes,
-                                int32_t *num_accepted, const spec_tree_aux_t *aux,
-                                void *workspace, size_t workspace_bytes, void *stream)
-{
-    if (!tree_sizes_ok(B, N, V, dtype))
-        return SPEC_EINVAL;
-    if (B == 0)
-        return SPEC_OK;
-    const size_t esz = dtype == SPEC_F32 ? 4 : 2;
-    if (!target_logits || !parents || !tokens || !n_nodes || !out_tokens || !path_nodes ||
-        !num_accepted)
-        return SPEC_EINVAL;
-    if (!aligned(target_logits, esz) || !aligned(parents, 4) || !aligned(tokens, 4) ||
-        !aligned(n_nodes, 4) || !aligned(out_tokens, 4) || !aligned(path_nodes, 4) ||
-        !aligned(num_accepted, 4) || (aux && aux->seq_status && !aligned(aux->seq_status, 4)) ||
-        (aux && aux->argmax && !aligned(aux->argmax, 4)))
-        return SPEC_EINVAL;
-    if (!workspace || !aligned(workspace, 256) ||
-        workspace_bytes < spec_verify_tree_workspace_size(B, N, V, dtype))
-        return SPEC_EWORKSPACE;
-    TreeParams p{};
-    p.target = target_logits;
-    p.parents = parents;
-    p.tokens = tokens;
-    p.n_nodes = n_nodes;
-    p.N = N;
-    p.V = V;
-    p.B = B;
-    p.out_tokens = out_tokens;
-    p.path_nodes = path_nodes;
-    p.num_accepted = num_accepted;
-    p.seq_status = aux ? aux->seq_status : nullptr;
-    p.argmax = aux ? aux->argmax : nullptr;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    const int nc = tree_nc(V, dtype);
-    if (dtype == SPEC_F32)
-        return launch_tree<F32>(p, aux, ws, nc, st);
-    return launch_tree<BF16>(p, aux, ws, nc, st);
-}
-
-extern "C" int spec_prompt_lookup(const int32_t *contexts, const int32_t *context_len, int32_t B,
-                                  int32_t T_max, int32_t n_min, int32_t n_max, int32_t k,
-                                  int32_t *draft_tokens, int32_t *draft_len, int32_t *match_n,
-                                  int32_t *match_start, void *stream)
-{
-    if (B < 0 || T_max < 0 || n_min < 1 || n_max < n_min || n_max > SPEC_MAX_NGRAM || k < 0 ||
-        k > SPEC_MAX_K || T_max > INT32_MAX - 1)
-        return SPEC_EINVAL;
-    if (B == 0)
-        return SPEC_OK;
-    if ((T_max > 0 && !contexts) || !context_len || (k > 0 && !draft_tokens) || !draft_len)
-        return SPEC_EINVAL;
-    if (!aligned(contexts, 4) || !aligned(context_len, 4) || !aligned(draft_tokens, 4) ||
-        !aligned(draft_len, 4) || !aligned(match_n, 4) || !aligned(match_start, 4))
-        return SPEC_EINVAL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int64_t b0 = 0; b0 < B; b0 += INT32_MAX / 2) {
-        const int64_t nb = std::min<int64_t>((int64_t)B - b0, INT32_MAX / 2);
-        hipLaunchKernelGGL(k_prompt_lookup, dim3((unsigned)nb), dim3(kThreads), 0, st,
-                           contexts ? contexts + b0 * T_max : nullptr, context_len + b0, T_max,
-                           n_min, n_max, k, draft_tokens ? draft_tokens + b0 * k : nullptr,
-                           draft_len + b0, match_n ? match_n + b0 : nullptr,
-                           match_start ? match_start + b0 : nullptr);
-        if (hipGetLastError() != hipSuccess)
-            return SPEC_ELAUNCH;
-    }
-    return SPEC_OK;
 }
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int32_t dtype)
