@@ -36,6 +36,8 @@ constexpr int kTrStride = 68;       // LDS row of 64 lanes, skewed across banks
 constexpr int kMaxNgram = SPEC_MAX_NGRAM;
 constexpr int kFoldBatch = 8;       // partial loads in flight per lane when folding
 constexpr int kDeviceVersion = 300;  // 0.3.0
+// Early exit: positions below this one get a launch each; the rest share one.
+constexpr int kEarlyExitSingle = 3;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 

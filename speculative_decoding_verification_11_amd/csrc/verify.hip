@@ -1199,6 +1199,46 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
     }
 }
 
+// Positions P..k in one launch: every remaining row (target rows P..L,
+// draft rows P..L-1) of the sequences on position P's list. Once few
+// sequences are left, a launch per position costs more than reading the
+// rows after a stop that will never be used. The workgroup that completes
+// a sequence's chunks decides its positions P, P+1, ... up to the stop.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
+{
+    __shared__ RowShared sh;
+    const int64_t item = blockIdx.x;
+    const int k = p.k, nc = p.nc, rows = 2 * k + 1;
+    const int nt = k - P + 1, R = 2 * nt - 1;  // target rows P..k, draft rows P..k-1
+    const int64_t j = item / ((int64_t)R * nc);
+    if (j >= p.ee_count[P])
+        return;
+    const int rest = (int)(item % ((int64_t)R * nc));
+    const int slot = rest / nc, c = rest % nc;
+    const int64_t b = p.ee_list[(int64_t)P * p.B + j];
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    const bool greedy = tau == 0.f;
+    const bool is_target = slot < nt;
+    const int i = is_target ? P + slot : P + slot - nt;
+    if (is_target ? i > L : (greedy || i >= L))
+        return;
+    const float2 part = ee_chunk<D>(p, b, is_target ? 0 : 1, c, i, tau, sh);
+    if (threadIdx.x != 0)
+        return;
+    publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c, part);
+    drain_stores();  // the partial is visible before the count
+    int items = 0;
+    for (int x = P; x <= L; ++x)
+        items += ee_items(nc, greedy, x, L);
+    if (counter_add(p.ee_done + (int64_t)P * p.B + b, 1) != items - 1)
+        return;
+    for (int x = P; x <= L; ++x)
+        if (!ee_decide<D>(p, b, x, L, tau, true))
+            break;
+}
+
 // ===========================================================================
 // Host side.
 // ===========================================================================
@@ -1296,9 +1336,14 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                                0, stream, p);
             hipLaunchKernelGGL(k_ee_decide0<D>, dim3((unsigned)((nb + kThreads - 1) / kThreads)),
                                dim3(kThreads), 0, stream, p);
-            for (int i = 1; i <= k; ++i)
+            const int P = std::min(k + 1, kEarlyExitSingle);
+            for (int i = 1; i < P; ++i)
                 hipLaunchKernelGGL(k_ee_rowstats<D>, dim3((unsigned)(nb * 2 * nc)),
                                    dim3(kThreads), 0, stream, p, i);
+            if (P <= k)
+                hipLaunchKernelGGL(k_ee_tail<D>,
+                                   dim3((unsigned)(nb * (2 * (k - P + 1) - 1) * nc)),
+                                   dim3(kThreads), 0, stream, p, P);
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
         }
