@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -113,7 +115,24 @@ def cpu_baseline(batch, seed: int, nseq: int) -> dict:
                       f"{dt:.2f} s wall"}
 
 
-def bench_tree(hip, ev, K: int, W: int) -> dict:
+def roof(achieved_gbps: float, what: str) -> dict:
+    """HBM roofline of an extra entry point: bytes read once over `what`."""
+    return {"bound": "hbm", "achieved": achieved_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved_gbps / PEAK_HBM_GBPS, "over": what}
+
+
+def timed_oracle(fn, units: float, unit: str, sample: str) -> dict:
+    from oracle import parity
+
+    nthreads = parity.host_threads(cap=16)
+    t0 = time.perf_counter()
+    fn(nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": units / dt, "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": f"{sample}, {nthreads} threads, {dt:.2f} s wall"}
+
+
+def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
     """Greedy tree verification on workload t3: nodes per second, and the
     node-row kernel's bandwidth (each node row read once, HIP events)."""
     import torch
@@ -155,13 +174,24 @@ def bench_tree(hip, ev, K: int, W: int) -> dict:
            "bytes_read_once": nbytes, "row_kernel": "k_tree_rowstats",
            "row_kernel_us_mean": row_mean * 1e3,
            "row_kernel_GBps": nbytes / (row_mean * 1e-3) / 1e9,
-           "mean_accepted_depth": float(out[2].float().mean())}
+           "mean_accepted_depth": float(out[2].float().mean()),
+           "roofline": roof(nbytes / (row_mean * 1e-3) / 1e9, "k_tree_rowstats, HIP events")}
+    if cpu:
+        import oracle
+
+        n_cpu = tw.B
+        th = wl.tree_to_host_arrays(wl.TreeBatch(tw, tb.target[:n_cpu], tb.parents[:n_cpu],
+                                                 tb.tokens[:n_cpu], tb.n_nodes[:n_cpu]))
+        res["cpu_baseline"] = timed_oracle(
+            lambda nt: oracle.spec_tree_ref(th["target"], th["parents"], th["tokens"],
+                                            th["n_nodes"], nthreads=nt),
+            n_cpu * tw.N, "nodes/s", f"all {tw.B} trees of the same batch, fp64 C oracle")
     log(f"[bench] tree {ms_step:.4f} ms/step; rows {row_mean * 1e3:.1f} us "
         f"({res['row_kernel_GBps']:.0f} GB/s)")
     return res
 
 
-def bench_lookup(K: int, W: int) -> dict:
+def bench_lookup(K: int, W: int, cpu: bool) -> dict:
     """Prompt-lookup drafting on workload p3: contexts per second and the
     kernel's bandwidth over the context tokens (one kernel per call, timed
     with torch events on the stream it is launched on)."""
@@ -195,7 +225,15 @@ def bench_lookup(K: int, W: int) -> dict:
            "value": lw.B / (ms_step * 1e-3), "unit": "contexts/s", "ms_per_step": ms_step,
            "context_bytes": nbytes, "kernel": "k_prompt_lookup", "kernel_us_mean": k_ms * 1e3,
            "kernel_GBps": nbytes / (k_ms * 1e-3) / 1e9,
-           "mean_draft_len": float(out[1].float().mean())}
+           "mean_draft_len": float(out[1].float().mean()),
+           "roofline": roof(nbytes / (k_ms * 1e-3) / 1e9, "k_prompt_lookup, torch events")}
+    if cpu:
+        import oracle
+
+        res["cpu_baseline"] = timed_oracle(
+            lambda nt: oracle.spec_prompt_lookup_ref(ctx_np, lens_np, lw.n_min, lw.n_max, lw.k),
+            lw.B, "contexts/s", f"all {lw.B} contexts of the same batch, C oracle (one thread: "
+                                "it searches from the end and stops at the first match)")
     log(f"[bench] prompt lookup {ms_step:.4f} ms/step; kernel {k_ms * 1e3:.1f} us "
         f"({res['kernel_GBps']:.0f} GB/s)")
     return res
@@ -347,6 +385,9 @@ def main() -> int:
             "position_loop_us_mean": loop_mean * 1e3,
             "position_loop_GBps": ee_bytes / (loop_mean * 1e-3) / 1e9,
             "outputs_identical": bool(torch.equal(n_ee, n_acc.cpu())),
+            "roofline": roof(ee_bytes / (loop_mean * 1e-3) / 1e9,
+                             "the position loop (rows up to each stop, read once), HIP events"),
+            "cpu_baseline": "the oracle of the top-level cpu_baseline (identical outputs)",
         }
         log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
             f"for {ee_bytes / 1e9:.3f} GB")
@@ -372,14 +413,28 @@ def main() -> int:
         topp = {"entry_point": "spec_verify_top_p", "top_p": 0.95,
                 "value": positions / (tp_ms * 1e-3), "unit": "positions/s", "ms_per_step": tp_ms,
                 "rows_filtered": t_rows + d_rows,
-                "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum())}
+                "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
+                "roofline": roof(alg_bytes / (tp_ms * 1e-3) / 1e9,
+                                 "the whole step (each row counted once; k_nucleus reads every "
+                                 "row twice more)")}
+        if not args.no_cpu_baseline:
+            import oracle
+            from oracle import parity
+
+            n_cpu = 64
+            hs = wl.to_host_arrays(batch.select(range(n_cpu)))
+            topp["cpu_baseline"] = timed_oracle(
+                lambda nt: parity.oracle_on(hs, seed, nthreads=nt, top_p=np.full(n_cpu, 0.95,
+                                                                                 np.float32)),
+                n_cpu * (w.k + 1), "positions/s",
+                f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-p")
         log(f"[bench] top-p {tp_ms:.4f} ms/step")
     tree = None
     if not args.no_tree:
-        tree = bench_tree(hip, ev, K, W)
+        tree = bench_tree(hip, ev, K, W, not args.no_cpu_baseline)
     lookup = None
     if not args.no_lookup:
-        lookup = bench_lookup(K, W)
+        lookup = bench_lookup(K, W, not args.no_cpu_baseline)
     for a, b in ev:
         hip.hipEventDestroy(a)
         hip.hipEventDestroy(b)
