@@ -384,8 +384,8 @@ __device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, in
             for (int u = 0; u < kBatch; ++u) {
                 const int64_t gi = (int64_t)(h + u) * kThreads + tid;
                 const bool in = gi < sp.ngroups;
-                lt[u] = in ? vt[gi] : u32x4{0u, 0u, 0u, 0u};
-                ld[u] = in && r.resid ? vd[gi] : u32x4{0u, 0u, 0u, 0u};
+                lt[u] = in ? stream_load(vt + gi) : u32x4{0u, 0u, 0u, 0u};
+                ld[u] = in && r.resid ? stream_load(vd + gi) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
