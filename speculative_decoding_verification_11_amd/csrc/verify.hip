@@ -646,7 +646,12 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 // next digit among the elements that match the digits found so far; 64-bit
 // integer sums make the result independent of the order of the adds. The
 // crossing is found by an integer scan from the top bin; the target mass
-// ceil(top_p * total) is formed exactly in 128 bits.
+// ceil(top_p * total) is formed exactly in 128 bits. A bf16 row first takes
+// one pass that counts the elements of each key within kWinKeys keys below
+// the row max (a key's fixed-point mass is its count times one element's)
+// and adds up the rest; only when the crossing lies below that window does
+// the row go through the radix passes. Both give the same integers, and both
+// skip the elements whose fixed-point mass is 0.
 // ===========================================================================
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
@@ -693,12 +698,45 @@ __device__ inline uint64_t mass_target(uint64_t total, float top_p)
     return q + ((lo & ((1ull << sh) - 1)) != 0 ? 1 : 0);
 }
 
+// bf16 rows: exact counts per key over kWinKeys entries of a compressed key
+// order below the row max. Magnitudes under 2^-14 (and zero) share the entry
+// kTinyIdx, whose mass is summed element by element instead; every other
+// entry is one bf16 value. From a max of about 16, 8192 entries reach below
+// -2^30, so the rows' mass lies inside the window. One more counter, at
+// kWinKeys, takes the values beyond the window.
+constexpr int kWinKeys = 8192;
+constexpr uint32_t kTinyBits = 113u << 7;  // bf16 magnitude bits of 2^-14
+constexpr uint32_t kTinyIdx = 0x8000u - kTinyBits;
+
+// Compressed index of a 16-bit order key: monotone, and one-to-one except
+// that all magnitudes below 2^-14 map to kTinyIdx.
+__device__ inline uint32_t compress_key(uint32_t key)
+{
+    if (key >= 0x8000u) {
+        const uint32_t u = key - 0x8000u;  // magnitude bits of a positive value
+        return u < kTinyBits ? kTinyIdx : kTinyIdx + 1u + (u - kTinyBits);
+    }
+    const uint32_t u = 0x7fffu - key;  // magnitude bits of a negative value
+    return u < kTinyBits ? kTinyIdx : kTinyIdx - 1u - (u - kTinyBits);
+}
+
+// The order key of a compressed index other than kTinyIdx.
+__device__ inline uint32_t expand_key(uint32_t c)
+{
+    return c > kTinyIdx ? 0x8000u + (c - kTinyIdx - 1u + kTinyBits)
+                        : 0x7fffu - (kTinyIdx - 1u - c + kTinyBits);
+}
+
 struct NucleusShared {
-    unsigned long long hist[kBins];
+    union {
+        unsigned long long hist[kBins];  // radix pass: fixed-point mass per digit
+        uint32_t cnt[kWinKeys + 1];      // window pass: elements per key
+    };
     unsigned long long wsum[kWaves];
     unsigned long long above;
     int digit;
     float rs;  // row max
+    float tc;  // window pass: entries below this (x - m) * scale are not counted
 };
 
 // Visits every element of row[0, V) as fp32 (16-byte loads where aligned).
@@ -732,7 +770,82 @@ __device__ __forceinline__ void for_each_logit(const typename D::Elem *row, int6
         f(D::at(row, sp.z + tid));
 }
 
-// One workgroup per row of every sequence with 0 < top_p < 1.
+// Two 16-bit lanes of one 32-bit register (packed integer arithmetic).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ inline uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline uint32_t as_u32(i16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Sum over the workgroup of one value per thread.
+__device__ inline uint64_t block_sum(uint64_t v, NucleusShared &sh)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    __syncthreads();  // wsum is free
+    if (lane == 0)
+        sh.wsum[wave] = v;
+    __syncthreads();
+    uint64_t t = 0;
+    for (int q = 0; q < kWaves; ++q)
+        t += sh.wsum[q];
+    return t;
+}
+
+// Crossing search over n masses in the order i = 0, 1, ... (thread t owns
+// [t*per, (t+1)*per)): the first i at which the running sum reaches `need`
+// (>= 1) goes to sh.digit, the sum before it to sh.above; sh.digit = -1 if
+// all n together stay below `need`. Integer sums: the result does not
+// depend on the order of any addition.
+template <class M>
+__device__ inline void crossing(int n, uint64_t need, M &&mass, NucleusShared &sh)
+{
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int per = n >= kThreads ? n / kThreads : 1;
+    const bool owns = tid * per < n;
+    uint64_t loc = 0;
+    if (owns)
+        for (int q = 0; q < per; ++q)
+            loc += mass(tid * per + q);
+    uint64_t incl = loc;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint64_t o = __shfl_up(incl, off, kWave);
+        if (lane >= off)
+            incl += o;
+    }
+    if (tid == 0)
+        sh.digit = -1;
+    __syncthreads();  // wsum is free; digit is reset
+    if (lane == kWave - 1)
+        sh.wsum[wave] = incl;
+    __syncthreads();
+    uint64_t before = 0;
+    for (int q = 0; q < wave; ++q)
+        before += sh.wsum[q];
+    const uint64_t excl = before + incl - loc;
+    if (owns && excl < need && need <= excl + loc) {
+        uint64_t cum = excl;
+        for (int q = 0; q < per; ++q) {
+            const uint64_t mq = mass(tid * per + q);
+            if (cum + mq >= need) {
+                sh.digit = tid * per + q;
+                sh.above = cum;
+                break;
+            }
+            cum += mq;
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup per row of every sequence with 0 < top_p < 1. The kept set
+// is the smallest run of keys from the top whose fixed-point mass reaches
+// ceil(top_p * total); every mass is an integer sum, so the threshold and
+// the kept mass do not depend on how the row is split or visited.
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
 {
@@ -743,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
     const int64_t rb = blockIdx.x;
     const int slot = (int)(rb % rows);
     const int64_t b = rb / rows;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
     const float top_p = p.top_p[b];
@@ -757,11 +870,19 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
                              : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
     const float scale = temp_scale(tau);
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
+    // Elements with (x - m) * scale below this weigh 0 in fixed point.
+    const float zlim = -(float)(p.fix_bits + 2);
     if (tid == 0) {
+        const float2 *pp = p.partials + (b * rows + slot) * (int64_t)nc;
         float m = -INFINITY;  // the row max: the largest chunk max
         for (int c = 0; c < nc; ++c)
-            m = fmaxf(m, p.partials[(b * rows + slot) * (int64_t)nc + c].x);
+            m = fmaxf(m, pp[c].x);
+        float z = 0.f;  // the row's mass relative to its max
+        for (int c = 0; c < nc; ++c)
+            z += pp[c].y * exp2_fast((pp[c].x - m) * scale);
         sh.rs = m;
+        // (x - m) * scale < tc: together at most V * 2^tc = (1 - top_p) z / 4
+        sh.tc = fmaxf(zlim, __log2f((1.f - top_p) * z / (float)p.V) - 2.f);
         sh.above = 0;
     }
     __syncthreads();
@@ -769,7 +890,165 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
     auto fixed = [&](float x) {
         return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
     };
+    float2 *const out = p.nucleus + b * rows + slot;
 
+    if constexpr (KB == 16) {
+        // One pass: every element with the same bf16 value has the same
+        // fixed-point mass, so counts per key near the top give the masses
+        // exactly. In raw bits r, with magnitude u = r & 0x7fff and
+        // d = max(u - kTinyBits + 1, 0), the window entry is A - d for a
+        // positive and A + d for a negative value, A being the entry of the
+        // tiny values (d = 0), all of it in 16-bit arithmetic: two elements
+        // per 32-bit word.
+        const uint32_t cm = compress_key(order_key<D>(m));
+        const uint32_t A = cm - kTinyIdx;
+        // Window entry of the lowest bf16 value at or below x (x rounded
+        // down to bf16).
+        auto entry_below = [&](float x) {
+            const uint32_t bx = __float_as_uint(x);
+            uint32_t r = bx >> 16;
+            if ((bx & 0xffffu) && (bx & 0x80000000u))
+                r += 1u;  // a truncated negative value: one step further down
+            return cm - compress_key((r & 0x8000u) ? (~r & 0xffffu) : (r | 0x8000u));
+        };
+        // Entries from iz on hold values below m + (zlim - 2) / scale: they
+        // weigh 0. Entries in [kWinKeys, iz) have mass but no counter.
+        const uint32_t iz =
+            __builtin_amdgcn_readfirstlane(entry_below(m + (zlim - 2.f) / scale) + 1u);
+        const bool wide = iz > (uint32_t)kWinKeys;
+        // Entries from wc on hold values with (x - m) * scale < tc. Together
+        // those weigh at most V * 2^tc = (1 - top_p) / 4 of the row, so the
+        // crossing lies above them; and each weighs below 2^31 in fixed
+        // point. They are not counted: their entries hold that weight
+        // instead, which each element adds to the total.
+        const float tc = fminf(sh.tc, (float)(30 - p.fix_bits));
+        const uint32_t wc = __builtin_amdgcn_readfirstlane(
+            min(entry_below(m + tc / scale) + 1u, (uint32_t)kWinKeys));
+        for (int q = tid; q <= kWinKeys; q += kThreads) {
+            uint32_t v = 0;
+            if ((uint32_t)q >= wc && q < kWinKeys && (uint32_t)q != A && (uint32_t)q <= cm)
+                v = (uint32_t)fixed(key_value<D>(expand_key(cm - (uint32_t)q)));
+            sh.cnt[q] = v;
+        }
+        __syncthreads();
+        unsigned long long below = 0, tiny = 0;
+        const u16x2 a2 = (u16x2)(unsigned short)A;
+        const u16x2 w2 = (u16x2)(unsigned short)kWinKeys;
+        const u16x2 wm2 = (u16x2)(unsigned short)(kWinKeys - 1);
+        const u16x2 tb2 = (u16x2)(unsigned short)kTinyBits;
+        const u16x2 tbm2 = (u16x2)(unsigned short)(kTinyBits - 1u);
+        // Tiny values and values beyond the window with mass: one by one
+        // (their entries, A and kWinKeys, hold 0).
+        auto rare = [&](uint32_t r, uint32_t idx) {
+            const bool is_tiny = (r & 0x7fffu) < kTinyBits;
+            const bool beyond = idx >= (uint32_t)kWinKeys && idx < iz;
+            const unsigned long long f = fixed(__uint_as_float(r << 16));
+            tiny += is_tiny ? f : 0ull;
+            below += !is_tiny && beyond ? f : 0ull;
+        };
+        auto visit_slot = [&](uint32_t slot) {
+            const uint32_t v = sh.cnt[slot];
+            if (slot < wc)
+                atomicAdd(&sh.cnt[slot], 1u);
+            below += slot < wc ? 0u : v;
+        };
+        // Eight elements (one 16-byte load): all window reads are issued
+        // before the counts and the sums, so one wait covers them.
+        auto visit_group = [&](const u32x4 &g) {
+            const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+            uint32_t idx[4], slot[8];
+            bool any_rare = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u16x2 u = as_u16x2(w[j] & 0x7fff7fffu);
+                const u16x2 d = __builtin_bit_cast(
+                    u16x2,
+                    __builtin_elementwise_max(__builtin_bit_cast(i16x2, u - tbm2), (i16x2)0));
+                const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
+                idx[j] = (as_u32(a2 + d) & neg) | (as_u32(a2 - d) & ~neg);
+                const uint32_t s2 = as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), w2));
+                slot[2 * j] = s2 & 0xffffu;
+                slot[2 * j + 1] = s2 >> 16;
+                const bool has_tiny = as_u32(__builtin_elementwise_min(u, tb2)) != as_u32(tb2);
+                const bool has_beyond =
+                    as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), wm2)) != idx[j];
+                any_rare |= has_tiny || (wide && has_beyond);
+            }
+            uint32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = sh.cnt[slot[j]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (slot[j] < wc)
+                    atomicAdd(&sh.cnt[slot[j]], 1u);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                below += slot[j] < wc ? 0u : v[j];
+            if (any_rare) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    rare(w[j] & 0xffffu, idx[j] & 0xffffu);
+                    rare(w[j] >> 16, idx[j] >> 16);
+                }
+            }
+        };
+        {
+            const Span sp = make_span<D>(row, 0, p.V);
+            const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
+            for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
+                u32x4 r[kTiles];
+#pragma unroll
+                for (int u = 0; u < kTiles; ++u) {
+                    const int64_t vi = base + u * kThreads + tid;
+                    r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < kTiles; ++u)
+                    if (base + u * kThreads + tid < sp.ngroups)
+                        visit_group(r[u]);
+            }
+            auto visit_one = [&](uint32_t r) {
+                const uint32_t u = r & 0x7fffu;
+                const uint32_t d = u < kTinyBits ? 0u : u - (kTinyBits - 1u);
+                const uint32_t idx = ((r & 0x8000u) ? A + d : A - d) & 0xffffu;
+                visit_slot(min(idx, (uint32_t)kWinKeys));
+                rare(r, idx);
+            };
+            if (sp.s + tid < sp.a)
+                visit_one((uint32_t)row[sp.s + tid]);
+            if (sp.z + tid < sp.e)
+                visit_one((uint32_t)row[sp.z + tid]);
+        }
+        const uint64_t tiny_total = block_sum(tiny, sh);
+        auto key_mass = [&](int idx) -> uint64_t {
+            if ((uint32_t)idx == A)
+                return tiny_total;
+            const uint32_t n = (uint32_t)idx < wc ? sh.cnt[idx] : 0u;
+            return n ? (uint64_t)n * fixed(key_value<D>(expand_key(cm - (uint32_t)idx))) : 0;
+        };
+        uint64_t win = 0;
+        for (int q = 0; q < kWinKeys / kThreads; ++q)
+            win += key_mass(tid * (kWinKeys / kThreads) + q);
+        if (tid == 0 && A >= (uint32_t)kWinKeys)
+            win += tiny_total;  // the tiny entry lies beyond the window
+        const uint64_t total = block_sum(win + below, sh);
+        crossing(kWinKeys, mass_target(total, top_p), key_mass, sh);
+        const int d = sh.digit;
+        if (d >= 0 && (uint32_t)d != A) {
+            if (tid == 0) {
+                const uint64_t kept = sh.above + key_mass(d);
+                *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)d)),
+                                   (float)kept / fscale);
+            }
+            return;
+        }
+        // The crossing lies among the tiny magnitudes or below the counted
+        // entries: radix passes.
+        __syncthreads();
+    }
+
+    // Radix passes: kDigitBits of the key at a time, from the top.
     uint64_t target = 0, above = 0;
     uint32_t prefix = 0;
     int done = 0;
@@ -781,6 +1060,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
         __syncthreads();
         unsigned long long mine = 0;
         for_each_logit<D>(row, p.V, [&](float x) {
+            if ((x - m) * scale < zlim)
+                return;
             const uint32_t key = order_key<D>(x);
             if (done == 0 || (key >> (KB - done)) == prefix) {
                 const unsigned long long wf = fixed(x);
@@ -788,65 +1069,17 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
                 mine += wf;
             }
         });
-        if (done == 0) {  // the row's total mass sets the target
-#pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1)
-                mine += __shfl_xor(mine, off, kWave);
-            if (lane == 0)
-                sh.wsum[wave] = mine;
-        }
+        if (done == 0)  // the row's total mass sets the target
+            target = mass_target(block_sum(mine, sh), top_p);
         __syncthreads();
-        if (done == 0) {
-            uint64_t total = 0;
-            for (int q = 0; q < kWaves; ++q)
-                total += sh.wsum[q];
-            target = mass_target(total, top_p);
-        }
-        // Crossing: thread t owns bins [nb - (t+1)*per, nb - t*per), scanned
-        // from the top; an exclusive scan over threads in that order.
-        const uint64_t need = target - above;
-        const int per = nb >= kThreads ? nb / kThreads : 1;
-        const bool owns = tid * per < nb;
-        uint64_t loc = 0;
-        if (owns)
-            for (int q = 0; q < per; ++q)
-                loc += sh.hist[nb - 1 - tid * per - q];
-        uint64_t incl = loc;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint64_t o = __shfl_up(incl, off, kWave);
-            if (lane >= off)
-                incl += o;
-        }
-        __syncthreads();  // everyone has read the histogram sums; wsum is free
-        if (lane == kWave - 1)
-            sh.wsum[wave] = incl;
-        __syncthreads();
-        uint64_t before = 0;
-        for (int q = 0; q < wave; ++q)
-            before += sh.wsum[q];
-        const uint64_t excl = before + incl - loc;
-        if (owns && excl < need && need <= excl + loc) {
-            uint64_t cum = excl;
-            for (int q = 0; q < per; ++q) {
-                const int bin = nb - 1 - tid * per - q;
-                if (cum + sh.hist[bin] >= need) {
-                    sh.digit = bin;
-                    sh.above = cum;
-                    break;
-                }
-                cum += sh.hist[bin];
-            }
-        }
-        __syncthreads();
-        const int d = sh.digit;
+        crossing(nb, target - above, [&](int q) -> uint64_t { return sh.hist[nb - 1 - q]; }, sh);
+        const int d = nb - 1 - sh.digit;  // the crossing always exists here
         above += sh.above;
         prefix = (prefix << w) | (uint32_t)d;
         done += w;
         if (done == KB && tid == 0) {
             const uint64_t kept = above + sh.hist[d];
-            p.nucleus[b * rows + slot] =
-                make_float2(key_value<D>(prefix), (float)kept / fscale);
+            *out = make_float2(key_value<D>(prefix), (float)kept / fscale);
         }
         __syncthreads();  // sh.hist is cleared next pass
     }

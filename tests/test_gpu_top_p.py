@@ -131,6 +131,123 @@ def test_top_p_tied_levels_bf16():
     check(total, "top-p ties")
 
 
+def _bf16_of_key(key):
+    """bf16 bits whose order-preserving key (sign flipped for positives, all
+    bits flipped for negatives) is `key`."""
+    key = int(key)
+    return key & 0x7FFF if key & 0x8000 else (~key) & 0xFFFF
+
+
+def _key_of_bf16(u):
+    u = int(u)
+    return (u | 0x8000) if not u & 0x8000 else (~u) & 0xFFFF
+
+
+# The bf16 nucleus counts tokens per key over a window of 8192 entries of a
+# compressed key order below the row max, where magnitudes under 2^-14 share
+# one entry; a crossing among those tiny magnitudes or below the window goes
+# through the radix passes instead. Inputs below put crossings on both sides.
+_TINY_BITS = 113 << 7
+_TINY_IDX = 0x8000 - _TINY_BITS
+
+
+def _compress(key):
+    if key >= 0x8000:
+        u = key - 0x8000
+        return _TINY_IDX if u < _TINY_BITS else _TINY_IDX + 1 + (u - _TINY_BITS)
+    u = 0x7FFF - key
+    return _TINY_IDX if u < _TINY_BITS else _TINY_IDX - 1 - (u - _TINY_BITS)
+
+
+def _expand(c):
+    return (0x8000 + (c - _TINY_IDX - 1 + _TINY_BITS) if c > _TINY_IDX
+            else 0x7FFF - (_TINY_IDX - 1 - c + _TINY_BITS))
+
+
+def _bf16(x):
+    return int(bf16_bits(np.array([x], np.float32))[0])
+
+
+def _level_rows(rng, B, nrows, V, levels):
+    """[B, nrows, V] bf16 rows holding `levels` = [(bits, count), ...], the
+    rest of each row at the last level, shuffled per row."""
+    out = np.empty((B, nrows, V), np.uint16)
+    for b in range(B):
+        for r in range(nrows):
+            row = np.full(V, levels[-1][0], np.uint16)
+            at = 0
+            for bits, n in levels[:-1]:
+                row[at:at + n] = bits
+                at += n
+            out[b, r] = row[rng.permutation(V)]
+    return out
+
+
+def _crossing_levels(t, tau, top_p):
+    """Index of the level (distinct logit, from the top) that ends each
+    sequence's row-0 nucleus, in fp64."""
+    tv = bf16_to_f32(t).astype(np.float64)
+    res = []
+    for b in range(t.shape[0]):
+        x = tv[b, 0] / np.float64(tau[b])
+        lv = sorted(set(x.tolist()), reverse=True)
+        mass = np.array([np.exp(x[x == v] - x.max()).sum() for v in lv])
+        res.append(int(np.argmax(np.cumsum(mass) >= float(top_p[b]) * mass.sum())))
+    return res
+
+
+def _run_levels(t, d, tau, top_p, label):
+    B, k = d.shape[0], d.shape[1]
+    g = bf16_to_f32(d).argmax(axis=2).astype(np.int32)
+    L = np.full(B, k, np.int32)
+    cb = raw_batch(t, d, g, L, tau)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    total = parity.Report()
+    for seed in (11, 12, 13):
+        say(f"[case] top-p {label} seed={seed}")
+        g_ = run_tp(gb, seed, top_p)
+        r = parity.oracle_on(h, seed, top_p=top_p)
+        total.merge(parity.compare(g_, r, L, tau, k))
+    check(total, f"top-p {label}")
+
+
+def test_top_p_crossing_among_tiny_logits_bf16():
+    """Heavy levels at +3e-6 and -2e-6 (both under 2^-14, so both in the
+    shared tiny entry) and at 0.25 and -8 (entries of their own): top_p puts
+    the crossing on each of them."""
+    rng = np.random.default_rng(57)
+    B, k, V = 8, 2, 4096
+    lv = [(_bf16(1.0), 1), (_bf16(0.25), 1000), (_bf16(3e-6), 1000), (_bf16(-2e-6), 1000),
+          (_bf16(-8.0), 0)]
+    assert _compress(_key_of_bf16(lv[2][0])) == _compress(_key_of_bf16(lv[3][0])) == _TINY_IDX
+    t = _level_rows(rng, B, k + 1, V, lv)
+    d = _level_rows(rng, B, k, V, [(_bf16(1.0), 1), (_bf16(0.25), 900), (_bf16(3e-6), 1100),
+                                   (_bf16(-2e-6), 1000), (_bf16(-8.0), 0)])
+    tau = np.ones(B, np.float32)
+    top_p = np.array([0.3, 0.55, 0.85, 0.99995] * 2, np.float32)
+    assert _crossing_levels(t, tau, top_p) == [1, 2, 3, 4] * 2
+    _run_levels(t, d, tau, top_p, "tiny levels")
+
+
+def test_top_p_crossing_at_the_window_edge_bf16():
+    """Levels on the last window entry below the max and on the first entry
+    past it (about -6.8e10; a temperature of 1e10 gives them weight)."""
+    rng = np.random.default_rng(58)
+    B, k, V = 6, 2, 4096
+    cm = _compress(_key_of_bf16(_bf16(1.0)))
+    a_bits, b_bits = _bf16_of_key(_expand(cm - 8191)), _bf16_of_key(_expand(cm - 8192))
+    lv = [(_bf16(1.0), 1), (a_bits, 1000), (b_bits, 1000), (_bf16(-3e10), 0)]
+    t = _level_rows(rng, B, k + 1, V, lv)
+    d = _level_rows(rng, B, k, V, [(_bf16(1.0), 1), (a_bits, 900), (b_bits, 1100),
+                                   (_bf16(-3e10), 0)])
+    tau = np.full(B, 1e10, np.float32)
+    top_p = np.array([0.5, 0.985, 0.995] * 2, np.float32)
+    # levels from the top: 1.0, -3e10, then the two edge levels
+    assert _crossing_levels(t, tau, top_p) == [1, 2, 3] * 2
+    _run_levels(t, d, tau, top_p, "window edge")
+
+
 def test_top_p_statuses_and_qzero():
     rng = np.random.default_rng(41)
     B, k, V = 7, 2, 64
