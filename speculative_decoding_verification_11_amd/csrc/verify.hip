@@ -727,12 +727,17 @@ __device__ inline uint32_t expand_key(uint32_t c)
                         : 0x7fffu - (kTinyIdx - 1u - c + kTinyBits);
 }
 
+// Workgroup of the nucleus search: eight waves share one row's table.
+constexpr int kNucThreads = 512;
+constexpr int kNucWaves = kNucThreads / kWave;
+constexpr int kNucTiles = 4;  // 16-byte loads in flight per thread (counting pass)
+
 struct NucleusShared {
     union {
         unsigned long long hist[kBins];  // radix pass: fixed-point mass per digit
         uint32_t cnt[kWinKeys + 1];      // window pass: elements per key
     };
-    unsigned long long wsum[kWaves];
+    unsigned long long wsum[kNucWaves];
     unsigned long long above;
     int digit;
     float rs;  // row max
@@ -746,16 +751,16 @@ __device__ __forceinline__ void for_each_logit(const typename D::Elem *row, int6
     const Span sp = make_span<D>(row, 0, V);
     const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
     const int tid = threadIdx.x;
-    for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
+    for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kTiles) {
         u32x4 r[kTiles];
 #pragma unroll
         for (int u = 0; u < kTiles; ++u) {
-            const int64_t vi = base + u * kThreads + tid;
+            const int64_t vi = base + u * kNucThreads + tid;
             r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kTiles; ++u) {
-            if (base + u * kThreads + tid < sp.ngroups) {
+            if (base + u * kNucThreads + tid < sp.ngroups) {
                 float x[D::kVec];
                 D::unpack(r[u], x);
 #pragma unroll
@@ -790,7 +795,7 @@ __device__ inline uint64_t block_sum(uint64_t v, NucleusShared &sh)
         sh.wsum[wave] = v;
     __syncthreads();
     uint64_t t = 0;
-    for (int q = 0; q < kWaves; ++q)
+    for (int q = 0; q < kNucWaves; ++q)
         t += sh.wsum[q];
     return t;
 }
@@ -804,7 +809,7 @@ template <class M>
 __device__ inline void crossing(int n, uint64_t need, M &&mass, NucleusShared &sh)
 {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int per = n >= kThreads ? n / kThreads : 1;
+    const int per = n >= kNucThreads ? n / kNucThreads : 1;
     const bool owns = tid * per < n;
     uint64_t loc = 0;
     if (owns)
@@ -847,7 +852,7 @@ __device__ inline void crossing(int n, uint64_t need, M &&mass, NucleusShared &s
 // ceil(top_p * total); every mass is an integer sum, so the threshold and
 // the kept mass do not depend on how the row is split or visited.
 template <class D>
-__global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
+__global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
 {
     using E = typename D::Elem;
     constexpr int KB = D::kKeyBits;
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
         const float tc = fminf(sh.tc, (float)(30 - p.fix_bits));
         const uint32_t wc = __builtin_amdgcn_readfirstlane(
             min(entry_below(m + tc / scale) + 1u, (uint32_t)kWinKeys));
-        for (int q = tid; q <= kWinKeys; q += kThreads) {
+        for (int q = tid; q <= kWinKeys; q += kNucThreads) {
             uint32_t v = 0;
             if ((uint32_t)q >= wc && q < kWinKeys && (uint32_t)q != A && (uint32_t)q <= cm)
                 v = (uint32_t)fixed(key_value<D>(expand_key(cm - (uint32_t)q)));
@@ -996,16 +1001,16 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
         {
             const Span sp = make_span<D>(row, 0, p.V);
             const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
-            for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
-                u32x4 r[kTiles];
+            for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kNucTiles) {
+                u32x4 r[kNucTiles];
 #pragma unroll
-                for (int u = 0; u < kTiles; ++u) {
-                    const int64_t vi = base + u * kThreads + tid;
+                for (int u = 0; u < kNucTiles; ++u) {
+                    const int64_t vi = base + u * kNucThreads + tid;
                     r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
-                for (int u = 0; u < kTiles; ++u)
-                    if (base + u * kThreads + tid < sp.ngroups)
+                for (int u = 0; u < kNucTiles; ++u)
+                    if (base + u * kNucThreads + tid < sp.ngroups)
                         visit_group(r[u]);
             }
             auto visit_one = [&](uint32_t r) {
@@ -1028,8 +1033,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
             return n ? (uint64_t)n * fixed(key_value<D>(expand_key(cm - (uint32_t)idx))) : 0;
         };
         uint64_t win = 0;
-        for (int q = 0; q < kWinKeys / kThreads; ++q)
-            win += key_mass(tid * (kWinKeys / kThreads) + q);
+        for (int q = 0; q < kWinKeys / kNucThreads; ++q)
+            win += key_mass(tid * (kWinKeys / kNucThreads) + q);
         if (tid == 0 && A >= (uint32_t)kWinKeys)
             win += tiny_total;  // the tiny entry lies beyond the window
         const uint64_t total = block_sum(win + below, sh);
@@ -1055,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(Params p)
     while (done < KB) {
         const int w = min(kDigitBits, KB - done);
         const int nb = 1 << w;
-        for (int q = tid; q < nb; q += kThreads)
+        for (int q = tid; q < nb; q += kNucThreads)
             sh.hist[q] = 0;
         __syncthreads();
         unsigned long long mine = 0;
@@ -1560,7 +1565,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
             if (p.top_p)
-                hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kThreads), 0,
+                hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads), 0,
                                    stream, p);
             hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
                                dim3(kThreads), 0, stream, p);
