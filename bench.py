@@ -3,13 +3,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 
-A step is one spec_verify call (row statistics, accept scan, residual/bonus
-draw: four kernels) over one batch of synthetic logits already resident in
-HBM. Prints one JSON line: verified positions per second (B*(k+1) per step),
-the roofline of the dominant kernel (k_rowstats, which reads every logit row
-once: algorithmic bytes over its own mean duration, timed with HIP events
-that the library records around it on the launch stream), and the fp64 CPU
-oracle timed on a bounded sample of the same batch on the host cores.
+A step is one spec_verify call (row statistics; decision and draw sums;
+locate: three kernels) over one batch of synthetic logits already resident
+in HBM. Prints one JSON line: verified positions per second (B*(k+1) per
+step), the roofline of the dominant kernel (k_rowstats, which reads every
+logit row once: algorithmic bytes over its own mean duration, timed with HIP
+events that the library records around it on the launch stream, on every
+--event-every'th timed step: each event pair stalls the stream for a few
+microseconds, which would otherwise count in the step time), and the fp64
+CPU oracle timed on a bounded sample of the same batch on the host cores.
 
     python bench.py --copy-probe BYTES
 runs a plain device copy of known size (the calibration for rocprofv3 HBM
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft positions/sec (B*(k+1)/s) + achieved HBM GB/s vs peak, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD specification
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "k_rowstats_c5_hbm_counters.txt")
+EVENT_EVERY = 4  # set from --event-every
 
 
 def log(msg: str) -> None:
@@ -132,6 +135,22 @@ def timed_oracle(fn, units: float, unit: str, sample: str) -> dict:
             "sample": f"{sample}, {nthreads} threads, {dt:.2f} s wall"}
 
 
+def sampled(i: int) -> bool:
+    """Timed steps that carry a kernel event pair."""
+    return i % EVENT_EVERY == 0
+
+
+def elapsed_ms(hip, ev, K: int) -> list:
+    """Durations of the sampled steps' event pairs, sorted."""
+    ms = []
+    for i in range(K):
+        if sampled(i):
+            m = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(m), ev[i][0], ev[i][1]) == 0
+            ms.append(m.value)
+    return sorted(ms)
+
+
 def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
     """Greedy tree verification on workload t3: nodes per second, and the
     node-row kernel's bandwidth (each node row read once, HIP events)."""
@@ -157,14 +176,10 @@ def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(events=(ev[i][0].value, ev[i][1].value))
+        step(events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = []
-    for a, b in ev:
-        m = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(m), a, b) == 0
-        ms.append(m.value)
+    ms = elapsed_ms(hip, ev, K)
     row_mean = sum(ms) / len(ms)
     nodes = int(tb.n_nodes.sum())
     nbytes = tb.bytes_read()
@@ -212,13 +227,16 @@ def bench_lookup(K: int, W: int, cpu: bool) -> dict:
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
+    for i, (a, b) in enumerate(evs):
+        if sampled(i):
+            a.record()
         sv.spec_prompt_lookup(ctx, lens, lw.n_min, lw.n_max, lw.k, out=out)
-        b.record()
+        if sampled(i):
+            b.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    k_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    k_list = [a.elapsed_time(b) for i, (a, b) in enumerate(evs) if sampled(i)]
+    k_ms = sum(k_list) / len(k_list)
     nbytes = int(lens.to(torch.int64).sum()) * 4
     ms_step = elapsed * 1e3 / K
     res = {"entry_point": "spec_prompt_lookup", "workload": f"{lw.name}: {lw.description}",
@@ -243,6 +261,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the kernel's HIP event pair on every Nth timed step")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed calls for at least this long before the warmup steps: "
@@ -263,6 +283,8 @@ def main() -> int:
                     help="skip timing the top-p entry point on the same batch")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
+    global EVENT_EVERY
+    EVENT_EVERY = max(1, args.event_every)
 
     if args.gpus != 1:
         log(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU only "
@@ -317,12 +339,7 @@ def main() -> int:
            workspace=ws, out=outs[i % len(copies)], events=events)
 
     def event_ms():
-        ms = []
-        for a, b in ev:
-            m = ctypes.c_float()
-            assert hip.hipEventElapsedTime(ctypes.byref(m), a, b) == 0
-            ms.append(m.value)
-        return sorted(ms)
+        return elapsed_ms(hip, [(a.value, b.value) for a, b in ev], K)
 
     log(f"[bench] settle {args.settle_ms:.0f} ms, then warmup {W} steps, {len(copies)} rotating copies")
     n_settle = 0
@@ -338,7 +355,7 @@ def main() -> int:
     log(f"[bench] timing {K} steps")
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, events=(ev[i][0].value, ev[i][1].value))
+        step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -363,7 +380,8 @@ def main() -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i, events=(ev[i][0].value, ev[i][1].value), fn=sv.spec_verify_early_exit)
+            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None,
+                 fn=sv.spec_verify_early_exit)
         torch.cuda.synchronize()
         ee_elapsed = time.perf_counter() - t0
         loop_ms = event_ms()
@@ -475,6 +493,8 @@ def main() -> int:
             "traffic": traffic,
             "kernel_us_mean": k1_mean * 1e3,
             "kernel_us_median": k1_median * 1e3,
+            "events": f"HIP event pair around k_rowstats on every {EVENT_EVERY}th of the "
+                      f"{K} timed steps ({len(k1_ms)} samples)",
         },
     }
     if early is not None:

@@ -14,9 +14,10 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Four launches per call, stream-ordered, no host synchronisation. Every
-// hand-over between workgroups crosses a launch boundary, so no workgroup
-// ever waits for another and nothing needs device-scope atomics:
+// Three launches per call (top-p adds k_nucleus before k_draw),
+// stream-ordered, no host synchronisation. Every hand-over between
+// workgroups crosses a launch boundary, so no workgroup ever waits for
+// another and nothing needs device-scope atomics:
 //
 //   k_rowstats  one workgroup per 32 KiB chunk of every logit row the step
 //               needs (b-major). Each streams its chunk once with 16-byte
@@ -24,17 +25,18 @@
 //               2^((x - max) * log2(e)/tau)) for sampling rows, (max logit,
 //               lowest index of it) for greedy rows. This kernel carries
 //               all of the algorithmic HBM traffic and runs at copy speed.
-//   k_decide    one wave per sequence: fold the partials in chunk order,
-//               gather p_i(g_i) and q_i(g_i), draw Philox, run the
-//               left-to-right test, write the accepted prefix, and record
-//               the draw row j, its kind, the uniform v and the normalisers.
-//   k_draw      one workgroup per chunk of each sequence's draw row: fp64
-//               sum of the draw weights w = max(0, p_j - q_j) (or p_L for a
-//               bonus) over the chunk.
-//   k_locate    one workgroup per sequence: the chunk where the cumulative
-//               weight passes v * S, then the 2048-element tile, the group
-//               and the element, from one coalesced read of that chunk and
-//               fp64 block scans.
+//   k_draw      one workgroup per chunk of each sequence's draw row. Its
+//               first wave takes the sequence's decision: fold the partials
+//               in chunk order, gather p_i(g_i) and q_i(g_i), draw Philox,
+//               run the left-to-right test (every workgroup of the sequence
+//               gets the same result; the first one writes the accepted
+//               prefix and the record of the draw row j, its kind, the
+//               uniform v and the normalisers). Then the workgroup sums the
+//               draw weights w = max(0, p_j - q_j) (or p_L for a bonus) over
+//               its chunk in fp64, per segment and in all.
+//   k_locate    one wave per sequence: the chunk where the cumulative weight
+//               passes v * S, then the segment, the group and the element,
+//               from those sums and one read of the group.
 //
 // k_draw re-reads the one or two draw rows of each sequence (about a fifth
 // of the bytes k_rowstats reads). Doing those sums inside k_rowstats while
@@ -42,7 +44,9 @@
 // re-reading them afterwards: the sums wait on decisions, and the waiting
 // workgroups hold slots the streaming needs. Folding the locate into k_draw
 // (last workgroup of a sequence) costs more than its own launch: its
-// registers halve the occupancy of the latency-bound sums.
+// registers halve the occupancy of the latency-bound sums. The decision in
+// k_draw costs each workgroup a few microseconds of one wave, hidden behind
+// the other workgroups' reads, and saves a launch.
 //
 // Nothing here is a dense contraction, so there is no MFMA: the step is bound
 // by HBM bandwidth.
@@ -87,7 +91,7 @@ struct Params {
     uint32_t key0, key1, seq_base;
     int64_t n_row_items;  // B * (2k+1) * nc
     float2 *partials;     // [B][2k+1][nc], written by k_rowstats
-    Decision *decisions;  // [B], written by k_decide
+    Decision *decisions;  // [B], written by the decision (k_draw, or early exit)
     double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the draw row
     double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
     const float *top_p;   // [B] or null: nucleus parameter per sequence
@@ -96,6 +100,7 @@ struct Params {
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
     int32_t *ee_done;     // [k+1][B]: early exit: chunks finished per position
+    int32_t decide_in_draw;  // k_draw takes the decisions itself (not early exit)
     int32_t *out_tokens, *num_accepted;
     AuxDev aux;
 };
@@ -113,7 +118,7 @@ struct LocateShared {
 // accepted prefix, num_accepted, diagnostics and the decision record.
 // ===========================================================================
 template <class D>
-__device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
+__device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane, bool write)
 {
     using E = typename D::Elem;
     const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
@@ -161,11 +166,11 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
         const uint64_t stop = __ballot(lane < L && amax != g);
         const int j = stop ? __ffsll((unsigned long long)stop) - 1 : L;
         const int tok = __shfl(amax, j, kWave);
-        if (lane <= k)
+        if (write && lane <= k)
             out[lane] = lane < j ? g : (lane == j ? tok : -1);
         dec.row = j;
         dec.kind = SPEC_DRAW_GREEDY;
-        if (lane == 0)
+        if (write && lane == 0)
             p.num_accepted[b] = j;
     } else if (status == SPEC_SEQ_OK) {
         const float scale = temp_scale(tau);
@@ -225,7 +230,7 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
         if (__shfl((int)qzero, j, kWave)) {
             status = SPEC_SEQ_QZERO;
         } else {
-            if (lane <= k && lane != j)
+            if (write && lane <= k && lane != j)
                 out[lane] = lane < j ? g : -1;  // position j: written by the locate
             dec.row = j;
             dec.kind = j < L ? SPEC_DRAW_RESIDUAL : SPEC_DRAW_BONUS;
@@ -237,21 +242,23 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
             dec.zd = __shfl(dz, j, kWave);
             dec.tht = __shfl(tth, j, kWave);
             dec.thd = __shfl(dth, j, kWave);
-            if (lane == 0)
+            if (write && lane == 0)
                 p.num_accepted[b] = j;
         }
     }
 
     if (status != SPEC_SEQ_OK) {
-        if (lane <= k)
+        if (write && lane <= k)
             out[lane] = -1;
-        if (lane == 0)
+        if (write && lane == 0)
             p.num_accepted[b] = 0;
         dec.row = -1;
         dec.kind = SPEC_DRAW_NONE;
         pg = qg = NAN;
         amax = -1;
     }
+    if (!write)
+        return dec;
     const AuxDev &aux = p.aux;
     if (lane < k) {
         if (aux.p_g) aux.p_g[b * k + lane] = lane < L ? pg : NAN;
@@ -270,6 +277,7 @@ __device__ __forceinline__ void decide(const Params &p, int64_t b, int lane)
             if (aux.resid_mass) aux.resid_mass[b] = NAN;
         }
     }
+    return dec;
 }
 
 // Draw weight of one token: w = max(0, p - q) for a residual (p alone for a
@@ -495,7 +503,7 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
     const int nc = p.nc;
     const Decision dec = p.decisions[b];
     if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
-        return;  // greedy or error: k_decide wrote everything
+        return;  // greedy or error: the decision wrote everything
     const DrawRows<D> r = draw_rows<D>(p, b, dec);
     const double *mw = reinterpret_cast<const double *>(p.masses + b * (int64_t)nc);
     const bool staged = nc <= kMaxLdsChunks / 2;
@@ -1109,7 +1117,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
     if (!valid_len(L, k) || !valid_temp(tau))
-        return;  // k_decide reports the sequence
+        return;  // the decision reports the sequence
     const bool greedy = tau == 0.f;
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
@@ -1125,27 +1133,32 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
         p.partials[item] = part;
 }
 
-// One wave per sequence.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_decide(Params p)
-{
-    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-    if (b < p.B)
-        decide<D>(p, b, (int)(threadIdx.x % kWave));
-}
-
 // One workgroup per chunk of each sequence's draw row, sequences in reverse
 // order: the rows k_rowstats read last may still be in the last-level cache.
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_draw(Params p)
 {
     __shared__ DrawShared sh;
+    __shared__ Decision sdec;
     const int nc = p.nc;
     const int64_t b = (int64_t)p.B - 1 - (int64_t)(blockIdx.x / nc);
     const int c = (int)(blockIdx.x % nc);
-    const Decision dec = p.decisions[b];  // uniform: one scalar load
+    Decision dec;
+    if (p.decide_in_draw) {
+        // Every workgroup of the sequence takes its decision (the first one
+        // also writes the prefix, the counts and the record for the locate).
+        if (threadIdx.x < kWave) {
+            const Decision d = decide<D>(p, b, (int)threadIdx.x, c == 0);
+            if (threadIdx.x == 0)
+                sdec = d;
+        }
+        __syncthreads();
+        dec = sdec;
+    } else {
+        dec = p.decisions[b];  // uniform: one scalar load
+    }
     if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
-        return;  // greedy or error: k_decide wrote everything
+        return;  // greedy or error: the decision wrote everything
     chunk_weight_sums<D>(p, b, c, dec, sh);
 }
 
@@ -1567,8 +1580,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
             if (p.top_p)
                 hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads), 0,
                                    stream, p);
-            hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
-                               dim3(kThreads), 0, stream, p);
+            p.decide_in_draw = 1;
         } else {
             hipLaunchKernelGGL(k_ee_rowstats0<D>, dim3((unsigned)(nb * 2 * nc)), dim3(kThreads),
                                0, stream, p);
