@@ -38,6 +38,9 @@ constexpr int kFoldBatch = 8;       // partial loads in flight per lane when fol
 constexpr int kDeviceVersion = 300;  // 0.3.0
 // Early exit: positions below this one get a launch each; the rest share one.
 constexpr int kEarlyExitSingle = 3;
+// Draw grids up to this many workgroups (about 16 per CU) take their
+// decisions inside k_draw; larger ones get a k_decide launch first.
+constexpr int64_t kFoldDecisionItems = 4096;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 

@@ -14,7 +14,7 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Three launches per call (top-p adds k_nucleus before k_draw),
+// Three or four launches per call (top-p adds k_nucleus before k_draw),
 // stream-ordered, no host synchronisation. Every hand-over between
 // workgroups crosses a launch boundary, so no workgroup ever waits for
 // another and nothing needs device-scope atomics:
@@ -25,15 +25,17 @@
 //               2^((x - max) * log2(e)/tau)) for sampling rows, (max logit,
 //               lowest index of it) for greedy rows. This kernel carries
 //               all of the algorithmic HBM traffic and runs at copy speed.
-//   k_draw      one workgroup per chunk of each sequence's draw row. Its
-//               first wave takes the sequence's decision: fold the partials
-//               in chunk order, gather p_i(g_i) and q_i(g_i), draw Philox,
-//               run the left-to-right test (every workgroup of the sequence
-//               gets the same result; the first one writes the accepted
-//               prefix and the record of the draw row j, its kind, the
-//               uniform v and the normalisers). Then the workgroup sums the
-//               draw weights w = max(0, p_j - q_j) (or p_L for a bonus) over
-//               its chunk in fp64, per segment and in all.
+//   k_decide    one wave per sequence: fold the partials in chunk order,
+//               gather p_i(g_i) and q_i(g_i), draw Philox, run the
+//               left-to-right test, write the accepted prefix, and record
+//               the draw row j, its kind, the uniform v and the normalisers.
+//               For batches whose draw grid is small (kFoldDecisionItems),
+//               the first wave of every k_draw workgroup takes its sequence's
+//               decision instead (all get the same; the first one writes it)
+//               and this launch is skipped.
+//   k_draw      one workgroup per chunk of each sequence's draw row: sums
+//               of the draw weights w = max(0, p_j - q_j) (or p_L for a
+//               bonus) over its chunk in fp64, per segment and in all.
 //   k_locate    one wave per sequence: the chunk where the cumulative weight
 //               passes v * S, then the segment, the group and the element,
 //               from those sums and one read of the group.
@@ -45,8 +47,9 @@
 // workgroups hold slots the streaming needs. Folding the locate into k_draw
 // (last workgroup of a sequence) costs more than its own launch: its
 // registers halve the occupancy of the latency-bound sums. The decision in
-// k_draw costs each workgroup a few microseconds of one wave, hidden behind
-// the other workgroups' reads, and saves a launch.
+// k_draw costs each workgroup a few microseconds of one wave before its
+// reads: worth a launch when the draw grid fits the chip about once, not
+// when it takes several rounds.
 //
 // Nothing here is a dense contraction, so there is no MFMA: the step is bound
 // by HBM bandwidth.
@@ -100,7 +103,7 @@ struct Params {
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
     int32_t *ee_done;     // [k+1][B]: early exit: chunks finished per position
-    int32_t decide_in_draw;  // k_draw takes the decisions itself (not early exit)
+    int32_t decide_in_draw;  // k_draw takes the decisions itself (small batches)
     int32_t *out_tokens, *num_accepted;
     AuxDev aux;
 };
@@ -1133,6 +1136,15 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
         p.partials[item] = part;
 }
 
+// One wave per sequence (large batches: see kFoldDecisionItems).
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_decide(Params p)
+{
+    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    if (b < p.B)
+        decide<D>(p, b, (int)(threadIdx.x % kWave), true);
+}
+
 // One workgroup per chunk of each sequence's draw row, sequences in reverse
 // order: the rows k_rowstats read last may still be in the last-level cache.
 template <class D>
@@ -1580,7 +1592,11 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
             if (p.top_p)
                 hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads), 0,
                                    stream, p);
-            p.decide_in_draw = 1;
+            if (nb * nc <= kFoldDecisionItems)
+                p.decide_in_draw = 1;
+            else
+                hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
+                                   dim3(kThreads), 0, stream, p);
         } else {
             hipLaunchKernelGGL(k_ee_rowstats0<D>, dim3((unsigned)(nb * 2 * nc)), dim3(kThreads),
                                0, stream, p);
