@@ -95,6 +95,12 @@ def _load():
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                              ctypes.c_uint32] + [P] * 12
         lib.spec_verify_topp_ref.restype = ctypes.c_int
+        lib.ref_topk_row.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P, P]
+        lib.ref_topk_row.restype = ctypes.c_double
+        lib.spec_verify_filter_ref.argtypes = [P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                               ctypes.c_uint32] + [P] * 12
+        lib.spec_verify_filter_ref.restype = ctypes.c_int
         lib.ref_tree_greedy.argtypes = [P, P, P, ctypes.c_int, P, P]
         lib.ref_tree_greedy.restype = ctypes.c_int
         lib.spec_tree_ref.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int32, ctypes.c_int32,
@@ -169,6 +175,17 @@ def nucleus_row(row: np.ndarray, p: np.ndarray, top_p: float):
     return q, float(kept), float(thr[0]), float(mg[0])
 
 
+def topk_row(row: np.ndarray, p: np.ndarray, top_k: int):
+    """Top-k filter of one row (reading TK1). row: the logits; p: their
+    softmax (or an already filtered row). Returns (filtered p, kept mass,
+    threshold logit)."""
+    row, dt = _logits(row)
+    q = np.ascontiguousarray(np.asarray(p, dtype=np.float64)).copy()
+    thr = np.zeros(1)
+    kept = _load().ref_topk_row(_ptr(row), dt, row.shape[-1], int(top_k), _ptr(q), _ptr(thr))
+    return q, float(kept), float(thr[0])
+
+
 def round_sampling(p: np.ndarray, q: np.ndarray, g, u, v):
     """One sampling round from explicit probabilities and uniforms.
 
@@ -217,12 +234,15 @@ def round_greedy(amax, g):
 
 def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
                     draft_len, temperature, seed: int, seq_base: int = 0,
-                    nthreads: int = 1, top_p=None) -> dict:
+                    nthreads: int = 1, top_p=None, top_k=None) -> dict:
     """The whole step on host arrays (see spec_verify_ref.c for the contract).
 
     target [B, k+1, V] and draft [B, k, V] are float32 or uint16 (bf16 bits).
     ``nthreads`` > 1 runs disjoint slices of sequences in parallel threads;
     each slice keeps its global sequence index, so results do not change.
+    ``top_p`` (fp32) and ``top_k`` (int32), scalars or [B], filter every
+    sampling row (readings TP1, TK1); ``margin_nucleus`` is returned with
+    ``top_p``.
     """
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
@@ -240,6 +260,9 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
     tp = None
     if top_p is not None:
         tp = np.ascontiguousarray(np.broadcast_to(np.asarray(top_p, dtype=np.float32), (B,)).copy())
+    tk = None
+    if top_k is not None:
+        tk = np.ascontiguousarray(np.broadcast_to(np.asarray(top_k, dtype=np.int32), (B,)).copy())
 
     res = dict(
         out_tokens=np.full((B, k + 1), -1, dtype=np.int32),
@@ -262,6 +285,17 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         if b1 <= b0:
             return 0
         sl = slice(b0, b1)
+        if tk is not None:
+            mn = res["margin_nucleus"][sl] if tp is not None else None
+            outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
+                                         "argmax", "resid_mass", "margin_accept", "margin_draw")]
+            return lib.spec_verify_filter_ref(
+                _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
+                _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]), _ptr(tk[sl]),
+                _ptr(tp[sl]) if tp is not None else None, b1 - b0, k, V,
+                ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF),
+                *[_ptr(o) for o in outs], _ptr(mn) if mn is not None else None,
+                _ptr(res["draw_row"][sl]), _ptr(res["draw_kind"][sl]))
         if tp is None:
             outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
                                          "argmax", "resid_mass", "margin_accept", "margin_draw",

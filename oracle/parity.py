@@ -36,20 +36,24 @@ def host_threads(cap: int = 16) -> int:
     return max(1, min(cap, n))
 
 
-def oracle_on(host: dict, seed: int, seqs=None, nthreads: int = 1, top_p=None) -> dict:
+def oracle_on(host: dict, seed: int, seqs=None, nthreads: int = 1, top_p=None,
+              top_k=None) -> dict:
     """Run the oracle on all sequences, or on the listed ones (each with its
-    own global index as the Philox sequence index). ``top_p``: None, or [B]
-    nucleus parameters."""
+    own global index as the Philox sequence index). ``top_p`` / ``top_k``:
+    None, or [B] filter parameters."""
     t, d, g, L, tau = (host["target"], host["draft"], host["draft_tokens"], host["draft_len"],
                        host["temperature"])
     tp = None if top_p is None else np.broadcast_to(np.asarray(top_p, np.float32), (len(L),))
+    tk = None if top_k is None else np.broadcast_to(np.asarray(top_k, np.int32), (len(L),))
     if seqs is None:
-        return spec_verify_ref(t, d, g, L, tau, seed, seq_base=0, nthreads=nthreads, top_p=tp)
+        return spec_verify_ref(t, d, g, L, tau, seed, seq_base=0, nthreads=nthreads, top_p=tp,
+                               top_k=tk)
     seqs = [int(b) for b in seqs]
 
     def one(b):
         return spec_verify_ref(t[b:b + 1], d[b:b + 1], g[b:b + 1], L[b:b + 1], tau[b:b + 1], seed,
-                               seq_base=b, top_p=None if tp is None else tp[b:b + 1])
+                               seq_base=b, top_p=None if tp is None else tp[b:b + 1],
+                               top_k=None if tk is None else tk[b:b + 1])
 
     if nthreads > 1:
         with ThreadPoolExecutor(max_workers=nthreads) as ex:

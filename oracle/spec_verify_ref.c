@@ -52,6 +52,13 @@
  *       reaches top_p times the row's mass; ties at the boundary are all
  *       kept. The kept tokens are renormalised and the rest get 0. The
  *       draft row is filtered with the same top_p. top_p >= 1 keeps all.
+ *   TK1 top-k (the same key limitation, for the other common sampling
+ *       parameter): keep whole levels from the top until they hold at
+ *       least top_k tokens -- every token tied with the top_k-th largest
+ *       logit is kept -- and renormalise; top_k <= 0 or >= V keeps all.
+ *       With both parameters the row is filtered by top-k first and the
+ *       nucleus is then taken on the result (the usual order of sampling
+ *       pipelines; the pages give no order).
  *   P1  prompt lookup: n-gram sizes are tried from n_max down to n_min; for
  *       a size n the match is the most recent occurrence of the context's
  *       last n tokens that ends before the last token; the proposal is the
@@ -198,6 +205,56 @@ double ref_nucleus_row(const void *row, int dtype, int64_t V, double top_p, doub
         a = b;
     }
     free(it);
+    for (int64_t x = 0; x < V; x++) {
+        double lx = ref_logit(row, dtype, (size_t)x);
+        p[x] = lx >= *thr ? p[x] / kept : 0.0;
+    }
+    return kept;
+}
+
+/* ------------------------------------------------------------------ */
+/* Top-k filter of one probability row (reading TK1): levels are visited */
+/* from the largest logit down and kept until they hold at least top_k  */
+/* tokens; that level and all above it are kept, the rest get 0, and    */
+/* the kept tokens are renormalised in place. Returns the kept mass     */
+/* before renormalisation; *thr = the boundary logit (keep x >= *thr).  */
+/* top_k <= 0 or >= V keeps everything (*thr = -inf).                    */
+/* ------------------------------------------------------------------ */
+double ref_topk_row(const void *row, int dtype, int64_t V, int64_t top_k, double *p, double *thr)
+{
+    double total = 0.0;
+    for (int64_t x = 0; x < V; x++)
+        total += p[x];
+    *thr = -INFINITY;
+    if (top_k <= 0 || top_k >= V)
+        return total;
+    ref_level_item *it = malloc(sizeof(ref_level_item) * (size_t)V);
+    if (!it)
+        return NAN;
+    for (int64_t x = 0; x < V; x++) {
+        it[x].x = ref_logit(row, dtype, (size_t)x);
+        if (it[x].x == 0.0)
+            it[x].x = 0.0; /* -0 and +0 are one level */
+        it[x].i = x;
+    }
+    qsort(it, (size_t)V, sizeof(ref_level_item), ref_level_desc);
+    int64_t count = 0;
+    for (int64_t a = 0; a < V;) {
+        int64_t b = a;
+        while (b < V && it[b].x == it[a].x)
+            b++;
+        count += b - a;
+        if (count >= top_k) {
+            *thr = it[a].x;
+            break;
+        }
+        a = b;
+    }
+    free(it);
+    double kept = 0.0;
+    for (int64_t x = 0; x < V; x++)
+        if (ref_logit(row, dtype, (size_t)x) >= *thr)
+            kept += p[x];
     for (int64_t x = 0; x < V; x++) {
         double lx = ref_logit(row, dtype, (size_t)x);
         p[x] = lx >= *thr ? p[x] / kept : 0.0;
@@ -398,7 +455,8 @@ int ref_round_greedy(const int64_t *amax, const int32_t *g, int L, int32_t *out)
 /* ------------------------------------------------------------------ */
 static int verify_batch(const void *target, const void *draft, int dtype,
                         const int32_t *draft_tokens, const int32_t *draft_len,
-                        const float *temperature, const float *top_p, int32_t B, int32_t k,
+                        const float *temperature, const int32_t *top_k, const float *top_p,
+                        int32_t B, int32_t k,
                         int64_t V, uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
                         int32_t *num_accepted, int32_t *seq_status, double *p_g, double *q_g,
                         int32_t *argmax, double *resid_mass, double *margin_accept,
@@ -475,6 +533,16 @@ static int verify_batch(const void *target, const void *draft, int dtype,
                 ref_softmax_row(trow0 + (size_t)i * V * esz, dtype, V, tau, p + (size_t)i * V);
             for (int i = 0; i < L; i++)
                 ref_softmax_row(drow0 + (size_t)i * V * esz, dtype, V, tau, q + (size_t)i * V);
+            if (top_k && top_k[b] > 0 && (int64_t)top_k[b] < V) {
+                /* top-k first (TK1), on every target and draft row */
+                double thr;
+                for (int i = 0; i <= L; i++)
+                    ref_topk_row(trow0 + (size_t)i * V * esz, dtype, V, top_k[b],
+                                 p + (size_t)i * V, &thr);
+                for (int i = 0; i < L; i++)
+                    ref_topk_row(drow0 + (size_t)i * V * esz, dtype, V, top_k[b],
+                                 q + (size_t)i * V, &thr);
+            }
             if (top_p && top_p[b] < 1.0f) {
                 /* the same nucleus rule on every target and draft row */
                 const double tp = (double)top_p[b];
@@ -531,8 +599,8 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
                     double *resid_mass, double *margin_accept, double *margin_draw,
                     int32_t *draw_row, int32_t *draw_kind)
 {
-    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, B, k,
-                        V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, NULL, B,
+                        k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, NULL, draw_row,
                         draw_kind);
 }
@@ -550,8 +618,27 @@ int spec_verify_topp_ref(const void *target, const void *draft, int dtype,
                          double *margin_draw, double *margin_nucleus, int32_t *draw_row,
                          int32_t *draw_kind)
 {
-    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_p, B, k,
-                        V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, top_p,
+                        B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+                        argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
+                        draw_row, draw_kind);
+}
+
+/* The whole step with top-k and nucleus filtering (TK1 then TP1): top_k */
+/* [B] int32 (may be NULL: no top-k), top_p [B] fp32 (may be NULL: no    */
+/* top-p). The top-p checks and margins are those of spec_verify_topp_ref */
+/* (the nucleus margin is taken on the top-k-filtered row).               */
+int spec_verify_filter_ref(const void *target, const void *draft, int dtype,
+                           const int32_t *draft_tokens, const int32_t *draft_len,
+                           const float *temperature, const int32_t *top_k, const float *top_p,
+                           int32_t B, int32_t k, int64_t V, uint64_t seed, uint32_t seq_base,
+                           int32_t *out_tokens, int32_t *num_accepted, int32_t *seq_status,
+                           double *p_g, double *q_g, int32_t *argmax, double *resid_mass,
+                           double *margin_accept, double *margin_draw, double *margin_nucleus,
+                           int32_t *draw_row, int32_t *draw_kind)
+{
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_k, top_p,
+                        B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
                         draw_row, draw_kind);
 }

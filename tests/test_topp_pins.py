@@ -170,8 +170,14 @@ def test_losslessness_for_a_filtered_pair():
 
 TOPP_MUTATIONS = {
     "strict_crossing": ("if (cum >= target) {", "if (cum > target) {"),
-    "not_renormalised": ("p[x] = lx >= *thr ? p[x] / kept : 0.0;", "p[x] = lx >= *thr ? p[x] : 0.0;"),
-    "ties_cut": ("while (b < V && it[b].x == it[a].x)", "while (b < V && b == a)"),
+    "not_renormalised": ("    free(it);\n    for (int64_t x = 0; x < V; x++) {\n"
+                         "        double lx = ref_logit(row, dtype, (size_t)x);\n"
+                         "        p[x] = lx >= *thr ? p[x] / kept : 0.0;",
+                         "    free(it);\n    for (int64_t x = 0; x < V; x++) {\n"
+                         "        double lx = ref_logit(row, dtype, (size_t)x);\n"
+                         "        p[x] = lx >= *thr ? p[x] : 0.0;"),
+    "ties_cut": ("        while (b < V && it[b].x == it[a].x)\n            level += p[it[b++].i];",
+                 "        while (b < V && b == a)\n            level += p[it[b++].i];"),
     "lowest_first": ("return u->x > v->x ? -1 : 1;", "return u->x < v->x ? -1 : 1;"),
 }
 
