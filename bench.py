@@ -279,6 +279,8 @@ def main() -> int:
                     help="skip timing greedy tree verification (workload t3)")
     ap.add_argument("--no-lookup", action="store_true",
                     help="skip timing prompt-lookup drafting (workload p3)")
+    ap.add_argument("--no-top-k", action="store_true",
+                    help="skip timing spec_verify_top_k_top_p (top-k 50, top-p 0.95)")
     ap.add_argument("--no-top-p", action="store_true",
                     help="skip timing the top-p entry point on the same batch")
     ap.add_argument("--copy-probe", type=int, default=0)
@@ -434,7 +436,7 @@ def main() -> int:
                 "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
                 "roofline": roof(alg_bytes / (tp_ms * 1e-3) / 1e9,
                                  "the whole step (each row counted once; k_nucleus reads every "
-                                 "row twice more)")}
+                                 "bf16 row once more)")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
@@ -447,6 +449,49 @@ def main() -> int:
                 n_cpu * (w.k + 1), "positions/s",
                 f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-p")
         log(f"[bench] top-p {tp_ms:.4f} ms/step")
+    topk = None
+    if not args.no_top_k:
+        # The same batch with top-k 50 and then top-p 0.95 on every row.
+        log(f"[bench] top-k 50 + top-p 0.95: warmup {W} steps, timing {K} steps")
+        tk = torch.full((w.B,), 50, dtype=torch.int32, device="cuda:0")
+        tp = torch.full((w.B,), 0.95, dtype=torch.float32, device="cuda:0")
+
+        def fk(*a, **kw):
+            return sv.spec_verify_top_k_top_p(*a[:5], tk, tp, *a[5:], **kw)
+
+        for i in range(W):
+            step(i, fn=fk)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i, fn=fk)
+        torch.cuda.synchronize()
+        tk_ms = (time.perf_counter() - t0) * 1e3 / K
+        _, _, aux_tk = sv.spec_verify_top_k_top_p(copies[0].target, copies[0].draft,
+                                                  copies[0].draft_tokens, copies[0].draft_len,
+                                                  copies[0].temperature, tk, tp, seed, aux=True)
+        st = aux_tk["seq_status"].cpu()
+        topk = {"entry_point": "spec_verify_top_k_top_p", "top_k": 50, "top_p": 0.95,
+                "value": positions / (tk_ms * 1e-3), "unit": "positions/s", "ms_per_step": tk_ms,
+                "rows_filtered": t_rows + d_rows,
+                "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
+                "roofline": roof(alg_bytes / (tk_ms * 1e-3) / 1e9,
+                                 "the whole step (each row counted once; k_nucleus reads every "
+                                 "bf16 row once more)")}
+        if not args.no_cpu_baseline:
+            import oracle
+            from oracle import parity
+
+            n_cpu = 64
+            hs = wl.to_host_arrays(batch.select(range(n_cpu)))
+            topk["cpu_baseline"] = timed_oracle(
+                lambda nt: parity.oracle_on(hs, seed, nthreads=nt,
+                                            top_k=np.full(n_cpu, 50, np.int32),
+                                            top_p=np.full(n_cpu, 0.95, np.float32)),
+                n_cpu * (w.k + 1), "positions/s",
+                f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-k "
+                "and top-p")
+        log(f"[bench] top-k + top-p {tk_ms:.4f} ms/step")
     tree = None
     if not args.no_tree:
         tree = bench_tree(hip, ev, K, W, not args.no_cpu_baseline)
@@ -501,6 +546,8 @@ def main() -> int:
         result["early_exit"] = early
     if topp is not None:
         result["top_p"] = topp
+    if topk is not None:
+        result["top_k_top_p"] = topk
     if tree is not None:
         result["tree"] = tree
     if lookup is not None:

@@ -203,9 +203,10 @@ int spec_verify_early_exit(const void *target_logits, const void *draft_logits, 
  * temperature, before the tokens). top_p is [B] fp32 device memory and
  * must not be NULL; everything else is as for spec_verify, with aux->q_g
  * and p_g the filtered probabilities and resid_mass the filtered mass.
- * The nucleus of a row is found exactly (a radix select over the logits,
- * with the row masses summed in 64-bit fixed point), at the cost of
- * reading each filtered row two more times (three for fp32 logits).
+ * The nucleus of a row is found exactly, with the row masses summed in
+ * 64-bit fixed point: one more read of each filtered bf16 row (per-key
+ * counts), or a radix select over the logits (fp32 rows, and bf16 rows
+ * whose crossing falls outside the counted keys: two or three more reads).
  */
 int spec_verify_top_p(const void *target_logits, const void *draft_logits, int32_t dtype,
                       const int32_t *draft_tokens, const int32_t *draft_len,
@@ -213,6 +214,30 @@ int spec_verify_top_p(const void *target_logits, const void *draft_logits, int32
                       int32_t V, uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
                       int32_t *num_accepted, const spec_verify_aux_t *aux, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * The step with top-k and top-p sampling parameters (the same key
+ * limitation: verification uses the target's own sampling parameters).
+ * For a sampling sequence with 0 < top_k[b] < V, every target row i <= L
+ * and draft row i < L first keeps whole levels from the largest logit down
+ * until they hold at least top_k[b] tokens (every token tied with the
+ * top_k-th largest logit is kept) and is renormalised; then, if top_p is
+ * given and top_p[b] < 1, the nucleus is taken on that result as for
+ * spec_verify_top_p. top_k[b] <= 0 or >= V applies no top-k. Either
+ * pointer may be NULL (that filter is off) but not both; top_k is [B]
+ * int32 and top_p [B] fp32 device memory. Statuses, outputs and
+ * diagnostics are those of spec_verify_top_p, on the filtered rows. The
+ * top-k threshold is found exactly from per-key counts (bf16 rows, when
+ * the top_k-th token lies among the counted keys below the row max) or by
+ * a radix select over the counts.
+ */
+int spec_verify_top_k_top_p(const void *target_logits, const void *draft_logits, int32_t dtype,
+                            const int32_t *draft_tokens, const int32_t *draft_len,
+                            const float *temperature, const int32_t *top_k, const float *top_p,
+                            int32_t B, int32_t k, int32_t V, uint64_t seed, uint32_t seq_base,
+                            int32_t *out_tokens, int32_t *num_accepted,
+                            const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* ------------------------------------------------------------------------
  * Greedy verification of candidate trees.

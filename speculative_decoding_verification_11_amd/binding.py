@@ -28,7 +28,7 @@ DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
 STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
 
-EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_top_p",
+EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_top_p", "spec_verify_top_k_top_p",
             "spec_verify_workspace_size",
             "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_prompt_lookup",
             "spec_verify_strerror", "spec_verify_version")
@@ -94,6 +94,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.spec_verify_top_p.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, u64, u32, P, P,
                                           ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
         lib.spec_verify_top_p.restype = ctypes.c_int
+        lib.spec_verify_top_k_top_p.argtypes = [P, P, i32, P, P, P, P, P, i32, i32, i32, u64, u32,
+                                                P, P, ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
+        lib.spec_verify_top_k_top_p.restype = ctypes.c_int
         lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.spec_verify_tree_workspace_size.restype = ctypes.c_size_t
         lib.spec_verify_tree.argtypes = [P, i32, P, P, P, i32, i32, i32, P, P, P,
@@ -177,8 +180,44 @@ def spec_verify_top_p(target: torch.Tensor, draft: Optional[torch.Tensor],
                    seq_base, aux, workspace, out, events, top_p=tp)
 
 
+def _per_sequence(value, B, dtype, name, device):
+    """A scalar broadcast to [B], or a checked contiguous [B] tensor."""
+    if isinstance(value, torch.Tensor):
+        if (tuple(value.shape) != (B,) or value.dtype != dtype or value.device != device
+                or not value.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous [{B}] {dtype} on {device}")
+        return value
+    return torch.full((B,), value, dtype=dtype, device=device)
+
+
+def spec_verify_top_k_top_p(target: torch.Tensor, draft: Optional[torch.Tensor],
+                            draft_tokens: Optional[torch.Tensor],
+                            draft_len: Optional[torch.Tensor] = None,
+                            temperature: Union[float, torch.Tensor] = 1.0,
+                            top_k: Union[int, torch.Tensor, None] = 0,
+                            top_p: Union[float, torch.Tensor, None] = None, seed: int = 0, *,
+                            seq_base: int = 0, aux: bool = False,
+                            workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None,
+                            events: Optional[tuple] = None):
+    """spec_verify with top-k, then top-p, filtering of every target and
+    draft row (C entry point spec_verify_top_k_top_p). top_k: int or [B]
+    int32 (<= 0 or >= V: no top-k); top_p: None (no top-p), float or [B]
+    float32."""
+    B, dev = target.shape[0], target.device
+    tk = None if top_k is None else _per_sequence(
+        int(top_k) if not isinstance(top_k, torch.Tensor) else top_k, B, torch.int32, "top_k", dev)
+    tp = None if top_p is None else _per_sequence(
+        float(top_p) if not isinstance(top_p, torch.Tensor) else top_p, B, torch.float32, "top_p",
+        dev)
+    if tk is None and tp is None:
+        raise ValueError("top_k and top_p cannot both be None")
+    return _verify("spec_verify_top_k_top_p", target, draft, draft_tokens, draft_len, temperature,
+                   seed, seq_base, aux, workspace, out, events, top_p=tp, top_k=tk,
+                   filters=True)
+
+
 def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, seq_base, aux,
-            workspace, out, events, top_p=None):
+            workspace, out, events, top_p=None, top_k=None, filters=False):
     """Verify B drafted continuations on the GPU.
 
     target [B, k+1, V] and draft [B, k, V]: float32 or bfloat16, contiguous,
@@ -253,7 +292,10 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
 
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        extra = (top_p.data_ptr(),) if top_p is not None else ()
+        if filters:
+            extra = (_ptr(top_k), _ptr(top_p))
+        else:
+            extra = (top_p.data_ptr(),) if top_p is not None else ()
         rc = getattr(lib, entry)(
             target.data_ptr(), _ptr(draft) if k > 0 else None, dt,
             _ptr(draft_tokens) if k > 0 else None, _ptr(draft_len), temp.data_ptr(), *extra,

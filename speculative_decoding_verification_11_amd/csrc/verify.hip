@@ -98,6 +98,7 @@ struct Params {
     double2 *masses;      // [B][nc]: (sum w, sum p) per chunk of the draw row
     double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
     const float *top_p;   // [B] or null: nucleus parameter per sequence
+    const int32_t *top_k; // [B] or null: top-k parameter per sequence
     float2 *nucleus;      // [B][2k+1]: top-p (threshold logit, kept mass) per row
     int32_t fix_bits;     // top-p: fixed-point fraction bits of the row masses
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
@@ -205,7 +206,9 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
         // Top-p: each row keeps its logits >= its threshold, normalised by
         // the kept mass (k_nucleus); otherwise the whole row and Z.
         float tz = ts.z, tth = -INFINITY, dz = ds.z, dth = -INFINITY;
-        if (p.top_p && p.top_p[b] < 1.f) {
+        const bool filtered = (p.top_p && p.top_p[b] < 1.f) ||
+                              (p.top_k && p.top_k[b] > 0 && p.top_k[b] < V);
+        if (filtered) {
             if (lane <= L) {
                 const float2 n = p.nucleus[b * rows + lane];
                 tth = n.x;
@@ -743,10 +746,15 @@ constexpr int kNucThreads = 512;
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kNucTiles = 4;  // 16-byte loads in flight per thread (counting pass)
 
+struct RadixBins {
+    unsigned long long hist[kBins];  // fixed-point mass per digit
+    uint32_t cnt[kBins];             // elements per digit (top-k)
+};
+
 struct NucleusShared {
     union {
-        unsigned long long hist[kBins];  // radix pass: fixed-point mass per digit
-        uint32_t cnt[kWinKeys + 1];      // window pass: elements per key
+        RadixBins rx;                 // radix passes
+        uint32_t cnt[kWinKeys + 1];   // window pass: elements per key
     };
     unsigned long long wsum[kNucWaves];
     unsigned long long above;
@@ -858,10 +866,282 @@ __device__ inline void crossing(int n, uint64_t need, M &&mass, NucleusShared &s
     __syncthreads();
 }
 
-// One workgroup per row of every sequence with 0 < top_p < 1. The kept set
-// is the smallest run of keys from the top whose fixed-point mass reaches
-// ceil(top_p * total); every mass is an integer sum, so the threshold and
-// the kept mass do not depend on how the row is split or visited.
+// Result of a selection: the threshold key (keep keys >= it) and the
+// fixed-point mass of the kept tokens.
+struct Selection {
+    uint32_t key;
+    unsigned long long kept;
+};
+
+// Radix select over the order keys of a row, kDigitBits at a time from the
+// top, among the tokens with key >= lo. BY_COUNT: the crossing of the
+// running count reaching `count` (top-k); otherwise of the running
+// fixed-point mass reaching ceil(top_p * the mass of those tokens).
+template <class D, bool BY_COUNT>
+__device__ __forceinline__ Selection radix_select(const typename D::Elem *row, int64_t V, float m, float scale,
+                                  float fscale, float zlim, uint32_t lo, int64_t count,
+                                  float top_p, NucleusShared &sh)
+{
+    constexpr int KB = D::kKeyBits;
+    const int tid = threadIdx.x;
+    auto fixed = [&](float x) {
+        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
+    };
+    uint64_t need = 0, above = 0, mass_above = 0;
+    uint32_t prefix = 0;
+    int done = 0;
+    Selection res{0u, 0ull};
+    while (done < KB) {
+        const int w = min(kDigitBits, KB - done);
+        const int nb = 1 << w;
+        for (int q = tid; q < nb; q += kNucThreads) {
+            sh.rx.hist[q] = 0;
+            sh.rx.cnt[q] = 0;
+        }
+        __syncthreads();
+        unsigned long long mine = 0;
+        for_each_logit<D>(row, V, [&](float x) {
+            const float t = (x - m) * scale;
+            if (!BY_COUNT && t < zlim)
+                return;  // weighs 0 (a count still counts it)
+            const uint32_t key = order_key<D>(x);
+            if (key < lo || (done != 0 && (key >> (KB - done)) != prefix))
+                return;
+            const uint32_t bin = (key >> (KB - done - w)) & (uint32_t)(nb - 1);
+            if (BY_COUNT)
+                atomicAdd(&sh.rx.cnt[bin], 1u);
+            if (t >= zlim) {
+                const unsigned long long wf = fixed(x);
+                atomicAdd(&sh.rx.hist[bin], wf);
+                mine += wf;
+            }
+        });
+        if (done == 0)
+            need = BY_COUNT ? (uint64_t)count : mass_target(block_sum(mine, sh), top_p);
+        __syncthreads();
+        if (BY_COUNT)
+            crossing(nb, need - above,
+                     [&](int q) -> uint64_t { return sh.rx.cnt[nb - 1 - q]; }, sh);
+        else
+            crossing(nb, need - above, [&](int q) -> uint64_t { return sh.rx.hist[nb - 1 - q]; },
+                     sh);
+        const int d = nb - 1 - max(sh.digit, 0);  // the crossing always exists here
+        above += sh.above;
+        if (BY_COUNT) {  // the masses of the bins above d
+            uint64_t mm = 0;
+            for (int q = tid; q < nb; q += kNucThreads)
+                mm += q > d ? sh.rx.hist[q] : 0ull;
+            mass_above += block_sum(mm, sh);
+        }
+        prefix = (prefix << w) | (uint32_t)d;
+        done += w;
+        if (done == KB)
+            res = Selection{prefix, (BY_COUNT ? mass_above : above) + sh.rx.hist[d]};
+        __syncthreads();  // the bins are cleared next pass
+    }
+    return res;
+}
+
+// One counting pass over a bf16 row (see the top-p notes above). Top-p
+// alone: only the entries that can hold the crossing are counted, the
+// rest add their weight from the table. With top-k: every window entry is
+// counted, the top-k threshold is the entry where the running count
+// reaches top_k, and the nucleus, if any, is taken among the entries up
+// to it. Returns false when the answer is not in the window (then the
+// radix passes decide).
+template <class D>
+__device__ __forceinline__ bool window_select(const typename D::Elem *row, int64_t V, float m, float scale,
+                              int fix_bits, float zlim, float tc_mass, bool k_on, int64_t top_k,
+                              bool p_on, float top_p, float2 *out, NucleusShared &sh)
+{
+    const int tid = threadIdx.x;
+    const float fscale = __uint_as_float((uint32_t)(127 + fix_bits) << 23);  // 2^fix_bits
+    auto fixed = [&](float x) {
+        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
+    };
+    // In raw bits r, with magnitude u = r & 0x7fff and
+    // d = max(u - kTinyBits + 1, 0), the window entry is A - d for a
+    // positive and A + d for a negative value, A being the entry of the
+    // tiny values (d = 0), all of it in 16-bit arithmetic: two elements per
+    // 32-bit word.
+    const uint32_t cm = compress_key(order_key<D>(m));
+    const uint32_t A = cm - kTinyIdx;
+    // Window entry of the lowest bf16 value at or below x (x rounded down
+    // to bf16).
+    auto entry_below = [&](float x) {
+        const uint32_t bx = __float_as_uint(x);
+        uint32_t r = bx >> 16;
+        if ((bx & 0xffffu) && (bx & 0x80000000u))
+            r += 1u;  // a truncated negative value: one step further down
+        return cm - compress_key((r & 0x8000u) ? (~r & 0xffffu) : (r | 0x8000u));
+    };
+    // Entries from iz on hold values below m + (zlim - 2) / scale: they
+    // weigh 0. Top-p alone: entries in [kWinKeys, iz) have mass but no
+    // counter (summed one by one); with top-k they lie below every counted
+    // entry and play no part.
+    const uint32_t iz =
+        __builtin_amdgcn_readfirstlane(entry_below(m + (zlim - 2.f) / scale) + 1u);
+    const bool wide = !k_on && iz > (uint32_t)kWinKeys;
+    // Top-p alone: entries from wc on hold values with (x - m) * scale < tc.
+    // Together those weigh at most V * 2^tc = (1 - top_p) / 4 of the row, so
+    // the crossing lies above them; and each weighs below 2^31 in fixed
+    // point. They are not counted: their entries hold that weight instead,
+    // which each element adds to the total. With top-k, wc = kWinKeys.
+    const float tc = fminf(tc_mass, (float)(30 - fix_bits));
+    const uint32_t wc = k_on ? (uint32_t)kWinKeys
+                             : __builtin_amdgcn_readfirstlane(
+                                   min(entry_below(m + tc / scale) + 1u, (uint32_t)kWinKeys));
+    for (int q = tid; q <= kWinKeys; q += kNucThreads) {
+        uint32_t v = 0;
+        if ((uint32_t)q >= wc && q < kWinKeys && (uint32_t)q != A && (uint32_t)q <= cm)
+            v = (uint32_t)fixed(key_value<D>(expand_key(cm - (uint32_t)q)));
+        sh.cnt[q] = v;
+    }
+    __syncthreads();
+    unsigned long long below = 0, tiny = 0;
+    const u16x2 a2 = (u16x2)(unsigned short)A;
+    const u16x2 w2 = (u16x2)(unsigned short)kWinKeys;
+    const u16x2 wm2 = (u16x2)(unsigned short)(kWinKeys - 1);
+    const u16x2 tb2 = (u16x2)(unsigned short)kTinyBits;
+    const u16x2 tbm2 = (u16x2)(unsigned short)(kTinyBits - 1u);
+    // Tiny values and values beyond the window with mass: one by one
+    // (their entries, A and kWinKeys, hold no weight).
+    auto rare = [&](uint32_t r, uint32_t idx) {
+        const bool is_tiny = (r & 0x7fffu) < kTinyBits;
+        const bool beyond = wide && idx >= (uint32_t)kWinKeys && idx < iz;
+        const unsigned long long f = fixed(__uint_as_float(r << 16));
+        tiny += is_tiny ? f : 0ull;
+        below += !is_tiny && beyond ? f : 0ull;
+    };
+    auto visit_slot = [&](uint32_t slot) {
+        const uint32_t v = sh.cnt[slot];
+        if (slot < wc)
+            atomicAdd(&sh.cnt[slot], 1u);
+        below += slot < wc ? 0u : v;
+    };
+    // Eight elements (one 16-byte load): all window reads are issued before
+    // the counts and the sums, so one wait covers them.
+    auto visit_group = [&](const u32x4 &g) {
+        const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+        uint32_t idx[4], slot[8];
+        bool any_rare = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u16x2 u = as_u16x2(w[j] & 0x7fff7fffu);
+            const u16x2 d = __builtin_bit_cast(
+                u16x2, __builtin_elementwise_max(__builtin_bit_cast(i16x2, u - tbm2), (i16x2)0));
+            const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
+            idx[j] = (as_u32(a2 + d) & neg) | (as_u32(a2 - d) & ~neg);
+            const uint32_t s2 = as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), w2));
+            slot[2 * j] = s2 & 0xffffu;
+            slot[2 * j + 1] = s2 >> 16;
+            const bool has_tiny = as_u32(__builtin_elementwise_min(u, tb2)) != as_u32(tb2);
+            const bool has_beyond =
+                as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), wm2)) != idx[j];
+            any_rare |= has_tiny || (wide && has_beyond);
+        }
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = sh.cnt[slot[j]];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (slot[j] < wc)
+                atomicAdd(&sh.cnt[slot[j]], 1u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            below += slot[j] < wc ? 0u : v[j];
+        if (any_rare) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                rare(w[j] & 0xffffu, idx[j] & 0xffffu);
+                rare(w[j] >> 16, idx[j] >> 16);
+            }
+        }
+    };
+    {
+        const Span sp = make_span<D>(row, 0, V);
+        const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
+        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kNucTiles) {
+            u32x4 r[kNucTiles];
+#pragma unroll
+            for (int u = 0; u < kNucTiles; ++u) {
+                const int64_t vi = base + u * kNucThreads + tid;
+                r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < kNucTiles; ++u)
+                if (base + u * kNucThreads + tid < sp.ngroups)
+                    visit_group(r[u]);
+        }
+        auto visit_one = [&](uint32_t r) {
+            const uint32_t u = r & 0x7fffu;
+            const uint32_t d = u < kTinyBits ? 0u : u - (kTinyBits - 1u);
+            const uint32_t idx = ((r & 0x8000u) ? A + d : A - d) & 0xffffu;
+            visit_slot(min(idx, (uint32_t)kWinKeys));
+            rare(r, idx);
+        };
+        if (sp.s + tid < sp.a)
+            visit_one((uint32_t)row[sp.s + tid]);
+        if (sp.z + tid < sp.e)
+            visit_one((uint32_t)row[sp.z + tid]);
+    }
+    const uint64_t tiny_total = block_sum(tiny, sh);
+    auto key_mass = [&](int idx) -> uint64_t {
+        if ((uint32_t)idx == A)
+            return tiny_total;
+        const uint32_t n = (uint32_t)idx < wc ? sh.cnt[idx] : 0u;
+        return n ? (uint64_t)n * fixed(key_value<D>(expand_key(cm - (uint32_t)idx))) : 0;
+    };
+    constexpr int kPer = kWinKeys / kNucThreads;
+    uint64_t total, need;
+    int last = kWinKeys - 1;  // the nucleus is taken among entries [0, last]
+    if (k_on) {
+        // The top-k threshold: the entry where the running count reaches
+        // top_k (the count of the tiny entry is its number of tiny values).
+        crossing(kWinKeys, (uint64_t)top_k, [&](int q) -> uint64_t { return sh.cnt[q]; }, sh);
+        const int dk = sh.digit;
+        if (dk < 0 || (uint32_t)dk == A)
+            return false;  // fewer than top_k values in the window, or tiny
+        last = dk;
+        uint64_t mine = 0;
+        for (int q = 0; q < kPer; ++q)
+            mine += tid * kPer + q <= last ? key_mass(tid * kPer + q) : 0ull;
+        total = block_sum(mine, sh);
+        if (!p_on) {
+            if (tid == 0)
+                *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)dk)),
+                                   (float)total / fscale);
+            return true;
+        }
+        need = mass_target(total, top_p);
+    } else {
+        uint64_t win = 0;
+        for (int q = 0; q < kPer; ++q)
+            win += key_mass(tid * kPer + q);
+        if (tid == 0 && A >= (uint32_t)kWinKeys)
+            win += tiny_total;  // the tiny entry lies beyond the window
+        total = block_sum(win + below, sh);
+        need = mass_target(total, top_p);
+    }
+    crossing(kWinKeys, need, [&](int q) -> uint64_t { return q <= last ? key_mass(q) : 0ull; },
+             sh);
+    const int d = sh.digit;
+    if (d < 0 || (uint32_t)d == A)
+        return false;  // among the tiny magnitudes or below the counted entries
+    if (tid == 0) {
+        const uint64_t kept = sh.above + key_mass(d);
+        *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)d)), (float)kept / fscale);
+    }
+    return true;
+}
+
+// One workgroup per row of every sampling sequence with a top-k or top-p
+// filter. Top-k keeps whole levels from the top until they hold at least
+// top_k tokens; the nucleus is the smallest run of keys from the top (of
+// what top-k kept) whose fixed-point mass reaches ceil(top_p * total).
+// Every mass is an integer sum, so the threshold and the kept mass do not
+// depend on how the row is split or visited.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
 {
@@ -875,8 +1155,13 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
     const int tid = threadIdx.x;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
-    const float top_p = p.top_p[b];
-    if (!valid_len(L, k) || !valid_temp(tau) || tau == 0.f || !(top_p > 0.f) || !(top_p < 1.f))
+    const float top_p = p.top_p ? p.top_p[b] : 1.f;
+    const int64_t top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
+    if (!valid_len(L, k) || !valid_temp(tau) || tau == 0.f || !(top_p > 0.f))
+        return;
+    const bool p_on = top_p < 1.f;
+    const bool k_on = top_k > 0 && top_k < (int64_t)p.V;
+    if (!p_on && !k_on)
         return;
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
@@ -898,207 +1183,33 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
             z += pp[c].y * exp2_fast((pp[c].x - m) * scale);
         sh.rs = m;
         // (x - m) * scale < tc: together at most V * 2^tc = (1 - top_p) z / 4
-        sh.tc = fmaxf(zlim, __log2f((1.f - top_p) * z / (float)p.V) - 2.f);
+        sh.tc = p_on ? fmaxf(zlim, __log2f((1.f - top_p) * z / (float)p.V) - 2.f) : zlim;
         sh.above = 0;
     }
     __syncthreads();
-    const float m = sh.rs;
-    auto fixed = [&](float x) {
-        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
-    };
+    const float m = sh.rs, tc = sh.tc;
     float2 *const out = p.nucleus + b * rows + slot;
 
     if constexpr (KB == 16) {
-        // One pass: every element with the same bf16 value has the same
-        // fixed-point mass, so counts per key near the top give the masses
-        // exactly. In raw bits r, with magnitude u = r & 0x7fff and
-        // d = max(u - kTinyBits + 1, 0), the window entry is A - d for a
-        // positive and A + d for a negative value, A being the entry of the
-        // tiny values (d = 0), all of it in 16-bit arithmetic: two elements
-        // per 32-bit word.
-        const uint32_t cm = compress_key(order_key<D>(m));
-        const uint32_t A = cm - kTinyIdx;
-        // Window entry of the lowest bf16 value at or below x (x rounded
-        // down to bf16).
-        auto entry_below = [&](float x) {
-            const uint32_t bx = __float_as_uint(x);
-            uint32_t r = bx >> 16;
-            if ((bx & 0xffffu) && (bx & 0x80000000u))
-                r += 1u;  // a truncated negative value: one step further down
-            return cm - compress_key((r & 0x8000u) ? (~r & 0xffffu) : (r | 0x8000u));
-        };
-        // Entries from iz on hold values below m + (zlim - 2) / scale: they
-        // weigh 0. Entries in [kWinKeys, iz) have mass but no counter.
-        const uint32_t iz =
-            __builtin_amdgcn_readfirstlane(entry_below(m + (zlim - 2.f) / scale) + 1u);
-        const bool wide = iz > (uint32_t)kWinKeys;
-        // Entries from wc on hold values with (x - m) * scale < tc. Together
-        // those weigh at most V * 2^tc = (1 - top_p) / 4 of the row, so the
-        // crossing lies above them; and each weighs below 2^31 in fixed
-        // point. They are not counted: their entries hold that weight
-        // instead, which each element adds to the total.
-        const float tc = fminf(sh.tc, (float)(30 - p.fix_bits));
-        const uint32_t wc = __builtin_amdgcn_readfirstlane(
-            min(entry_below(m + tc / scale) + 1u, (uint32_t)kWinKeys));
-        for (int q = tid; q <= kWinKeys; q += kNucThreads) {
-            uint32_t v = 0;
-            if ((uint32_t)q >= wc && q < kWinKeys && (uint32_t)q != A && (uint32_t)q <= cm)
-                v = (uint32_t)fixed(key_value<D>(expand_key(cm - (uint32_t)q)));
-            sh.cnt[q] = v;
-        }
-        __syncthreads();
-        unsigned long long below = 0, tiny = 0;
-        const u16x2 a2 = (u16x2)(unsigned short)A;
-        const u16x2 w2 = (u16x2)(unsigned short)kWinKeys;
-        const u16x2 wm2 = (u16x2)(unsigned short)(kWinKeys - 1);
-        const u16x2 tb2 = (u16x2)(unsigned short)kTinyBits;
-        const u16x2 tbm2 = (u16x2)(unsigned short)(kTinyBits - 1u);
-        // Tiny values and values beyond the window with mass: one by one
-        // (their entries, A and kWinKeys, hold 0).
-        auto rare = [&](uint32_t r, uint32_t idx) {
-            const bool is_tiny = (r & 0x7fffu) < kTinyBits;
-            const bool beyond = idx >= (uint32_t)kWinKeys && idx < iz;
-            const unsigned long long f = fixed(__uint_as_float(r << 16));
-            tiny += is_tiny ? f : 0ull;
-            below += !is_tiny && beyond ? f : 0ull;
-        };
-        auto visit_slot = [&](uint32_t slot) {
-            const uint32_t v = sh.cnt[slot];
-            if (slot < wc)
-                atomicAdd(&sh.cnt[slot], 1u);
-            below += slot < wc ? 0u : v;
-        };
-        // Eight elements (one 16-byte load): all window reads are issued
-        // before the counts and the sums, so one wait covers them.
-        auto visit_group = [&](const u32x4 &g) {
-            const uint32_t w[4] = {g.x, g.y, g.z, g.w};
-            uint32_t idx[4], slot[8];
-            bool any_rare = false;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u16x2 u = as_u16x2(w[j] & 0x7fff7fffu);
-                const u16x2 d = __builtin_bit_cast(
-                    u16x2,
-                    __builtin_elementwise_max(__builtin_bit_cast(i16x2, u - tbm2), (i16x2)0));
-                const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
-                idx[j] = (as_u32(a2 + d) & neg) | (as_u32(a2 - d) & ~neg);
-                const uint32_t s2 = as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), w2));
-                slot[2 * j] = s2 & 0xffffu;
-                slot[2 * j + 1] = s2 >> 16;
-                const bool has_tiny = as_u32(__builtin_elementwise_min(u, tb2)) != as_u32(tb2);
-                const bool has_beyond =
-                    as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), wm2)) != idx[j];
-                any_rare |= has_tiny || (wide && has_beyond);
-            }
-            uint32_t v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = sh.cnt[slot[j]];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (slot[j] < wc)
-                    atomicAdd(&sh.cnt[slot[j]], 1u);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                below += slot[j] < wc ? 0u : v[j];
-            if (any_rare) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    rare(w[j] & 0xffffu, idx[j] & 0xffffu);
-                    rare(w[j] >> 16, idx[j] >> 16);
-                }
-            }
-        };
-        {
-            const Span sp = make_span<D>(row, 0, p.V);
-            const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
-            for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kNucTiles) {
-                u32x4 r[kNucTiles];
-#pragma unroll
-                for (int u = 0; u < kNucTiles; ++u) {
-                    const int64_t vi = base + u * kNucThreads + tid;
-                    r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int u = 0; u < kNucTiles; ++u)
-                    if (base + u * kNucThreads + tid < sp.ngroups)
-                        visit_group(r[u]);
-            }
-            auto visit_one = [&](uint32_t r) {
-                const uint32_t u = r & 0x7fffu;
-                const uint32_t d = u < kTinyBits ? 0u : u - (kTinyBits - 1u);
-                const uint32_t idx = ((r & 0x8000u) ? A + d : A - d) & 0xffffu;
-                visit_slot(min(idx, (uint32_t)kWinKeys));
-                rare(r, idx);
-            };
-            if (sp.s + tid < sp.a)
-                visit_one((uint32_t)row[sp.s + tid]);
-            if (sp.z + tid < sp.e)
-                visit_one((uint32_t)row[sp.z + tid]);
-        }
-        const uint64_t tiny_total = block_sum(tiny, sh);
-        auto key_mass = [&](int idx) -> uint64_t {
-            if ((uint32_t)idx == A)
-                return tiny_total;
-            const uint32_t n = (uint32_t)idx < wc ? sh.cnt[idx] : 0u;
-            return n ? (uint64_t)n * fixed(key_value<D>(expand_key(cm - (uint32_t)idx))) : 0;
-        };
-        uint64_t win = 0;
-        for (int q = 0; q < kWinKeys / kNucThreads; ++q)
-            win += key_mass(tid * (kWinKeys / kNucThreads) + q);
-        if (tid == 0 && A >= (uint32_t)kWinKeys)
-            win += tiny_total;  // the tiny entry lies beyond the window
-        const uint64_t total = block_sum(win + below, sh);
-        crossing(kWinKeys, mass_target(total, top_p), key_mass, sh);
-        const int d = sh.digit;
-        if (d >= 0 && (uint32_t)d != A) {
-            if (tid == 0) {
-                const uint64_t kept = sh.above + key_mass(d);
-                *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)d)),
-                                   (float)kept / fscale);
-            }
+        if (window_select<D>(row, p.V, m, scale, p.fix_bits, zlim, tc, k_on, top_k, p_on, top_p,
+                             out, sh))
+            return;
+        __syncthreads();  // the radix passes reuse the shared memory
+    }
+    uint32_t lo = 0;
+    if (k_on) {
+        const Selection sk = radix_select<D, true>(row, p.V, m, scale, fscale, zlim, 0u, top_k,
+                                                   top_p, sh);
+        if (!p_on) {
+            if (tid == 0)
+                *out = make_float2(key_value<D>(sk.key), (float)sk.kept / fscale);
             return;
         }
-        // The crossing lies among the tiny magnitudes or below the counted
-        // entries: radix passes.
-        __syncthreads();
+        lo = sk.key;
     }
-
-    // Radix passes: kDigitBits of the key at a time, from the top.
-    uint64_t target = 0, above = 0;
-    uint32_t prefix = 0;
-    int done = 0;
-    while (done < KB) {
-        const int w = min(kDigitBits, KB - done);
-        const int nb = 1 << w;
-        for (int q = tid; q < nb; q += kNucThreads)
-            sh.hist[q] = 0;
-        __syncthreads();
-        unsigned long long mine = 0;
-        for_each_logit<D>(row, p.V, [&](float x) {
-            if ((x - m) * scale < zlim)
-                return;
-            const uint32_t key = order_key<D>(x);
-            if (done == 0 || (key >> (KB - done)) == prefix) {
-                const unsigned long long wf = fixed(x);
-                atomicAdd(&sh.hist[(key >> (KB - done - w)) & (uint32_t)(nb - 1)], wf);
-                mine += wf;
-            }
-        });
-        if (done == 0)  // the row's total mass sets the target
-            target = mass_target(block_sum(mine, sh), top_p);
-        __syncthreads();
-        crossing(nb, target - above, [&](int q) -> uint64_t { return sh.hist[nb - 1 - q]; }, sh);
-        const int d = nb - 1 - sh.digit;  // the crossing always exists here
-        above += sh.above;
-        prefix = (prefix << w) | (uint32_t)d;
-        done += w;
-        if (done == KB && tid == 0) {
-            const uint64_t kept = above + sh.hist[d];
-            *out = make_float2(key_value<D>(prefix), (float)kept / fscale);
-        }
-        __syncthreads();  // sh.hist is cleared next pass
-    }
+    const Selection sp = radix_select<D, false>(row, p.V, m, scale, fscale, zlim, lo, 0, top_p, sh);
+    if (tid == 0)
+        *out = make_float2(key_value<D>(sp.key), (float)sp.kept / fscale);
 }
 
 // ===========================================================================
@@ -1563,6 +1674,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         p.segs = reinterpret_cast<double *>(ws + lay.segs) + b0 * nc * 2 * kSegs;
         p.nucleus = reinterpret_cast<float2 *>(ws + lay.nucleus) + b0 * rows;
         if (p.top_p) p.top_p += b0;
+        if (p.top_k) p.top_k += b0;
         // Early-exit lists and counters are per slice (indexed by the
         // slice's own B), so each slice uses the arrays from their start.
         p.ee_count = reinterpret_cast<int32_t *>(ws + lay.ee_count);
@@ -1589,7 +1701,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                                stream, p);
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
-            if (p.top_p)
+            if (p.top_p || p.top_k)
                 hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads), 0,
                                    stream, p);
             if (nb * nc <= kFoldDecisionItems)
@@ -1624,7 +1736,8 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
 
 int verify_entry(const void *target_logits, const void *draft_logits, int32_t dtype,
                  const int32_t *draft_tokens, const int32_t *draft_len, const float *temperature,
-                 const float *top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                 const int32_t *top_k, const float *top_p, int32_t B, int32_t k, int32_t V,
+                 uint64_t seed,
                  uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
                  const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
                  void *stream, bool early_exit)
@@ -1642,7 +1755,7 @@ int verify_entry(const void *target_logits, const void *draft_logits, int32_t dt
     if (!aligned(target_logits, esz) || (draft_logits && !aligned(draft_logits, esz)) ||
         !aligned(temperature, 4) || !aligned(out_tokens, 4) || !aligned(num_accepted, 4) ||
         (draft_tokens && !aligned(draft_tokens, 4)) || (draft_len && !aligned(draft_len, 4)) ||
-        !aligned(top_p, 4))
+        !aligned(top_p, 4) || !aligned(top_k, 4))
         return SPEC_EINVAL;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
         return SPEC_EWORKSPACE;
@@ -1662,6 +1775,7 @@ int verify_entry(const void *target_logits, const void *draft_logits, int32_t dt
     p.out_tokens = out_tokens;
     p.num_accepted = num_accepted;
     p.top_p = top_p;
+    p.top_k = top_k;
     {
         // fixed-point masses of a row: V elements of at most 2^F each must
         // sum below 2^62
@@ -1696,8 +1810,8 @@ extern "C" int spec_verify(const void *target_logits, const void *draft_logits, 
                            size_t workspace_bytes, void *stream)
 {
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
-                        nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
-                        workspace_bytes, stream, false);
+                        nullptr, nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux,
+                        workspace, workspace_bytes, stream, false);
 }
 
 extern "C" int spec_verify_top_p(const void *target_logits, const void *draft_logits,
@@ -1711,8 +1825,24 @@ extern "C" int spec_verify_top_p(const void *target_logits, const void *draft_lo
     if (!top_p && B > 0)
         return SPEC_EINVAL;
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
-                        top_p, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
-                        workspace_bytes, stream, false);
+                        nullptr, top_p, B, k, V, seed, seq_base, out_tokens, num_accepted, aux,
+                        workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int spec_verify_top_k_top_p(const void *target_logits, const void *draft_logits,
+                                       int32_t dtype, const int32_t *draft_tokens,
+                                       const int32_t *draft_len, const float *temperature,
+                                       const int32_t *top_k, const float *top_p, int32_t B,
+                                       int32_t k, int32_t V, uint64_t seed, uint32_t seq_base,
+                                       int32_t *out_tokens, int32_t *num_accepted,
+                                       const spec_verify_aux_t *aux, void *workspace,
+                                       size_t workspace_bytes, void *stream)
+{
+    if (!top_k && !top_p && B > 0)
+        return SPEC_EINVAL;
+    return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
+                        top_k, top_p, B, k, V, seed, seq_base, out_tokens, num_accepted, aux,
+                        workspace, workspace_bytes, stream, false);
 }
 
 extern "C" int spec_verify_early_exit(const void *target_logits, const void *draft_logits,
@@ -1724,8 +1854,8 @@ extern "C" int spec_verify_early_exit(const void *target_logits, const void *dra
                                       void *workspace, size_t workspace_bytes, void *stream)
 {
     return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
-                        nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux, workspace,
-                        workspace_bytes, stream, true);
+                        nullptr, nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux,
+                        workspace, workspace_bytes, stream, true);
 }
 
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int32_t dtype)

@@ -129,6 +129,16 @@ def test_other_entry_points_reject_bad_arguments_before_any_launch(lib):
                                ctypes.c_uint64(0), ctypes.c_uint32(0), 0x5000, 0x6000, None, None,
                                1 << 20, None)
     assert rc == 2  # valid arguments, no workspace
+    # spec_verify_top_k_top_p: at least one filter; a misaligned top_k
+    def topk(tk, tp):
+        return lib.spec_verify_top_k_top_p(0x1000, 0x2000, 0, 0x3000, None, 0x4000, tk, tp, 2, 2,
+                                           64, ctypes.c_uint64(0), ctypes.c_uint32(0), 0x5000,
+                                           0x6000, None, None, 1 << 20, None)
+    assert topk(None, None) == 1
+    assert topk(0x7002, None) == 1
+    assert topk(0x7000, None) == 2  # valid arguments, no workspace
+    assert topk(None, 0x7000) == 2
+    assert topk(0x7000, 0x8000) == 2
     # spec_verify_tree: sizes, pointers, workspace
     def tree(**kw):
         a = dict(target=0x1000, dtype=1, par=0x2000, tok=0x3000, nn=0x4000, B=2, N=8, V=64,
