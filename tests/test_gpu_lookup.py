@@ -41,11 +41,13 @@ def test_lookup_parity_workloads(name):
     assert_same(g, r, name)
 
 
-@pytest.mark.parametrize("n_min,n_max,k", [(1, 1, 1), (1, 3, 5), (2, 4, 7), (3, 16, 63),
-                                           (1, 16, 0), (16, 16, 4)])
-def test_lookup_random_small_contexts(n_min, n_max, k):
+@pytest.mark.parametrize("n_min,n_max,k,T_max", [(1, 1, 1, 700), (1, 3, 5, 700), (2, 4, 7, 701),
+                                                 (3, 16, 63, 703), (1, 16, 0, 702),
+                                                 (16, 16, 4, 700)])
+def test_lookup_random_small_contexts(n_min, n_max, k, T_max):
+    """Odd T_max: rows start at every 4-byte alignment."""
     rng = np.random.default_rng(100 * n_min + n_max + k)
-    B, T_max = 300, 700
+    B = 300
     ctx = rng.integers(0, int(rng.integers(1, 5)), size=(B, T_max)).astype(np.int32)
     for b in range(0, B, 3):  # some rows with a larger alphabet
         ctx[b] = rng.integers(0, 1000, size=T_max)
