@@ -1,0 +1,85 @@
+"""GPU parity over a seeded sweep of shapes, and agreement of the two ways
+the decisions are launched.
+
+The sweep draws small batches across the dimensions the kernels branch on:
+vocabularies on both sides of the 32 KiB chunk (16384 bf16 / 8192 fp32
+logits) and of one or several chunks, every draft length from 0 to k, k up
+to the maximum, greedy and sampling sequences in one batch, and the top-k /
+top-p filters. Every case is compared with the oracle at the usual
+tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+import speculative_decoding_verification_11_amd as sv  # noqa: E402
+from oracle import parity  # noqa: E402
+from test_gpu_parity import (DEV, _mixed_batch, batch_to, check, host, run_gpu,  # noqa: E402
+                             say)
+from test_gpu_top_k import run_tk  # noqa: E402
+
+SWEEP_V = {"bf16": (1, 2, 255, 16383, 16384, 16385, 32768, 40000),
+           "f32": (1, 3, 8191, 8192, 8193, 16385, 24577)}
+
+
+def _case(i):
+    rng = np.random.default_rng(9000 + i)
+    dtype = ("bf16", "f32")[i % 2]
+    V = int(rng.choice(SWEEP_V[dtype]))
+    k = int(rng.choice([0, 1, 2, 5, 8, 13, sv.MAX_K]))
+    B = int(rng.integers(1, 12 if k < 20 else 4))
+    taus = tuple(rng.choice([0.0, 0.3, 0.8, 1.0, 2.5], size=3))
+    return rng, dtype, V, k, B, taus
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_shape_sweep(i):
+    rng, dtype, V, k, B, taus = _case(i)
+    cb = _mixed_batch(rng, B, k, V, dtype, taus=taus)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    seed = int(rng.integers(0, 2**63))
+    filtered = i % 3 == 2 and V > 1
+    say(f"[case] sweep {i}: B={B} k={k} V={V} {dtype} taus={taus} filtered={filtered}")
+    if filtered:
+        top_k = rng.integers(0, V + 1, size=B).astype(np.int32)
+        top_p = rng.choice([0.3, 0.8, 0.95, 1.0], size=B).astype(np.float32)
+        g = run_tk(gb, seed, top_k, top_p)
+        r = parity.oracle_on(h, seed, top_k=top_k, top_p=top_p)
+    else:
+        g = run_gpu(gb, seed)
+        r = parity.oracle_on(h, seed)
+    check(parity.compare(g, r, h["draft_len"], h["temperature"], k), f"sweep {i}")
+
+
+def test_decision_in_draw_and_separate_launch_agree():
+    """Up to 4096 draw workgroups the decisions are taken inside the draw
+    kernel; above, by their own launch. One vocabulary chunk per row puts
+    B = 4096 and B = 4097 on either side; the shared sequences must come out
+    identical (each sequence draws from its own Philox counters)."""
+    rng = np.random.default_rng(77)
+    B, k, V = 4097, 3, 1000
+    cb = _mixed_batch(rng, B, k, V, "bf16", taus=(0.0, 0.7, 1.0, 1.3))
+    gb = batch_to(cb, DEV)
+    seed = 0x5EED
+    big = run_gpu(gb, seed)
+    small_batch = batch_to(_slice(cb, 4096), DEV)
+    small = run_gpu(small_batch, seed)
+    for key in small:
+        assert np.array_equal(small[key], big[key][:4096], equal_nan=True), key
+    h = host(cb)
+    rows = list(range(0, B, 97)) + [B - 1]
+    r = parity.oracle_on(h, seed, seqs=rows)
+    check(parity.compare(big, r, h["draft_len"], h["temperature"], k, rows=rows),
+          "decision launch")
+
+
+def _slice(cb, n):
+    from speculative_decoding_verification_11_amd import workloads as wl
+
+    return wl.Batch(cb.workload, cb.target[:n].contiguous(), cb.draft[:n].contiguous(),
+                    cb.draft_tokens[:n].contiguous(), cb.draft_len[:n].contiguous(),
+                    cb.temperature[:n].contiguous())
