@@ -86,6 +86,23 @@ def read_counter_traffic(workload: str):
         return None
 
 
+def read_kernel_traffic(*kernels: str):
+    """Scaled HBM bytes (read + written) per dispatch of the named kernels
+    from the same committed counter summary (taken with bench.py's default
+    workloads), if it was taken on the current kernel source; else None."""
+    if read_counter_traffic("c5") is None:
+        return None
+    out = {}
+    for line in open(PROFILE_COUNTERS):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0] in kernels:
+            try:
+                out[cells[0]] = int(float(cells[3]) + float(cells[4]))
+            except ValueError:
+                pass
+    return out or None
+
+
 def copy_probe(nbytes: int, reps: int = 5) -> None:
     import torch
 
@@ -190,7 +207,8 @@ def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
            "row_kernel_us_mean": row_mean * 1e3,
            "row_kernel_GBps": nbytes / (row_mean * 1e-3) / 1e9,
            "mean_accepted_depth": float(out[2].float().mean()),
-           "roofline": roof(nbytes / (row_mean * 1e-3) / 1e9, "k_tree_rowstats, HIP events")}
+           "roofline": roof(nbytes / (row_mean * 1e-3) / 1e9, "k_tree_rowstats, HIP events"),
+           "hbm_bytes_per_dispatch": read_kernel_traffic("k_tree_rowstats", "k_tree_decide")}
     if cpu:
         import oracle
 
@@ -244,7 +262,8 @@ def bench_lookup(K: int, W: int, cpu: bool) -> dict:
            "context_bytes": nbytes, "kernel": "k_prompt_lookup", "kernel_us_mean": k_ms * 1e3,
            "kernel_GBps": nbytes / (k_ms * 1e-3) / 1e9,
            "mean_draft_len": float(out[1].float().mean()),
-           "roofline": roof(nbytes / (k_ms * 1e-3) / 1e9, "k_prompt_lookup, torch events")}
+           "roofline": roof(nbytes / (k_ms * 1e-3) / 1e9, "k_prompt_lookup, torch events"),
+           "hbm_bytes_per_dispatch": read_kernel_traffic("k_prompt_lookup")}
     if cpu:
         import oracle
 
@@ -408,6 +427,8 @@ def main() -> int:
             "roofline": roof(ee_bytes / (loop_mean * 1e-3) / 1e9,
                              "the position loop (rows up to each stop, read once), HIP events"),
             "cpu_baseline": "the oracle of the top-level cpu_baseline (identical outputs)",
+            "hbm_bytes_per_dispatch": read_kernel_traffic("k_ee_rowstats0", "k_ee_rowstats",
+                                                          "k_ee_tail", "k_draw"),
         }
         log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
             f"for {ee_bytes / 1e9:.3f} GB")
@@ -436,7 +457,9 @@ def main() -> int:
                 "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
                 "roofline": roof(alg_bytes / (tp_ms * 1e-3) / 1e9,
                                  "the whole step (each row counted once; k_nucleus reads every "
-                                 "bf16 row once more)")}
+                                 "bf16 row once more)"),
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_rowstats", "k_nucleus",
+                                                              "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
@@ -477,7 +500,9 @@ def main() -> int:
                 "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
                 "roofline": roof(alg_bytes / (tk_ms * 1e-3) / 1e9,
                                  "the whole step (each row counted once; k_nucleus reads every "
-                                 "bf16 row once more)")}
+                                 "bf16 row once more)"),
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_rowstats", "k_nucleus",
+                                                              "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
