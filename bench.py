@@ -116,23 +116,49 @@ def copy_probe(nbytes: int, reps: int = 5) -> None:
     print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(batch, seed: int, nseq: int) -> dict:
+    """The oracle on the host cores: all of the batch (up to nseq sequences)
+    on up to 16 threads, and a 64-sequence slice on one thread; each the
+    median of three runs."""
     import oracle
     from oracle import parity
     from speculative_decoding_verification_11_amd import workloads as wl
 
     nthreads = parity.host_threads(cap=16)
+
+    def median_time(host, nt):
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.spec_verify_ref(host["target"], host["draft"], host["draft_tokens"],
+                                   host["draft_len"], host["temperature"], seed, seq_base=0,
+                                   nthreads=nt)
+            times.append(time.perf_counter() - t0)
+        return sorted(times)[1]
+
     sample = batch.select(range(min(nseq, batch.B)))
-    host = wl.to_host_arrays(sample)
-    t0 = time.perf_counter()
-    oracle.spec_verify_ref(host["target"], host["draft"], host["draft_tokens"], host["draft_len"],
-                           host["temperature"], seed, seq_base=0, nthreads=nthreads)
-    dt = time.perf_counter() - t0
+    dt = median_time(wl.to_host_arrays(sample), nthreads)
     positions = sample.B * (sample.k + 1)
+    one = batch.select(range(min(64, batch.B)))
+    dt1 = median_time(wl.to_host_arrays(one), 1)
     return {"value": positions / dt, "unit": "positions/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {sample.B} of {batch.B} sequences of the same batch "
                       f"({positions} positions), fp64 C oracle, {nthreads} threads, "
-                      f"{dt:.2f} s wall"}
+                      f"median of 3: {dt:.2f} s wall",
+            "value_1_thread": one.B * (one.k + 1) / dt1,
+            "sample_1_thread": f"first {one.B} sequences, one thread, median of 3: "
+                               f"{dt1:.2f} s wall",
+            "cpu_model": cpu_model()}
 
 
 def roof(achieved_gbps: float, what: str) -> dict:
