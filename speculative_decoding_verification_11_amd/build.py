@@ -14,10 +14,12 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-# verify.hip: spec_verify, spec_verify_top_p, spec_verify_early_exit;
-# tree.hip: spec_verify_tree; lookup.hip: spec_prompt_lookup (common.h is
-# their shared device header).
-SRCS = [os.path.join(CSRC, f) for f in ("verify.hip", "tree.hip", "lookup.hip")]
+# verify.hip: spec_verify, spec_verify_top_p, spec_verify_top_k_top_p,
+# spec_verify_early_exit (their kernels also in nucleus.hip and
+# early_exit.hip, sharing verify.h); tree.hip: spec_verify_tree; lookup.hip:
+# spec_prompt_lookup (common.h is the shared device header of all).
+SRCS = [os.path.join(CSRC, f)
+        for f in ("verify.hip", "nucleus.hip", "early_exit.hip", "tree.hip", "lookup.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "_build", "libspecverify.so")
 ARCH = "gfx950"

@@ -4,8 +4,9 @@
 // wave reductions, Philox4x32-10, input checks, and the row-statistics
 // chunk pass that every verification streams its logit rows through.
 //
-// Internal header: included by verify.hip, tree.hip and lookup.hip, each of
-// which gets its own copy of these inline functions and templates.
+// Internal header: included by every source of the library. Its names live
+// in namespace spv, so that the kernels of one source can be instantiated
+// on these types and launched from another.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +18,7 @@
 
 #include "spec_verify.h"
 
-namespace {
+namespace spv {
 
 constexpr int kThreads = 256;       // 4 waves of 64 lanes
 constexpr int kWave = 64;
@@ -374,4 +375,4 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
     return out;
 }
 
-}  // namespace
+}  // namespace spv

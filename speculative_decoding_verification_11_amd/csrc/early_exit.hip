@@ -1,0 +1,338 @@
+// early_exit.hip -- the early-exit schedule of the verification step on
+// MI355X (gfx950): positions taken one at a time for the whole batch, so
+// that rows after a sequence's first rejection are never read (kernels
+// launched from verify.hip).
+#include "verify.h"
+
+namespace spv {
+
+// ===========================================================================
+// Early-exit schedule. Rows after a sequence's first rejection never
+// influence its outputs, so positions can be taken one at a time for the
+// whole batch, each reading only the rows of the sequences still accepting.
+// Decisions, draws and RNG are those of the full step; the diagnostics of
+// rows that are never read (p_g, q_g, argmax past the stop) stay NaN / -1.
+//
+// Position 0 has its own decision launch (which also validates the inputs
+// and clears the counters). From position 1 on, the workgroup that finishes
+// the last chunk of a sequence's rows at position i takes that sequence's
+// decision at once, and a sequence that accepts is appended to the list of
+// position i + 1, so each position's launch only streams listed sequences.
+// ===========================================================================
+
+// Exchange of partials inside one launch: device-scope (write-through)
+// stores and loads, and a writer drains its stores (s_waitcnt) before the
+// relaxed device-scope count that tells the last workgroup to read them.
+// Agent-scope release/acquire would write back / invalidate the whole L2 of
+// the workgroup's XCD each time instead.
+__device__ inline void publish_float2(float2 *ptr, float2 v)
+{
+    const uint64_t bits = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(ptr), bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float2 fetch_float2(const float2 *ptr)
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(ptr), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ inline void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ inline int counter_add(int32_t *ptr, int32_t v)
+{
+    return __hip_atomic_fetch_add(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Row-statistics chunks of sequence b at position i.
+__device__ inline int ee_items(int nc, bool greedy, int i, int L)
+{
+    return nc * (1 + (!greedy && i < L ? 1 : 0));
+}
+
+// Outputs of a sequence that stops at position j (one thread). The first
+// pq_set entries of p_g / q_g and the first am_set of argmax were written
+// position by position; the rest become NaN / -1. A draw's token is left
+// to k_locate.
+__device__ inline void ee_stop(const Params &p, int64_t b, int j, int status,
+                               const Decision &dec, bool token_here, int token, int pq_set,
+                               int am_set)
+{
+    const int k = p.k;
+    int32_t *out = p.out_tokens + b * (k + 1);
+    const bool ok = status == SPEC_SEQ_OK;
+    for (int x = 0; x <= k; ++x) {
+        if (!ok || x > j)
+            out[x] = -1;
+        else if (x < j)
+            out[x] = p.draft_tokens[b * k + x];
+        else if (token_here)
+            out[x] = token;
+    }
+    p.num_accepted[b] = ok ? j : 0;
+    const AuxDev &aux = p.aux;
+    for (int x = ok ? pq_set : 0; x < k; ++x) {
+        if (aux.p_g) aux.p_g[b * k + x] = NAN;
+        if (aux.q_g) aux.q_g[b * k + x] = NAN;
+    }
+    if (aux.argmax)
+        for (int x = ok ? am_set : 0; x <= k; ++x)
+            aux.argmax[b * (k + 1) + x] = -1;
+    if (aux.seq_status) aux.seq_status[b] = status;
+    if (aux.draw_row) aux.draw_row[b] = ok ? j : -1;
+    if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS) {
+        if (aux.draw_kind) aux.draw_kind[b] = dec.kind;
+        if (aux.resid_mass) aux.resid_mass[b] = NAN;
+    }
+    p.decisions[b] = dec;
+}
+
+// Decision of sequence b at position i (one thread): the same folds (chunk
+// order), gathers, Philox draws and tests as the full step's decision, for
+// one position. Returns true when the sequence accepts g_i and goes on to
+// position i + 1. `published`: the partials were written in this launch.
+template <class D>
+__device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float tau,
+                                 bool published)
+{
+    using E = typename D::Elem;
+    const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
+    Decision dec = no_decision();
+    auto partial = [&](const float2 *q) { return published ? fetch_float2(q) : *q; };
+
+    const E *target = static_cast<const E *>(p.target);
+    const E *draft = static_cast<const E *>(p.draft);
+    const float2 *pt = p.partials + (b * rows + i) * (int64_t)nc;
+    const int g = i < L ? p.draft_tokens[b * k + i] : -1;
+    if (tau == 0.f) {
+        ArgMax acc{-INFINITY, INT32_MAX};
+        for (int c = 0; c < nc; ++c) {
+            const float2 t = partial(pt + c);
+            acc = argmax_merge(acc, ArgMax{t.x, __float_as_int(t.y)});
+        }
+        if (p.aux.argmax) p.aux.argmax[b * (k + 1) + i] = acc.i;
+        if (i < L && acc.i == g)
+            return true;
+        dec.row = i;
+        dec.kind = SPEC_DRAW_GREEDY;
+        ee_stop(p, b, i, SPEC_SEQ_OK, dec, true, acc.i, 0, i + 1);
+        return false;
+    }
+    const float scale = temp_scale(tau);
+    Soft ts{-INFINITY, 0.f}, ds{-INFINITY, 0.f};
+    for (int c = 0; c < nc; ++c) {
+        const float2 t = partial(pt + c);
+        ts = soft_merge(ts, Soft{t.x, t.y}, scale);
+    }
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)i, p.seq_base + (uint32_t)b, 0u, 0u),
+                                  p.key0, p.key1);
+    const float u = uniform24(w.x), v = uniform24(w.y);
+    if (i < L) {
+        const float2 *pd = p.partials + (b * rows + k + 1 + i) * (int64_t)nc;
+        for (int c = 0; c < nc; ++c) {
+            const float2 t = partial(pd + c);
+            ds = soft_merge(ds, Soft{t.x, t.y}, scale);
+        }
+        const float xt = D::at(target + (b * (k + 1) + i) * (int64_t)V, g);
+        const float xd = D::at(draft + (b * k + i) * (int64_t)V, g);
+        const float pg = exp2_fast((xt - ts.m) * scale) / ts.z;
+        const float qg = exp2_fast((xd - ds.m) * scale) / ds.z;
+        if (!(qg > 0.f)) {
+            ee_stop(p, b, i, SPEC_SEQ_QZERO, dec, false, 0, 0, 0);
+            return false;
+        }
+        if (p.aux.p_g) p.aux.p_g[b * k + i] = pg;
+        if (p.aux.q_g) p.aux.q_g[b * k + i] = qg;
+        if (u < fminf(1.f, pg / qg))
+            return true;
+    }
+    dec.row = i;
+    dec.kind = i < L ? SPEC_DRAW_RESIDUAL : SPEC_DRAW_BONUS;
+    dec.v = v;
+    dec.scale = scale;
+    dec.mt = ts.m;
+    dec.zt = ts.z;
+    dec.md = ds.m;
+    dec.zd = ds.z;
+    ee_stop(p, b, i, SPEC_SEQ_OK, dec, false, 0, i < L ? i + 1 : L, 0);
+    return false;
+}
+
+// Streams one chunk of target row i (slot 0) or draft row i (slot 1) of
+// sequence b; thread 0 returns the partial.
+template <class D>
+__device__ __forceinline__ float2 ee_chunk(const Params &p, int64_t b, int slot, int c, int i,
+                                           float tau, RowShared &sh)
+{
+    using E = typename D::Elem;
+    constexpr int64_t CH = chunk_elems<D>();
+    const int k = p.k;
+    const bool greedy = tau == 0.f;
+    const E *row = slot == 0 ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
+                             : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
+    const int64_t s = (int64_t)c * CH;
+    return chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy,
+                          greedy ? 0.f : temp_scale(tau), sh);
+}
+
+// Position 0: every sequence with a valid length and temperature.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
+{
+    __shared__ RowShared sh;
+    const int64_t item = blockIdx.x;
+    const int k = p.k, nc = p.nc, rows = 2 * k + 1;
+    if (item == 0 && threadIdx.x == 0)
+        p.ee_count[1] = 0;  // position 1's list, filled by k_ee_decide0
+    const int c = (int)(item % nc);
+    const int64_t rs = item / nc;
+    const int slot = (int)(rs % 2);
+    const int64_t b = rs / 2;
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    if (!(valid_len(L, k) && valid_temp(tau)))
+        return;
+    if (slot == 1 && (tau == 0.f || L == 0))
+        return;
+    const float2 part = ee_chunk<D>(p, b, slot, c, 0, tau, sh);
+    if (threadIdx.x == 0)
+        p.partials[(b * rows + (slot == 0 ? 0 : k + 1)) * (int64_t)nc + c] = part;
+}
+
+// Appends b to position i's list (one atomic per wave).
+__device__ inline void ee_enlist(const Params &p, int64_t b, int i, bool go)
+{
+    const uint64_t mask = __ballot(go);
+    if (!mask)
+        return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int leader = __ffsll((unsigned long long)mask) - 1;
+    int base = 0;
+    if (lane == leader)
+        base = counter_add(p.ee_count + i, __popcll(mask));
+    base = __shfl(base, leader, kWave);
+    if (go) {
+        const int rank = __popcll(mask & ((1ull << lane) - 1));
+        p.ee_list[(int64_t)i * p.B + base + rank] = (int32_t)b;
+    }
+}
+
+// Position 0's decisions, one thread per sequence; also validates the
+// inputs and clears the counters of the later positions.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p)
+{
+    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const bool in = b < p.B;
+    const int k = p.k, V = p.V;
+    if (blockIdx.x == 0 && threadIdx.x > 1 && threadIdx.x <= k + 1)
+        p.ee_count[threadIdx.x] = 0;  // positions 2..k (and k + 1, never read)
+    bool go = false;
+    if (in) {
+        for (int i = 1; i <= k; ++i)
+            p.ee_done[(int64_t)i * p.B + b] = 0;
+        const int L = p.draft_len ? p.draft_len[b] : k;
+        const float tau = p.temperature[b];
+        int status = SPEC_SEQ_OK;
+        if (!valid_len(L, k)) {
+            status = SPEC_SEQ_BAD_LEN;
+        } else if (!valid_temp(tau)) {
+            status = SPEC_SEQ_BAD_TEMP;
+        } else {
+            for (int x = 0; x < L; ++x) {
+                const int g = p.draft_tokens[b * k + x];
+                if (g < 0 || g >= V)
+                    status = SPEC_SEQ_BAD_TOKEN;
+            }
+        }
+        if (status != SPEC_SEQ_OK) {
+            const Decision dec = no_decision();
+            ee_stop(p, b, 0, status, dec, false, 0, 0, 0);
+        } else {
+            go = ee_decide<D>(p, b, 0, L, tau, false);
+        }
+    }
+    ee_enlist(p, b, 1, go);
+}
+
+// Position i >= 1: the sequences on position i's list. The workgroup that
+// completes a sequence's chunks decides it and lists it for i + 1.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
+{
+    __shared__ RowShared sh;
+    const int64_t item = blockIdx.x;
+    const int k = p.k, nc = p.nc, rows = 2 * k + 1;
+    const int64_t j = item / (2 * nc);
+    if (j >= p.ee_count[i])
+        return;
+    const int slot = (int)((item / nc) % 2);
+    const int c = (int)(item % nc);
+    const int64_t b = p.ee_list[(int64_t)i * p.B + j];
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    if (slot == 1 && (tau == 0.f || i >= L))
+        return;
+    const float2 part = ee_chunk<D>(p, b, slot, c, i, tau, sh);
+    if (threadIdx.x != 0)
+        return;
+    publish_float2(p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc + c, part);
+    drain_stores();  // the partial is visible before the count
+    const int items = ee_items(nc, tau == 0.f, i, L);
+    if (counter_add(p.ee_done + (int64_t)i * p.B + b, 1) != items - 1)
+        return;
+    if (ee_decide<D>(p, b, i, L, tau, true) && i < k) {
+        const int at = counter_add(p.ee_count + i + 1, 1);
+        p.ee_list[(int64_t)(i + 1) * p.B + at] = (int32_t)b;
+    }
+}
+
+// Positions P..k in one launch: every remaining row (target rows P..L,
+// draft rows P..L-1) of the sequences on position P's list. Once few
+// sequences are left, a launch per position costs more than reading the
+// rows after a stop that will never be used. The workgroup that completes
+// a sequence's chunks decides its positions P, P+1, ... up to the stop.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
+{
+    __shared__ RowShared sh;
+    const int64_t item = blockIdx.x;
+    const int k = p.k, nc = p.nc, rows = 2 * k + 1;
+    const int nt = k - P + 1, R = 2 * nt - 1;  // target rows P..k, draft rows P..k-1
+    const int64_t j = item / ((int64_t)R * nc);
+    if (j >= p.ee_count[P])
+        return;
+    const int rest = (int)(item % ((int64_t)R * nc));
+    const int slot = rest / nc, c = rest % nc;
+    const int64_t b = p.ee_list[(int64_t)P * p.B + j];
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    const bool greedy = tau == 0.f;
+    const bool is_target = slot < nt;
+    const int i = is_target ? P + slot : P + slot - nt;
+    if (is_target ? i > L : (greedy || i >= L))
+        return;
+    const float2 part = ee_chunk<D>(p, b, is_target ? 0 : 1, c, i, tau, sh);
+    if (threadIdx.x != 0)
+        return;
+    publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c, part);
+    drain_stores();  // the partial is visible before the count
+    int items = 0;
+    for (int x = P; x <= L; ++x)
+        items += ee_items(nc, greedy, x, L);
+    if (counter_add(p.ee_done + (int64_t)P * p.B + b, 1) != items - 1)
+        return;
+    for (int x = P; x <= L; ++x)
+        if (!ee_decide<D>(p, b, x, L, tau, true))
+            break;
+}
+
+template __global__ void k_ee_rowstats0<F32>(Params p);
+template __global__ void k_ee_rowstats0<BF16>(Params p);
+template __global__ void k_ee_decide0<F32>(Params p);
+template __global__ void k_ee_decide0<BF16>(Params p);
+template __global__ void k_ee_rowstats<F32>(Params p, int i);
+template __global__ void k_ee_rowstats<BF16>(Params p, int i);
+template __global__ void k_ee_tail<F32>(Params p, int P);
+template __global__ void k_ee_tail<BF16>(Params p, int P);
+
+}  // namespace spv

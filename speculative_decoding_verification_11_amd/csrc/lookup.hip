@@ -4,6 +4,8 @@
 
 namespace {
 
+using namespace spv;
+
 // ===========================================================================
 // Prompt-lookup drafting: search the context for a recent occurrence of its
 // own last n tokens and propose the tokens that followed it ("Speculative

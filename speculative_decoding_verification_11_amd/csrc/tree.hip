@@ -4,6 +4,8 @@
 
 namespace {
 
+using namespace spv;
+
 // ===========================================================================
 // Greedy verification of candidate trees. A tree's node 0 is the root (the
 // last committed position); node n >= 1 holds a drafted token and a parent
