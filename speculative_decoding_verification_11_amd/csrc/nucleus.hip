@@ -1,30 +1,32 @@
 // nucleus.hip -- the top-k and top-p (nucleus) filters of the verification
 // step on MI355X (gfx950): one workgroup per filtered row finds the row's
-// threshold logit and kept mass (k_nucleus, launched from verify.hip).
+// threshold logit and kept mass (k_filter for bf16 rows, k_nucleus for fp32
+// rows; launched from verify.hip).
 #include "verify.h"
 
 namespace spv {
 
 // ===========================================================================
-// Top-p. The pages require verification to use the target's own sampling
-// parameters, temperature and top-p ("Speculative Decoding and the Art of
-// Fast LLM Inference", "Why It Stays Exact", key limitation). Each row keeps
-// whole probability levels (equal logits) from the top until their mass
-// reaches top_p of the row's mass, and is renormalised over them; the draft
-// rows get the same rule. k_nucleus finds, per row, the smallest kept logit
-// and the kept mass by an exact radix select over an order-preserving key of
-// the logit: digits of 12 bits (then the rest), most significant first.
-// Each pass streams the row and adds every element's weight 2^((x-m)s), in
-// fixed point (fix_bits fraction bits), to a 4096-bin LDS histogram of the
-// next digit among the elements that match the digits found so far; 64-bit
-// integer sums make the result independent of the order of the adds. The
-// crossing is found by an integer scan from the top bin; the target mass
-// ceil(top_p * total) is formed exactly in 128 bits. A bf16 row first takes
-// one pass that counts the elements of each key within kWinKeys keys below
-// the row max (a key's fixed-point mass is its count times one element's)
-// and adds up the rest; only when the crossing lies below that window does
-// the row go through the radix passes. Both give the same integers, and both
-// skip the elements whose fixed-point mass is 0.
+// Top-k and top-p. The pages require verification to use the target's own
+// sampling parameters, temperature and top-p ("Speculative Decoding and the
+// Art of Fast LLM Inference", "Why It Stays Exact", key limitation). Top-k
+// keeps whole levels (equal logits) from the top until they hold at least
+// top_k tokens; top-p then keeps whole levels from the top until their mass
+// reaches top_p of what is left; the row is renormalised over what is kept,
+// and the draft rows get the same rule. Masses are fixed-point integers:
+// each token weighs floor(2^((x-m)s) * 2^fix_bits), m the row max, so every
+// sum is exact and independent of the order of the adds, and the target mass
+// ceil(top_p * total) is formed exactly in 128 bits.
+//
+// bf16 rows (k_filter) take one pass that counts the tokens of each bf16
+// value: tokens of one value weigh the same, so a value's mass is its count
+// times one token's weight, and neither the counts nor the window they live
+// in depend on the row max, which comes out of the counts. fp32 rows
+// (k_nucleus), and the bf16 rows the count cannot settle, go through an
+// exact radix select over an order-preserving key of the logit: digits of
+// 12 bits (then the rest), most significant first; each pass streams the row
+// and adds every token's weight (and count) to a 4096-bin LDS histogram of
+// the next digit among the tokens that match the digits found so far.
 // ===========================================================================
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
@@ -71,35 +73,6 @@ __device__ inline uint64_t mass_target(uint64_t total, float top_p)
     return q + ((lo & ((1ull << sh) - 1)) != 0 ? 1 : 0);
 }
 
-// bf16 rows: exact counts per key over kWinKeys entries of a compressed key
-// order below the row max. Magnitudes under 2^-14 (and zero) share the entry
-// kTinyIdx, whose mass is summed element by element instead; every other
-// entry is one bf16 value. From a max of about 16, 8192 entries reach below
-// -2^30, so the rows' mass lies inside the window. One more counter, at
-// kWinKeys, takes the values beyond the window.
-constexpr int kWinKeys = 8192;
-constexpr uint32_t kTinyBits = 113u << 7;  // bf16 magnitude bits of 2^-14
-constexpr uint32_t kTinyIdx = 0x8000u - kTinyBits;
-
-// Compressed index of a 16-bit order key: monotone, and one-to-one except
-// that all magnitudes below 2^-14 map to kTinyIdx.
-__device__ inline uint32_t compress_key(uint32_t key)
-{
-    if (key >= 0x8000u) {
-        const uint32_t u = key - 0x8000u;  // magnitude bits of a positive value
-        return u < kTinyBits ? kTinyIdx : kTinyIdx + 1u + (u - kTinyBits);
-    }
-    const uint32_t u = 0x7fffu - key;  // magnitude bits of a negative value
-    return u < kTinyBits ? kTinyIdx : kTinyIdx - 1u - (u - kTinyBits);
-}
-
-// The order key of a compressed index other than kTinyIdx.
-__device__ inline uint32_t expand_key(uint32_t c)
-{
-    return c > kTinyIdx ? 0x8000u + (c - kTinyIdx - 1u + kTinyBits)
-                        : 0x7fffu - (kTinyIdx - 1u - c + kTinyBits);
-}
-
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kNucTiles = 4;  // 16-byte loads in flight per thread (counting pass)
 
@@ -108,16 +81,34 @@ struct RadixBins {
     uint32_t cnt[kBins];             // elements per digit (top-k)
 };
 
+// The counting window of a bf16 row: entry (u - kTinyBits) | sign << 12 for
+// the magnitude bits u of the values in [2^-14, 2^18) of either sign, so one
+// entry per bf16 value and 8192 in all. In value order (position q from the
+// top): the positive entries from the largest (q < kSmallPos), the values
+// below 2^-14 in magnitude (q = kSmallPos), the negative entries from the
+// smallest magnitude.
+constexpr int kWinKeys = 8192;
+constexpr uint32_t kTinyBits = 113u << 7;  // bf16 magnitude bits of 2^-14
+constexpr int kSmallPos = kWinKeys / 2;
+constexpr int kOrderPos = kWinKeys + 1;
+constexpr int kSmallCap = 2048;  // listed values below 2^-14 (not zero) per row
+
 struct NucleusShared {
     union {
-        RadixBins rx;                 // radix passes
-        uint32_t cnt[kWinKeys + 1];   // window pass: elements per key
+        RadixBins rx;  // radix passes
+        struct {
+            uint32_t cnt[kWinKeys];            // tokens per window entry
+            unsigned short small[kSmallCap];   // bits of the values below 2^-14
+        } win;
     };
     unsigned long long wsum[kNucWaves];
     unsigned long long above;
     int digit;
     float rs;  // row max
-    float tc;  // window pass: entries below this (x - m) * scale are not counted
+    // Counting pass: tokens below 2^-14 (listed), zeros, tokens at or below
+    // -2^18; 1 + the largest order key seen, of all and of the low ones; any
+    // NaN or value at or above 2^18.
+    uint32_t n_small, n_zero, n_low, max_key, low_key, odd;
 };
 
 // Visits every element of row[0, V) as fp32 (16-byte loads where aligned).
@@ -177,15 +168,16 @@ __device__ inline uint64_t block_sum(uint64_t v, NucleusShared &sh)
 }
 
 // Crossing search over n masses in the order i = 0, 1, ... (thread t owns
-// [t*per, (t+1)*per)): the first i at which the running sum reaches `need`
-// (>= 1) goes to sh.digit, the sum before it to sh.above; sh.digit = -1 if
-// all n together stay below `need`. Integer sums: the result does not
+// [t*per, (t+1)*per), per = ceil(n / threads), and `mass` returns 0 from n
+// on): the first i at which the running sum reaches `need` (>= 1) goes to
+// sh.digit, the sum before it to sh.above; sh.digit = -1 if all n together
+// stay below `need`. Integer sums: the result does not
 // depend on the order of any addition.
 template <class M>
 __device__ inline void crossing(int n, uint64_t need, M &&mass, NucleusShared &sh)
 {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int per = n >= kNucThreads ? n / kNucThreads : 1;
+    const int per = (n + kNucThreads - 1) / kNucThreads;  // mass(q) is 0 for q >= n
     const bool owns = tid * per < n;
     uint64_t loc = 0;
     if (owns)
@@ -299,211 +291,306 @@ __device__ __forceinline__ Selection radix_select(const typename D::Elem *row, i
     return res;
 }
 
-// One counting pass over a bf16 row (see the top-p notes above). Top-p
-// alone: only the entries that can hold the crossing are counted, the
-// rest add their weight from the table. With top-k: every window entry is
-// counted, the top-k threshold is the entry where the running count
-// reaches top_k, and the nucleus, if any, is taken among the entries up
-// to it. Returns false when the answer is not in the window (then the
-// radix passes decide).
+// Top-k, then top-p, by radix selects (m the row max); the result goes to
+// *out as (threshold logit, kept mass, m, 0).
 template <class D>
-__device__ __forceinline__ bool window_select(const typename D::Elem *row, int64_t V, float m, float scale,
-                              int fix_bits, float zlim, float tc_mass, bool k_on, int64_t top_k,
-                              bool p_on, float top_p, float2 *out, NucleusShared &sh)
+__device__ __forceinline__ void radix_filter(const typename D::Elem *row, int64_t V, float m,
+                                             float scale, float fscale, float zlim, bool k_on,
+                                             int64_t top_k, bool p_on, float top_p, float4 *out,
+                                             NucleusShared &sh)
+{
+    uint32_t lo = 0;
+    if (k_on) {
+        const Selection sk =
+            radix_select<D, true>(row, V, m, scale, fscale, zlim, 0u, top_k, top_p, sh);
+        if (!p_on) {
+            if (threadIdx.x == 0)
+                *out = make_float4(key_value<D>(sk.key), (float)sk.kept / fscale, m, 0.f);
+            return;
+        }
+        lo = sk.key;
+    }
+    const Selection sp = radix_select<D, false>(row, V, m, scale, fscale, zlim, lo, 0, top_p, sh);
+    if (threadIdx.x == 0)
+        *out = make_float4(key_value<D>(sp.key), (float)sp.kept / fscale, m, 0.f);
+}
+
+// The row max by a pass over the row (the largest non-NaN logit).
+template <class D>
+__device__ inline float row_max(const typename D::Elem *row, int64_t V, NucleusShared &sh)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float mx = -INFINITY;
+    for_each_logit<D>(row, V, [&](float x) { mx = fmaxf(mx, x); });
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    __syncthreads();  // wsum is free
+    if (lane == 0)
+        sh.wsum[wave] = __float_as_uint(mx);
+    __syncthreads();
+    float m = -INFINITY;
+    for (int q = 0; q < kNucWaves; ++q)
+        m = fmaxf(m, __uint_as_float((uint32_t)sh.wsum[q]));
+    return m;
+}
+
+// Value and order key of window entry e.
+__device__ inline uint32_t entry_bits(uint32_t e)
+{
+    const uint32_t mag = kTinyBits + (e & 0xfffu);
+    return (e & 0x1000u) ? (0x8000u | mag) : mag;
+}
+__device__ inline float entry_value(uint32_t e) { return __uint_as_float(entry_bits(e) << 16); }
+__device__ inline uint32_t bf16_key(uint32_t r)  // order key of bf16 bits (+0 and -0: one)
+{
+    return (r & 0x8000u) ? ((r & 0x7fffu) ? (~r & 0xffffu) : 0x8000u) : (r | 0x8000u);
+}
+// Window entry at order position q (q != kSmallPos).
+__device__ inline uint32_t pos_entry(int q)
+{
+    return q < kSmallPos ? (uint32_t)(kSmallPos - 1 - q) : (uint32_t)(q - 1);
+}
+
+// The counting pass over a bf16 row: window counts, the listed small values,
+// the zeros and low values, and the row max key, all in sh.
+template <class D>
+__device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V,
+                                          NucleusShared &sh)
 {
     const int tid = threadIdx.x;
-    const float fscale = __uint_as_float((uint32_t)(127 + fix_bits) << 23);  // 2^fix_bits
+    for (int q = tid; q < kWinKeys; q += kNucThreads)
+        sh.win.cnt[q] = 0;
+    if (tid == 0) {
+        sh.n_small = sh.n_zero = sh.n_low = 0;
+        sh.max_key = sh.low_key = sh.odd = 0;
+    }
+    __syncthreads();
+    uint32_t zeros = 0, lows = 0, low_key = 0, small_key = 0, odd = 0;
+    // A token outside the window (its count, if any, is taken back by the
+    // caller).
+    auto rare = [&](uint32_t r) {
+        const uint32_t u = r & 0x7fffu;
+        if (u == 0) {
+            ++zeros;
+        } else if (u < kTinyBits) {
+            const uint32_t i = atomicAdd(&sh.n_small, 1u);
+            if (i < (uint32_t)kSmallCap)
+                sh.win.small[i] = (unsigned short)r;
+            small_key = max(small_key, bf16_key(r) + 1u);
+        } else if ((r & 0x8000u) && u <= 0x7f80u) {  // at or below -2^18, -inf included
+            ++lows;
+            low_key = max(low_key, bf16_key(r) + 1u);
+        } else {
+            odd = 1;  // at or above 2^18, or NaN
+        }
+    };
+    // Eight tokens (one 16-byte load), two per 32-bit word in 16-bit lanes:
+    // t = r - kTinyBits; a window token has t in [0, 0x1000) (positive) or
+    // [0x8000, 0x9000) (negative), so bits 12..14 of t are zero exactly for
+    // the window, and its entry is t's low 12 bits with the sign (bit 15)
+    // moved to bit 12. Every token is counted at that entry; the few outside
+    // the window are taken back.
+    const uint32_t tb2 = kTinyBits * 0x10001u;
+    auto visit_group = [&](const u32x4 &g) {
+        const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+        uint32_t t[4], e[4], any = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            t[j] = as_u32(as_u16x2(w[j]) - as_u16x2(tb2));
+            e[j] = (t[j] & 0x0fff0fffu) |
+                   (as_u32(as_u16x2(t[j]) >> (unsigned short)3) & 0x10001000u);
+            any |= t[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            atomicAdd(&sh.win.cnt[e[j] & 0xffffu], 1u);
+            atomicAdd(&sh.win.cnt[e[j] >> 16], 1u);
+        }
+        if (any & 0x70007000u) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sh16 = (j & 1) * 16;
+                if ((t[j >> 1] >> sh16) & 0x7000u) {
+                    atomicSub(&sh.win.cnt[(e[j >> 1] >> sh16) & 0xffffu], 1u);
+                    rare((w[j >> 1] >> sh16) & 0xffffu);
+                }
+            }
+        }
+    };
+    auto visit_one = [&](uint32_t r) {
+        const uint32_t t = (r - kTinyBits) & 0xffffu;
+        if (t & 0x7000u)
+            rare(r);
+        else
+            atomicAdd(&sh.win.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
+    };
+    const Span sp = make_span<D>(row, 0, V);
+    const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
+    for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kNucTiles) {
+        u32x4 r[kNucTiles];
+#pragma unroll
+        for (int u = 0; u < kNucTiles; ++u) {
+            const int64_t vi = base + u * kNucThreads + tid;
+            r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kNucTiles; ++u)
+            if (base + u * kNucThreads + tid < sp.ngroups)
+                visit_group(r[u]);
+    }
+    if (sp.s + tid < sp.a)
+        visit_one((uint32_t)__builtin_bit_cast(unsigned short, row[sp.s + tid]));
+    if (sp.z + tid < sp.e)
+        visit_one((uint32_t)__builtin_bit_cast(unsigned short, row[sp.z + tid]));
+    if (zeros)
+        atomicAdd(&sh.n_zero, zeros);
+    if (lows) {
+        atomicAdd(&sh.n_low, lows);
+        atomicMax(&sh.low_key, low_key);
+    }
+    if (odd)
+        atomicOr(&sh.odd, 1u);
+    __syncthreads();
+    // 1 + the row max key: the largest counted entry, small value, zero or
+    // low value.
+    uint32_t mk = max(small_key, sh.n_zero ? 0x8001u : 0u);
+    mk = max(mk, sh.low_key);
+    for (int q = tid; q < kWinKeys; q += kNucThreads)
+        if (sh.win.cnt[q])
+            mk = max(mk, bf16_key(entry_bits((uint32_t)q)) + 1u);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, kWave));
+    if ((tid & (kWave - 1)) == 0)
+        atomicMax(&sh.max_key, mk);
+    __syncthreads();
+}
+
+// One workgroup per bf16 row of every sampling sequence with a top-k or
+// top-p filter: the counting pass, then the thresholds from the counts (or,
+// when they cannot settle them, the radix passes). The row max goes out with
+// the result; k_rowstats does not read these rows.
+template <class D>
+__global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
+{
+    static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
+    using E = typename D::Elem;
+    __shared__ NucleusShared sh;
+    const int k = p.k, rows = 2 * k + 1;
+    const int64_t rb = blockIdx.x;
+    const int slot = (int)(rb % rows);
+    const int64_t b = rb / rows;
+    const int tid = threadIdx.x;
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    const float top_p = p.top_p ? p.top_p[b] : 1.f;
+    const int64_t top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
+    if (!valid_len(L, k) || !valid_temp(tau) || tau == 0.f || !(top_p > 0.f))
+        return;
+    const bool p_on = top_p < 1.f;
+    const bool k_on = top_k > 0 && top_k < (int64_t)p.V;
+    if (!p_on && !k_on)
+        return;
+    const bool is_target = slot <= k;
+    const int i = is_target ? slot : slot - (k + 1);
+    if (is_target ? i > L : i >= L)
+        return;
+    const E *row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
+                             : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
+    const float scale = temp_scale(tau);
+    const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
+    const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0
+    float4 *const out = p.nucleus + b * rows + slot;
+
+    count_row<D>(row, p.V, sh);
+    if (sh.odd) {  // NaN or a value at or above 2^18: the max by its own pass
+        const float m = row_max<D>(row, p.V, sh);
+        __syncthreads();
+        radix_filter<D>(row, p.V, m, scale, fscale, zlim, k_on, top_k, p_on, top_p, out, sh);
+        return;
+    }
+    const float m = key_value<D>(sh.max_key - 1u);
     auto fixed = [&](float x) {
         return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
     };
-    // In raw bits r, with magnitude u = r & 0x7fff and
-    // d = max(u - kTinyBits + 1, 0), the window entry is A - d for a
-    // positive and A + d for a negative value, A being the entry of the
-    // tiny values (d = 0), all of it in 16-bit arithmetic: two elements per
-    // 32-bit word.
-    const uint32_t cm = compress_key(order_key<D>(m));
-    const uint32_t A = cm - kTinyIdx;
-    // Window entry of the lowest bf16 value at or below x (x rounded down
-    // to bf16).
-    auto entry_below = [&](float x) {
-        const uint32_t bx = __float_as_uint(x);
-        uint32_t r = bx >> 16;
-        if ((bx & 0xffffu) && (bx & 0x80000000u))
-            r += 1u;  // a truncated negative value: one step further down
-        return cm - compress_key((r & 0x8000u) ? (~r & 0xffffu) : (r | 0x8000u));
-    };
-    // Entries from iz on hold values below m + (zlim - 2) / scale: they
-    // weigh 0. Top-p alone: entries in [kWinKeys, iz) have mass but no
-    // counter (summed one by one); with top-k they lie below every counted
-    // entry and play no part.
-    const uint32_t iz =
-        __builtin_amdgcn_readfirstlane(entry_below(m + (zlim - 2.f) / scale) + 1u);
-    const bool wide = !k_on && iz > (uint32_t)kWinKeys;
-    // Top-p alone: entries from wc on hold values with (x - m) * scale < tc.
-    // Together those weigh at most V * 2^tc = (1 - top_p) / 4 of the row, so
-    // the crossing lies above them; and each weighs below 2^31 in fixed
-    // point. They are not counted: their entries hold that weight instead,
-    // which each element adds to the total. With top-k, wc = kWinKeys.
-    const float tc = fminf(tc_mass, (float)(30 - fix_bits));
-    const uint32_t wc = k_on ? (uint32_t)kWinKeys
-                             : __builtin_amdgcn_readfirstlane(
-                                   min(entry_below(m + tc / scale) + 1u, (uint32_t)kWinKeys));
-    for (int q = tid; q <= kWinKeys; q += kNucThreads) {
-        uint32_t v = 0;
-        if ((uint32_t)q >= wc && q < kWinKeys && (uint32_t)q != A && (uint32_t)q <= cm)
-            v = (uint32_t)fixed(key_value<D>(expand_key(cm - (uint32_t)q)));
-        sh.cnt[q] = v;
-    }
-    __syncthreads();
-    unsigned long long below = 0, tiny = 0;
-    const u16x2 a2 = (u16x2)(unsigned short)A;
-    const u16x2 w2 = (u16x2)(unsigned short)kWinKeys;
-    const u16x2 wm2 = (u16x2)(unsigned short)(kWinKeys - 1);
-    const u16x2 tb2 = (u16x2)(unsigned short)kTinyBits;
-    const u16x2 tbm2 = (u16x2)(unsigned short)(kTinyBits - 1u);
-    // Tiny values and values beyond the window with mass: one by one
-    // (their entries, A and kWinKeys, hold no weight).
-    auto rare = [&](uint32_t r, uint32_t idx) {
-        const bool is_tiny = (r & 0x7fffu) < kTinyBits;
-        const bool beyond = wide && idx >= (uint32_t)kWinKeys && idx < iz;
-        const unsigned long long f = fixed(__uint_as_float(r << 16));
-        tiny += is_tiny ? f : 0ull;
-        below += !is_tiny && beyond ? f : 0ull;
-    };
-    auto visit_slot = [&](uint32_t slot) {
-        const uint32_t v = sh.cnt[slot];
-        if (slot < wc)
-            atomicAdd(&sh.cnt[slot], 1u);
-        below += slot < wc ? 0u : v;
-    };
-    // Eight elements (one 16-byte load): all window reads are issued before
-    // the counts and the sums, so one wait covers them.
-    auto visit_group = [&](const u32x4 &g) {
-        const uint32_t w[4] = {g.x, g.y, g.z, g.w};
-        uint32_t idx[4], slot[8];
-        bool any_rare = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u16x2 u = as_u16x2(w[j] & 0x7fff7fffu);
-            const u16x2 d = __builtin_bit_cast(
-                u16x2, __builtin_elementwise_max(__builtin_bit_cast(i16x2, u - tbm2), (i16x2)0));
-            const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
-            idx[j] = (as_u32(a2 + d) & neg) | (as_u32(a2 - d) & ~neg);
-            const uint32_t s2 = as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), w2));
-            slot[2 * j] = s2 & 0xffffu;
-            slot[2 * j + 1] = s2 >> 16;
-            const bool has_tiny = as_u32(__builtin_elementwise_min(u, tb2)) != as_u32(tb2);
-            const bool has_beyond =
-                as_u32(__builtin_elementwise_min(as_u16x2(idx[j]), wm2)) != idx[j];
-            any_rare |= has_tiny || (wide && has_beyond);
-        }
-        uint32_t v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = sh.cnt[slot[j]];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (slot[j] < wc)
-                atomicAdd(&sh.cnt[slot[j]], 1u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            below += slot[j] < wc ? 0u : v[j];
-        if (any_rare) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                rare(w[j] & 0xffffu, idx[j] & 0xffffu);
-                rare(w[j] >> 16, idx[j] >> 16);
-            }
-        }
-    };
-    {
-        const Span sp = make_span<D>(row, 0, V);
-        const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
-        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kNucThreads * kNucTiles) {
-            u32x4 r[kNucTiles];
-#pragma unroll
-            for (int u = 0; u < kNucTiles; ++u) {
-                const int64_t vi = base + u * kNucThreads + tid;
-                r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < kNucTiles; ++u)
-                if (base + u * kNucThreads + tid < sp.ngroups)
-                    visit_group(r[u]);
-        }
-        auto visit_one = [&](uint32_t r) {
-            const uint32_t u = r & 0x7fffu;
-            const uint32_t d = u < kTinyBits ? 0u : u - (kTinyBits - 1u);
-            const uint32_t idx = ((r & 0x8000u) ? A + d : A - d) & 0xffffu;
-            visit_slot(min(idx, (uint32_t)kWinKeys));
-            rare(r, idx);
+    const uint32_t n_small = sh.n_small, n_zero = sh.n_zero;
+    bool settled = n_small <= (uint32_t)kSmallCap;
+    if (settled) {
+        // The small values: zeros weigh one amount, the listed ones each
+        // their own.
+        uint64_t mine = tid == 0 ? (uint64_t)n_zero * fixed(0.f) : 0;
+        for (uint32_t q = tid; q < n_small; q += kNucThreads)
+            mine += fixed(__uint_as_float((uint32_t)sh.win.small[q] << 16));
+        const uint64_t small_mass = block_sum(mine, sh);
+        const uint64_t small_count = (uint64_t)n_small + n_zero;
+        int last = kOrderPos - 1;  // the nucleus is taken among positions [0, last]
+        auto count_at = [&](int q) -> uint64_t {
+            if (q >= kOrderPos)
+                return 0;
+            return q == kSmallPos ? small_count : sh.win.cnt[pos_entry(q)];
         };
-        if (sp.s + tid < sp.a)
-            visit_one((uint32_t)row[sp.s + tid]);
-        if (sp.z + tid < sp.e)
-            visit_one((uint32_t)row[sp.z + tid]);
-    }
-    const uint64_t tiny_total = block_sum(tiny, sh);
-    auto key_mass = [&](int idx) -> uint64_t {
-        if ((uint32_t)idx == A)
-            return tiny_total;
-        const uint32_t n = (uint32_t)idx < wc ? sh.cnt[idx] : 0u;
-        return n ? (uint64_t)n * fixed(key_value<D>(expand_key(cm - (uint32_t)idx))) : 0;
-    };
-    constexpr int kPer = kWinKeys / kNucThreads;
-    uint64_t total, need;
-    int last = kWinKeys - 1;  // the nucleus is taken among entries [0, last]
-    if (k_on) {
-        // The top-k threshold: the entry where the running count reaches
-        // top_k (the count of the tiny entry is its number of tiny values).
-        crossing(kWinKeys, (uint64_t)top_k, [&](int q) -> uint64_t { return sh.cnt[q]; }, sh);
-        const int dk = sh.digit;
-        if (dk < 0 || (uint32_t)dk == A)
-            return false;  // fewer than top_k values in the window, or tiny
-        last = dk;
-        uint64_t mine = 0;
-        for (int q = 0; q < kPer; ++q)
-            mine += tid * kPer + q <= last ? key_mass(tid * kPer + q) : 0ull;
-        total = block_sum(mine, sh);
-        if (!p_on) {
-            if (tid == 0)
-                *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)dk)),
-                                   (float)total / fscale);
-            return true;
+        auto mass_at = [&](int q) -> uint64_t {
+            if (q > last)
+                return 0;
+            if (q == kSmallPos)
+                return small_mass;
+            const uint32_t e = pos_entry(q), n = sh.win.cnt[e];
+            return n ? (uint64_t)n * fixed(entry_value(e)) : 0;
+        };
+        constexpr int kPer = (kOrderPos + kNucThreads - 1) / kNucThreads;
+        uint64_t total = 0;
+        if (k_on) {
+            // The top-k threshold: the position where the running count
+            // reaches top_k.
+            crossing(kOrderPos, (uint64_t)top_k, count_at, sh);
+            const int dk = sh.digit;
+            settled = dk >= 0 && dk != kSmallPos;
+            if (settled) {
+                last = dk;
+                uint64_t kept = 0;
+                for (int q = 0; q < kPer; ++q)
+                    kept += mass_at(tid * kPer + q);
+                total = block_sum(kept, sh);
+                if (!p_on) {
+                    if (tid == 0)
+                        *out = make_float4(entry_value(pos_entry(dk)), (float)total / fscale, m,
+                                           0.f);
+                    return;
+                }
+            }
+        } else {
+            // Tokens at or below -2^18 lie below the window: they must weigh 0.
+            settled = sh.n_low == 0 || fixed(key_value<D>(sh.low_key - 1u)) == 0;
+            if (settled) {
+                uint64_t all = 0;
+                for (int q = 0; q < kPer; ++q)
+                    all += mass_at(tid * kPer + q);
+                total = block_sum(all, sh);
+            }
         }
-        need = mass_target(total, top_p);
-    } else {
-        uint64_t win = 0;
-        for (int q = 0; q < kPer; ++q)
-            win += key_mass(tid * kPer + q);
-        if (tid == 0 && A >= (uint32_t)kWinKeys)
-            win += tiny_total;  // the tiny entry lies beyond the window
-        total = block_sum(win + below, sh);
-        need = mass_target(total, top_p);
+        if (settled) {
+            crossing(kOrderPos, mass_target(total, top_p), mass_at, sh);
+            const int d = sh.digit;
+            settled = d >= 0 && d != kSmallPos;
+            if (settled) {
+                if (tid == 0)
+                    *out = make_float4(entry_value(pos_entry(d)),
+                                       (float)(sh.above + mass_at(d)) / fscale, m, 0.f);
+                return;
+            }
+        }
     }
-    crossing(kWinKeys, need, [&](int q) -> uint64_t { return q <= last ? key_mass(q) : 0ull; },
-             sh);
-    const int d = sh.digit;
-    if (d < 0 || (uint32_t)d == A)
-        return false;  // among the tiny magnitudes or below the counted entries
-    if (tid == 0) {
-        const uint64_t kept = sh.above + key_mass(d);
-        *out = make_float2(key_value<D>(expand_key(cm - (uint32_t)d)), (float)kept / fscale);
-    }
-    return true;
+    __syncthreads();  // the radix passes reuse the shared memory
+    radix_filter<D>(row, p.V, m, scale, fscale, zlim, k_on, top_k, p_on, top_p, out, sh);
 }
 
-// One workgroup per row of every sampling sequence with a top-k or top-p
-// filter. Top-k keeps whole levels from the top until they hold at least
-// top_k tokens; the nucleus is the smallest run of keys from the top (of
-// what top-k kept) whose fixed-point mass reaches ceil(top_p * total).
-// Every mass is an integer sum, so the threshold and the kept mass do not
-// depend on how the row is split or visited.
+// One workgroup per fp32 row of every sampling sequence with a top-k or
+// top-p filter (the row max from the row statistics), by the radix passes.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
 {
     using E = typename D::Elem;
-    constexpr int KB = D::kKeyBits;
     __shared__ NucleusShared sh;
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     const int64_t rb = blockIdx.x;
@@ -528,48 +615,20 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
                              : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
     const float scale = temp_scale(tau);
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
-    // Elements with (x - m) * scale below this weigh 0 in fixed point.
-    const float zlim = -(float)(p.fix_bits + 2);
+    const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0
     if (tid == 0) {
         const float2 *pp = p.partials + (b * rows + slot) * (int64_t)nc;
         float m = -INFINITY;  // the row max: the largest chunk max
         for (int c = 0; c < nc; ++c)
             m = fmaxf(m, pp[c].x);
-        float z = 0.f;  // the row's mass relative to its max
-        for (int c = 0; c < nc; ++c)
-            z += pp[c].y * exp2_fast((pp[c].x - m) * scale);
         sh.rs = m;
-        // (x - m) * scale < tc: together at most V * 2^tc = (1 - top_p) z / 4
-        sh.tc = p_on ? fmaxf(zlim, __log2f((1.f - top_p) * z / (float)p.V) - 2.f) : zlim;
-        sh.above = 0;
     }
     __syncthreads();
-    const float m = sh.rs, tc = sh.tc;
-    float2 *const out = p.nucleus + b * rows + slot;
-
-    if constexpr (KB == 16) {
-        if (window_select<D>(row, p.V, m, scale, p.fix_bits, zlim, tc, k_on, top_k, p_on, top_p,
-                             out, sh))
-            return;
-        __syncthreads();  // the radix passes reuse the shared memory
-    }
-    uint32_t lo = 0;
-    if (k_on) {
-        const Selection sk = radix_select<D, true>(row, p.V, m, scale, fscale, zlim, 0u, top_k,
-                                                   top_p, sh);
-        if (!p_on) {
-            if (tid == 0)
-                *out = make_float2(key_value<D>(sk.key), (float)sk.kept / fscale);
-            return;
-        }
-        lo = sk.key;
-    }
-    const Selection sp = radix_select<D, false>(row, p.V, m, scale, fscale, zlim, lo, 0, top_p, sh);
-    if (tid == 0)
-        *out = make_float2(key_value<D>(sp.key), (float)sp.kept / fscale);
+    radix_filter<D>(row, p.V, sh.rs, scale, fscale, zlim, k_on, top_k, p_on, top_p,
+                    p.nucleus + b * rows + slot, sh);
 }
 
 template __global__ void k_nucleus<F32>(Params p);
-template __global__ void k_nucleus<BF16>(Params p);
+template __global__ void k_filter<BF16>(Params p);
 
 }  // namespace spv

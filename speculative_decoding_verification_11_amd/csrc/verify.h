@@ -52,7 +52,7 @@ struct Params {
     double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
     const float *top_p;   // [B] or null: nucleus parameter per sequence
     const int32_t *top_k; // [B] or null: top-k parameter per sequence
-    float2 *nucleus;      // [B][2k+1]: top-p (threshold logit, kept mass) per row
+    float4 *nucleus;      // [B][2k+1]: filtered rows (threshold logit, kept mass, row max, 0)
     int32_t fix_bits;     // top-p: fixed-point fraction bits of the row masses
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
@@ -62,9 +62,20 @@ struct Params {
     AuxDev aux;
 };
 
-// Kernels defined in the other sources (instantiated there for F32 and BF16).
+// Whether sequence b's rows go through a top-k or top-p filter (for a
+// sampling sequence whose inputs are valid): top_p below 1, or top_k
+// strictly between 0 and V.
+__device__ inline bool seq_filtered(const Params &p, int64_t b)
+{
+    return (p.top_p && p.top_p[b] < 1.f) ||
+           (p.top_k && p.top_k[b] > 0 && p.top_k[b] < p.V);
+}
+
+// Kernels defined in the other sources. k_filter: bf16 rows only.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p);
+template <class D>
+__global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p);
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p);
 template <class D>

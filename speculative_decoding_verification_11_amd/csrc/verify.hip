@@ -129,47 +129,48 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
     } else if (status == SPEC_SEQ_OK) {
         const float scale = temp_scale(tau);
         Soft ts{-INFINITY, 0.f}, ds{-INFINITY, 0.f};
-        if (lane <= L) {
-            const float2 *pp = p.partials + (b * rows + lane) * (int64_t)nc;
-            for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
-                float2 t[kFoldBatch];
-#pragma unroll
-                for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-                for (int q = 0; q < kFoldBatch; ++q)
-                    ts = soft_merge(ts, Soft{t[q].x, t[q].y}, scale);
-            }
-        }
-        if (lane < L) {
-            const float2 *pp = p.partials + (b * rows + k + 1 + lane) * (int64_t)nc;
-            for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
-                float2 t[kFoldBatch];
-#pragma unroll
-                for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-                for (int q = 0; q < kFoldBatch; ++q)
-                    ds = soft_merge(ds, Soft{t[q].x, t[q].y}, scale);
-            }
-        }
-        // Top-p: each row keeps its logits >= its threshold, normalised by
-        // the kept mass (k_nucleus); otherwise the whole row and Z.
-        float tz = ts.z, tth = -INFINITY, dz = ds.z, dth = -INFINITY;
-        const bool filtered = (p.top_p && p.top_p[b] < 1.f) ||
-                              (p.top_k && p.top_k[b] > 0 && p.top_k[b] < V);
-        if (filtered) {
+        // Top-k / top-p: each row keeps its logits >= its threshold,
+        // normalised by the kept mass; the filter pass also gives the row
+        // max. Otherwise: the whole row, max and Z folded from the partials.
+        float tth = -INFINITY, dth = -INFINITY;
+        if (seq_filtered(p, b)) {
             if (lane <= L) {
-                const float2 n = p.nucleus[b * rows + lane];
+                const float4 n = p.nucleus[b * rows + lane];
                 tth = n.x;
-                tz = n.y;
+                ts = Soft{n.z, n.y};
             }
             if (lane < L) {
-                const float2 n = p.nucleus[b * rows + k + 1 + lane];
+                const float4 n = p.nucleus[b * rows + k + 1 + lane];
                 dth = n.x;
-                dz = n.y;
+                ds = Soft{n.z, n.y};
+            }
+        } else {
+            if (lane <= L) {
+                const float2 *pp = p.partials + (b * rows + lane) * (int64_t)nc;
+                for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
+                    float2 t[kFoldBatch];
+#pragma unroll
+                    for (int q = 0; q < kFoldBatch; ++q)
+                        t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+                    for (int q = 0; q < kFoldBatch; ++q)
+                        ts = soft_merge(ts, Soft{t[q].x, t[q].y}, scale);
+                }
+            }
+            if (lane < L) {
+                const float2 *pp = p.partials + (b * rows + k + 1 + lane) * (int64_t)nc;
+                for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
+                    float2 t[kFoldBatch];
+#pragma unroll
+                    for (int q = 0; q < kFoldBatch; ++q)
+                        t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+                    for (int q = 0; q < kFoldBatch; ++q)
+                        ds = soft_merge(ds, Soft{t[q].x, t[q].y}, scale);
+                }
             }
         }
+        const float tz = ts.z, dz = ds.z;
         if (lane < L) {
             const float xt = D::at(target + (b * (k + 1) + lane) * (int64_t)V, g);
             const float xd = D::at(draft + (b * k + lane) * (int64_t)V, g);
@@ -617,6 +618,8 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
     if (!valid_len(L, k) || !valid_temp(tau))
         return;  // the decision reports the sequence
     const bool greedy = tau == 0.f;
+    if (D::kKeyBits == 16 && !greedy && seq_filtered(p, b))
+        return;  // a filtered bf16 row: k_filter reads it and finds its max
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
     if (is_target ? i > L : (greedy || i >= L))
@@ -703,7 +706,7 @@ bool layout_for(int32_t B, int32_t k, int32_t V, int32_t dtype, Layout *lay)
     lay->masses = lay->decisions + align_up(nb * sizeof(Decision), 256);
     lay->segs = lay->masses + align_up(nb * (size_t)lay->nc * sizeof(double2), 256);
     lay->nucleus = lay->segs + align_up(nb * (size_t)lay->nc * 2 * kSegs * sizeof(double), 256);
-    lay->ee_count = lay->nucleus + align_up(nb * (size_t)(2 * k + 1) * sizeof(float2), 256);
+    lay->ee_count = lay->nucleus + align_up(nb * (size_t)(2 * k + 1) * sizeof(float4), 256);
     lay->ee_list = lay->ee_count + align_up((size_t)(k + 2) * sizeof(int32_t), 256);
     lay->ee_done = lay->ee_list + align_up((size_t)(k + 1) * nb * sizeof(int32_t), 256);
     lay->total = lay->ee_done + align_up((size_t)(k + 1) * nb * sizeof(int32_t), 256);
@@ -742,7 +745,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         p.decisions = reinterpret_cast<Decision *>(ws + lay.decisions) + b0;
         p.masses = reinterpret_cast<double2 *>(ws + lay.masses) + b0 * nc;
         p.segs = reinterpret_cast<double *>(ws + lay.segs) + b0 * nc * 2 * kSegs;
-        p.nucleus = reinterpret_cast<float2 *>(ws + lay.nucleus) + b0 * rows;
+        p.nucleus = reinterpret_cast<float4 *>(ws + lay.nucleus) + b0 * rows;
         if (p.top_p) p.top_p += b0;
         if (p.top_k) p.top_k += b0;
         // Early-exit lists and counters are per slice (indexed by the
@@ -771,9 +774,14 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                                stream, p);
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
-            if (p.top_p || p.top_k)
-                hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads), 0,
-                                   stream, p);
+            if (p.top_p || p.top_k) {
+                if constexpr (D::kKeyBits == 16)
+                    hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)),
+                                       dim3(kNucThreads), 0, stream, p);
+                else
+                    hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)),
+                                       dim3(kNucThreads), 0, stream, p);
+            }
             if (nb * nc <= kFoldDecisionItems)
                 p.decide_in_draw = 1;
             else

@@ -184,6 +184,51 @@ def test_top_k_beyond_the_window_and_among_tiny_logits():
         check(total, "top-k far/tiny")
 
 
+def test_top_k_masked_rows_bf16():
+    """Rows mostly masked to -inf (or -3e38) with a few levels, zeros and
+    values under 2^-14 among them: top_k ending on a window level, on the
+    zeros or small values, and past every unmasked token (among the masked
+    ones); with and without top-p after it."""
+    rng = np.random.default_rng(34)
+    B, k, V = 8, 2, 30000
+    mask = [0xFF80, _bf16(-3e38)]
+    t = np.empty((B, k + 1, V), np.uint16)
+    d = np.empty((B, k, V), np.uint16)
+    for b in range(B):
+        lv = [(_bf16(4.0), 3), (_bf16(2.0), 30), (0, 50), (_bf16(1e-6), 20),
+              (_bf16(-0.5), 300), (mask[b % 2], 0)]
+        for i in range(k + 1):
+            t[b, i] = _shuffled(rng, V, lv)
+        for i in range(k):
+            d[b, i] = _shuffled(rng, V, lv)
+    g = bf16_to_f32(d).argmax(axis=2).astype(np.int32)
+    L = np.full(B, k, np.int32)
+    tau = np.full(B, 0.7, np.float32)
+    cb = raw_batch(t, d, g, L, tau)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    # 1 and 20: window levels; 40 and 60: the zeros; 90: the small values;
+    # 200: -0.5; 500 and 5000: among the masked tokens
+    top_k = np.array([1, 20, 40, 60, 90, 200, 500, 5000], np.int32)
+    for top_p in (None, np.full(B, 0.9, np.float32)):
+        total = parity.Report()
+        for seed in (31, 32):
+            say(f"[case] top-k masked top_p={top_p is not None} seed={seed}")
+            g_ = run_tk(gb, seed, top_k, top_p)
+            r = parity.oracle_on(h, seed, top_k=top_k, top_p=top_p)
+            total.merge(parity.compare(g_, r, L, tau, k))
+        check(total, "top-k masked")
+
+
+def _shuffled(rng, V, levels):
+    r = np.full(V, levels[-1][0], np.uint16)
+    at = 0
+    for bits, n in levels[:-1]:
+        r[at:at + n] = bits
+        at += n
+    return r[rng.permutation(V)]
+
+
 def test_top_k_statuses_and_qzero():
     rng = np.random.default_rng(42)
     B, k, V = 6, 2, 64

@@ -131,37 +131,18 @@ def test_top_p_tied_levels_bf16():
     check(total, "top-p ties")
 
 
-def _bf16_of_key(key):
-    """bf16 bits whose order-preserving key (sign flipped for positives, all
-    bits flipped for negatives) is `key`."""
-    key = int(key)
-    return key & 0x7FFF if key & 0x8000 else (~key) & 0xFFFF
+# A bf16 row is counted per value over a window of 8192 entries, the bf16
+# values with magnitude in [2^-14, 2^18) of either sign. Zeros, the values
+# below 2^-14 (listed one by one, up to 2048 per row) and those at or below
+# -2^18 are kept apart; a crossing among the small values, below the window,
+# or rows with values at or above 2^18, NaN or a full list go through the
+# radix passes instead. Inputs below put crossings on both sides of each edge.
+_TINY_BITS = 113 << 7        # magnitude bits of 2^-14
+_WIN_TOP = _TINY_BITS + 4096  # magnitude bits of 2^18
 
 
-def _key_of_bf16(u):
-    u = int(u)
-    return (u | 0x8000) if not u & 0x8000 else (~u) & 0xFFFF
-
-
-# The bf16 nucleus counts tokens per key over a window of 8192 entries of a
-# compressed key order below the row max, where magnitudes under 2^-14 share
-# one entry; a crossing among those tiny magnitudes or below the window goes
-# through the radix passes instead. Inputs below put crossings on both sides.
-_TINY_BITS = 113 << 7
-_TINY_IDX = 0x8000 - _TINY_BITS
-
-
-def _compress(key):
-    if key >= 0x8000:
-        u = key - 0x8000
-        return _TINY_IDX if u < _TINY_BITS else _TINY_IDX + 1 + (u - _TINY_BITS)
-    u = 0x7FFF - key
-    return _TINY_IDX if u < _TINY_BITS else _TINY_IDX - 1 - (u - _TINY_BITS)
-
-
-def _expand(c):
-    return (0x8000 + (c - _TINY_IDX - 1 + _TINY_BITS) if c > _TINY_IDX
-            else 0x7FFF - (_TINY_IDX - 1 - c + _TINY_BITS))
+def _in_window(bits):
+    return _TINY_BITS <= (int(bits) & 0x7FFF) < _WIN_TOP
 
 
 def _bf16(x):
@@ -213,14 +194,16 @@ def _run_levels(t, d, tau, top_p, label):
 
 
 def test_top_p_crossing_among_tiny_logits_bf16():
-    """Heavy levels at +3e-6 and -2e-6 (both under 2^-14, so both in the
-    shared tiny entry) and at 0.25 and -8 (entries of their own): top_p puts
-    the crossing on each of them."""
+    """Heavy levels at +3e-6 and -2e-6 (both under 2^-14, so both listed
+    apart from the window) and at 0.25 and -8 (window entries): top_p puts
+    the crossing on each of them. The draft rows list 2100 small values,
+    more than the list holds."""
     rng = np.random.default_rng(57)
     B, k, V = 8, 2, 4096
     lv = [(_bf16(1.0), 1), (_bf16(0.25), 1000), (_bf16(3e-6), 1000), (_bf16(-2e-6), 1000),
           (_bf16(-8.0), 0)]
-    assert _compress(_key_of_bf16(lv[2][0])) == _compress(_key_of_bf16(lv[3][0])) == _TINY_IDX
+    assert not _in_window(lv[2][0]) and not _in_window(lv[3][0])
+    assert _in_window(lv[1][0]) and _in_window(lv[4][0])
     t = _level_rows(rng, B, k + 1, V, lv)
     d = _level_rows(rng, B, k, V, [(_bf16(1.0), 1), (_bf16(0.25), 900), (_bf16(3e-6), 1100),
                                    (_bf16(-2e-6), 1000), (_bf16(-8.0), 0)])
@@ -230,22 +213,81 @@ def test_top_p_crossing_among_tiny_logits_bf16():
     _run_levels(t, d, tau, top_p, "tiny levels")
 
 
-def test_top_p_crossing_at_the_window_edge_bf16():
-    """Levels on the last window entry below the max and on the first entry
-    past it (about -6.8e10; a temperature of 1e10 gives them weight)."""
+def test_top_p_crossing_far_below_the_max_bf16():
+    """Levels at -6.8e10, far past the window's low end, weigh something at a
+    temperature of 1e10: a crossing there, and one at -3e10 above them."""
     rng = np.random.default_rng(58)
     B, k, V = 6, 2, 4096
-    cm = _compress(_key_of_bf16(_bf16(1.0)))
-    a_bits, b_bits = _bf16_of_key(_expand(cm - 8191)), _bf16_of_key(_expand(cm - 8192))
+    a_bits, b_bits = _bf16(-6.0e10), _bf16(-6.8e10)
     lv = [(_bf16(1.0), 1), (a_bits, 1000), (b_bits, 1000), (_bf16(-3e10), 0)]
     t = _level_rows(rng, B, k + 1, V, lv)
     d = _level_rows(rng, B, k, V, [(_bf16(1.0), 1), (a_bits, 900), (b_bits, 1100),
                                    (_bf16(-3e10), 0)])
     tau = np.full(B, 1e10, np.float32)
     top_p = np.array([0.5, 0.985, 0.995] * 2, np.float32)
-    # levels from the top: 1.0, -3e10, then the two edge levels
+    # levels from the top: 1.0, -3e10, then the two far levels
     assert _crossing_levels(t, tau, top_p) == [1, 2, 3] * 2
-    _run_levels(t, d, tau, top_p, "window edge")
+    _run_levels(t, d, tau, top_p, "far below")
+
+
+# The window's edges in bf16 bits: its largest and smallest positive values,
+# the largest value below it, zero and -0, and the same on the negative side.
+_EDGE = {"top": _WIN_TOP - 1, "2^18": _WIN_TOP, "2^-14": _TINY_BITS, "under": _TINY_BITS - 1,
+         "zero": 0x0000, "-0": 0x8000, "-2^-14": 0x8000 | _TINY_BITS,
+         "-under": 0x8000 | (_TINY_BITS - 1), "bottom": 0x8000 | (_WIN_TOP - 1),
+         "-2^18": 0x8000 | _WIN_TOP, "-inf": 0xFF80}
+
+
+@pytest.mark.parametrize("extra", [None, "2^18", "-2^18"])
+def test_top_p_window_edges_bf16(extra):
+    """Levels on every edge of the counting window at a temperature (1e6)
+    that gives them all comparable weight, crossings put on each, the rest of
+    the row at -inf. With a level at 2^18 (past the window's top) the row max
+    comes from a pass of its own; with one at -2^18 (past its bottom) that
+    weighs something, the radix passes decide."""
+    rng = np.random.default_rng(59 + (extra is not None) + (extra == "-2^18"))
+    k, V = 1, 4096
+    names = ["top", "2^-14", "under", "zero", "-0", "-under", "-2^-14", "bottom"]
+    if extra == "2^18":
+        names = ["2^18"] + names
+    elif extra == "-2^18":
+        names = names + ["-2^18"]
+    lv = [(_EDGE[n], 300) for n in names] + [(_EDGE["-inf"], 0)]
+    assert [_in_window(b) for b, _ in lv[:-1]] == [n in ("top", "2^-14", "-2^-14", "bottom")
+                                                     for n in names]
+    tau_v = 1e6
+    # levels from the top (zero and -0 are one level)
+    x = np.array([bf16_to_f32(np.array([b], np.uint16))[0] for b, _ in lv[:-1]], np.float64)
+    order = sorted(set(x.tolist()), reverse=True)
+    w = np.array([300 * (2 if v == 0 else 1) * np.exp((v - order[0]) / tau_v) for v in order])
+    cum = np.cumsum(w) / w.sum()
+    # one top_p ending in the middle of each level
+    top_p = np.array([cum[i] - w[i] / w.sum() / 2 for i in range(len(order))], np.float32)
+    B = len(top_p)
+    t = _level_rows(rng, B, k + 1, V, lv)
+    d = _level_rows(rng, B, k, V, lv)
+    tau = np.full(B, tau_v, np.float32)
+    assert _crossing_levels(t, tau, top_p) == list(range(len(order)))
+    _run_levels(t, d, tau, top_p, f"window edges {extra}")
+
+
+def test_top_p_masked_rows_bf16():
+    """Most of each row masked to -inf (no weight, counted apart) or to -3e38,
+    the rest a few levels; crossings on each level."""
+    rng = np.random.default_rng(60)
+    B, k, V = 8, 2, 50000
+    mask = [_EDGE["-inf"], _bf16(-3e38)]
+    t = np.empty((B, k + 1, V), np.uint16)
+    d = np.empty((B, k, V), np.uint16)
+    for b in range(B):
+        lv = [(_bf16(5.0), 1), (_bf16(3.0), 40), (_bf16(1.0), 400), (0, 100),
+              (_bf16(-1.0), 2000), (mask[b % 2], 0)]
+        t[b] = _level_rows(rng, 1, k + 1, V, lv)[0]
+        d[b] = _level_rows(rng, 1, k, V, lv)[0]
+    tau = np.full(B, 0.9, np.float32)
+    top_p = np.array([0.05, 0.3, 0.6, 0.79, 0.9, 0.99, 0.7, 0.95], np.float32)
+    assert _crossing_levels(t, tau, top_p) == [0, 1, 2, 3, 4, 4, 2, 4]
+    _run_levels(t, d, tau, top_p, "masked rows")
 
 
 def test_top_p_statuses_and_qzero():
