@@ -470,9 +470,12 @@ def main() -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i, fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
+            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None,
+                 fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
         torch.cuda.synchronize()
         tp_ms = (time.perf_counter() - t0) * 1e3 / K
+        tp_pass = event_ms()
+        tp_pass_mean = sum(tp_pass) / len(tp_pass)
         _, _, aux_tp = sv.spec_verify_top_p(copies[0].target, copies[0].draft,
                                             copies[0].draft_tokens, copies[0].draft_len,
                                             copies[0].temperature, tp, seed, aux=True)
@@ -481,11 +484,11 @@ def main() -> int:
                 "value": positions / (tp_ms * 1e-3), "unit": "positions/s", "ms_per_step": tp_ms,
                 "rows_filtered": t_rows + d_rows,
                 "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
-                "roofline": roof(alg_bytes / (tp_ms * 1e-3) / 1e9,
-                                 "the whole step (each row counted once; k_nucleus reads every "
-                                 "bf16 row once more)"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_rowstats", "k_nucleus",
-                                                              "k_draw")}
+                "row_pass_us_mean": tp_pass_mean * 1e3,
+                "roofline": roof(alg_bytes / (tp_pass_mean * 1e-3) / 1e9,
+                                 "the row pass (k_filter reads each filtered row once; "
+                                 "k_rowstats skips them), HIP events"),
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
@@ -497,7 +500,7 @@ def main() -> int:
                                                                                  np.float32)),
                 n_cpu * (w.k + 1), "positions/s",
                 f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-p")
-        log(f"[bench] top-p {tp_ms:.4f} ms/step")
+        log(f"[bench] top-p {tp_ms:.4f} ms/step; row pass {tp_pass_mean * 1e3:.1f} us")
     topk = None
     if not args.no_top_k:
         # The same batch with top-k 50 and then top-p 0.95 on every row.
@@ -513,9 +516,11 @@ def main() -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i, fn=fk)
+            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None, fn=fk)
         torch.cuda.synchronize()
         tk_ms = (time.perf_counter() - t0) * 1e3 / K
+        tk_pass = event_ms()
+        tk_pass_mean = sum(tk_pass) / len(tk_pass)
         _, _, aux_tk = sv.spec_verify_top_k_top_p(copies[0].target, copies[0].draft,
                                                   copies[0].draft_tokens, copies[0].draft_len,
                                                   copies[0].temperature, tk, tp, seed, aux=True)
@@ -524,11 +529,11 @@ def main() -> int:
                 "value": positions / (tk_ms * 1e-3), "unit": "positions/s", "ms_per_step": tk_ms,
                 "rows_filtered": t_rows + d_rows,
                 "sequences_ok": int((st == 0).sum()), "sequences_qzero": int((st == 4).sum()),
-                "roofline": roof(alg_bytes / (tk_ms * 1e-3) / 1e9,
-                                 "the whole step (each row counted once; k_nucleus reads every "
-                                 "bf16 row once more)"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_rowstats", "k_nucleus",
-                                                              "k_draw")}
+                "row_pass_us_mean": tk_pass_mean * 1e3,
+                "roofline": roof(alg_bytes / (tk_pass_mean * 1e-3) / 1e9,
+                                 "the row pass (k_filter reads each filtered row once; "
+                                 "k_rowstats skips them), HIP events"),
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
@@ -542,7 +547,7 @@ def main() -> int:
                 n_cpu * (w.k + 1), "positions/s",
                 f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-k "
                 "and top-p")
-        log(f"[bench] top-k + top-p {tk_ms:.4f} ms/step")
+        log(f"[bench] top-k + top-p {tk_ms:.4f} ms/step; row pass {tk_pass_mean * 1e3:.1f} us")
     tree = None
     if not args.no_tree:
         tree = bench_tree(hip, ev, K, W, not args.no_cpu_baseline)

@@ -109,10 +109,11 @@ typedef struct {
     int32_t *draw_row;   /* [B]: row of the last emitted token (= num_accepted), -1 on error */
     int32_t *draw_kind;  /* [B]: SPEC_DRAW_*                                               */
     void *event_begin;   /* hipEvent_t or NULL: recorded on `stream` right before the     */
-    void *event_end;     /* row-statistics kernel (the one that reads every logit row),   */
-                         /* and right after it; when B is split into several launch      */
-                         /* slices (B * (2k+1) * ceil(V*e / 32 KiB) > 2^22), around the  */
-                         /* first slice's                                                */
+    void *event_end;     /* row pass (the kernels that read every logit row: the row      */
+                         /* statistics, and with a filter the filter pass) and right      */
+                         /* after it; when B is split into several launch slices          */
+                         /* (B * (2k+1) * ceil(V*e / 32 KiB) > 2^22), around the first    */
+                         /* slice's                                                       */
 } spec_verify_aux_t;
 
 /* Bytes of scratch device memory one spec_verify or spec_verify_early_exit
@@ -204,9 +205,12 @@ int spec_verify_early_exit(const void *target_logits, const void *draft_logits, 
  * must not be NULL; everything else is as for spec_verify, with aux->q_g
  * and p_g the filtered probabilities and resid_mass the filtered mass.
  * The nucleus of a row is found exactly, with the row masses summed in
- * 64-bit fixed point: one more read of each filtered bf16 row (per-key
- * counts), or a radix select over the logits (fp32 rows, and bf16 rows
- * whose crossing falls outside the counted keys: two or three more reads).
+ * 64-bit fixed point. A filtered bf16 row is read once, by a pass that
+ * counts its tokens per bf16 value (in place of the row statistics); an
+ * fp32 row, and a bf16 row the counts cannot settle (its crossing among
+ * magnitudes below 2^-14 or below -2^18, a value at or above 2^18, a NaN,
+ * or more than 2048 nonzero magnitudes below 2^-14), takes a radix select
+ * over the logits: two or three more reads.
  */
 int spec_verify_top_p(const void *target_logits, const void *draft_logits, int32_t dtype,
                       const int32_t *draft_tokens, const int32_t *draft_len,
@@ -227,9 +231,9 @@ int spec_verify_top_p(const void *target_logits, const void *draft_logits, int32
  * pointer may be NULL (that filter is off) but not both; top_k is [B]
  * int32 and top_p [B] fp32 device memory. Statuses, outputs and
  * diagnostics are those of spec_verify_top_p, on the filtered rows. The
- * top-k threshold is found exactly from per-key counts (bf16 rows, when
- * the top_k-th token lies among the counted keys below the row max) or by
- * a radix select over the counts.
+ * top-k threshold is found exactly from the per-value counts of the same
+ * single pass (bf16 rows, when the top_k-th token has a magnitude in
+ * [2^-14, 2^18)) or by a radix select over the counts.
  */
 int spec_verify_top_k_top_p(const void *target_logits, const void *draft_logits, int32_t dtype,
                             const int32_t *draft_tokens, const int32_t *draft_len,

@@ -164,8 +164,12 @@ __device__ inline float exp2_fast(float x)
     return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
 
+// The row-statistics arithmetic is kept free of fused multiply-adds, so that
+// every kernel that inlines it rounds the same way: the same chunk gives the
+// same partial whichever kernel computes it.
 __device__ inline Soft soft_merge(Soft a, Soft b, float scale)
 {
+#pragma clang fp contract(off)
     const float m = fmaxf(a.m, b.m);
     if (m == -INFINITY)
         return {m, 0.f};
@@ -175,6 +179,7 @@ __device__ inline Soft soft_merge(Soft a, Soft b, float scale)
 template <int N>
 __device__ inline void soft_update(Soft &st, const float (&x)[N], float scale)
 {
+#pragma clang fp contract(off)
     float bm = x[0];
 #pragma unroll
     for (int j = 1; j < N; ++j)
@@ -277,14 +282,17 @@ struct RowShared {
 // ===========================================================================
 // Row statistics of one chunk: returns the block's partial in thread 0.
 // ===========================================================================
+// `tid` in [0, kThreads): the lane's index among the kThreads lanes that
+// share `sh` (two such groups may share a workgroup, calling in step: the
+// function's barriers are workgroup-wide).
 template <class D>
-__device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64_t s, int64_t e, bool greedy,
-                              float scale, RowShared &sh)
+__device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64_t s, int64_t e,
+                                              bool greedy, float scale, RowShared &sh,
+                                              int tid = (int)threadIdx.x)
 {
     constexpr int NX = kTiles * D::kVec;
     const Span sp = make_span<D>(row, s, e);
     const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
-    const int tid = threadIdx.x;
     const u32x4 pad = {D::kNegInfWord, D::kNegInfWord, D::kNegInfWord, D::kNegInfWord};
     float2 out = make_float2(0.f, 0.f);
 

@@ -74,7 +74,7 @@ __device__ inline uint64_t mass_target(uint64_t total, float top_p)
 }
 
 constexpr int kNucWaves = kNucThreads / kWave;
-constexpr int kNucTiles = 4;  // 16-byte loads in flight per thread (counting pass)
+constexpr int kNucTiles = 8;  // 16-byte loads in flight per thread (counting pass)
 
 struct RadixBins {
     unsigned long long hist[kBins];  // fixed-point mass per digit
@@ -432,7 +432,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
 #pragma unroll
         for (int u = 0; u < kNucTiles; ++u) {
             const int64_t vi = base + u * kNucThreads + tid;
-            r[u] = vi < sp.ngroups ? vrow[vi] : u32x4{0u, 0u, 0u, 0u};
+            r[u] = vi < sp.ngroups ? stream_load(vrow + vi) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kNucTiles; ++u)
@@ -467,14 +467,16 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     __syncthreads();
 }
 
-// One workgroup per bf16 row of every sampling sequence with a top-k or
-// top-p filter: the counting pass, then the thresholds from the counts (or,
-// when they cannot settle them, the radix passes). The row max goes out with
-// the result; k_rowstats does not read these rows.
+// One workgroup per row of a call with top-k or top-p parameters (bf16
+// logits), in place of k_rowstats. A row of a sampling sequence with a
+// filter: the counting pass, then the thresholds from the counts (or, when
+// they cannot settle them, the radix passes), with the row max. Any other
+// row: its row statistics.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
 {
     static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
+    static_assert(kNucThreads == 2 * kThreads, "two row-statistics groups per workgroup");
     using E = typename D::Elem;
     __shared__ NucleusShared sh;
     const int k = p.k, rows = 2 * k + 1;
@@ -484,20 +486,41 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
     const int tid = threadIdx.x;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
-    const float top_p = p.top_p ? p.top_p[b] : 1.f;
-    const int64_t top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
-    if (!valid_len(L, k) || !valid_temp(tau) || tau == 0.f || !(top_p > 0.f))
-        return;
-    const bool p_on = top_p < 1.f;
-    const bool k_on = top_k > 0 && top_k < (int64_t)p.V;
-    if (!p_on && !k_on)
-        return;
+    if (!valid_len(L, k) || !valid_temp(tau))
+        return;  // the decision reports the sequence
+    const bool greedy = tau == 0.f;
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
-    if (is_target ? i > L : i >= L)
-        return;
     const E *row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
                              : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
+    if (greedy || !seq_filtered(p, b)) {
+        // A row without a filter: its row statistics, as k_rowstats gives
+        // them, two chunks at a time (one per half of the workgroup).
+        if (is_target ? i > L : (greedy || i >= L))
+            return;
+        __shared__ RowShared half_sh[2];
+        constexpr int64_t CH = chunk_elems<D>();
+        const int half = tid / kThreads, ht = tid % kThreads;
+        const float scale = greedy ? 0.f : temp_scale(tau);
+        float2 *const part = p.partials + (b * rows + slot) * (int64_t)p.nc;
+        for (int c0 = 0; c0 < p.nc; c0 += 2) {
+            const int c = c0 + half;  // past the last chunk: an empty range
+            const int64_t s = min64((int64_t)c * CH, (int64_t)p.V);
+            const float2 v = chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy, scale,
+                                            half_sh[half], ht);
+            if (ht == 0 && c < p.nc)
+                part[c] = v;
+        }
+        return;
+    }
+    const float top_p = p.top_p ? p.top_p[b] : 1.f;
+    const int64_t top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
+    if (!(top_p > 0.f))
+        return;  // the decision reports the sequence
+    const bool p_on = top_p < 1.f;
+    const bool k_on = top_k > 0 && top_k < (int64_t)p.V;
+    if (is_target ? i > L : i >= L)
+        return;
     const float scale = temp_scale(tau);
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
     const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0

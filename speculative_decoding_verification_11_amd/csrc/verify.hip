@@ -16,8 +16,8 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Three or four launches per call (a filter adds k_nucleus before k_draw),
-// stream-ordered, no host synchronisation. Every hand-over between
+// Three or four launches per call (with a filter, k_filter replaces
+// k_rowstats for bf16 logits; k_nucleus follows it for fp32), stream-ordered, no host synchronisation. Every hand-over between
 // workgroups crosses a launch boundary, so no workgroup ever waits for
 // another and nothing needs device-scope atomics:
 //
@@ -27,6 +27,10 @@
 //               2^((x - max) * log2(e)/tau)) for sampling rows, (max logit,
 //               lowest index of it) for greedy rows. This kernel carries
 //               all of the algorithmic HBM traffic and runs at copy speed.
+//               With a top-k or top-p filter on bf16 logits, k_filter takes
+//               its place: one workgroup per row, reading each row once
+//               (the row statistics for rows without a filter, counts and
+//               thresholds for the others).
 //   k_decide    one wave per sequence: fold the partials in chunk order,
 //               gather p_i(g_i) and q_i(g_i), draw Philox, run the
 //               left-to-right test, write the accepted prefix, and record
@@ -618,8 +622,6 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
     if (!valid_len(L, k) || !valid_temp(tau))
         return;  // the decision reports the sequence
     const bool greedy = tau == 0.f;
-    if (D::kKeyBits == 16 && !greedy && seq_filtered(p, b))
-        return;  // a filtered bf16 row: k_filter reads it and finds its max
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
     if (is_target ? i > L : (greedy || i >= L))
@@ -765,23 +767,24 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         if (a.draw_kind) a.draw_kind += b0;
         p.n_row_items = nb * per_seq_items;
 
-        // The events bracket the row statistics (and, for early exit, the
-        // per-position decisions) of the first slice only.
+        // The events bracket the row pass (row statistics and filter pass;
+        // for early exit, the per-position decisions) of the first slice.
         if (ev_begin && b0 == 0 && hipEventRecord(ev_begin, stream) != hipSuccess)
             return SPEC_ELAUNCH;
         if (!early_exit) {
-            hipLaunchKernelGGL(k_rowstats<D>, dim3((unsigned)p.n_row_items), dim3(kThreads), 0,
-                               stream, p);
-            if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
-                return SPEC_ELAUNCH;
-            if (p.top_p || p.top_k) {
-                if constexpr (D::kKeyBits == 16)
-                    hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)),
-                                       dim3(kNucThreads), 0, stream, p);
-                else
+            const bool filters = p.top_p || p.top_k;
+            if (filters && D::kKeyBits == 16) {
+                hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads),
+                                   0, stream, p);
+            } else {
+                hipLaunchKernelGGL(k_rowstats<D>, dim3((unsigned)p.n_row_items), dim3(kThreads),
+                                   0, stream, p);
+                if (filters)
                     hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)),
                                        dim3(kNucThreads), 0, stream, p);
             }
+            if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
+                return SPEC_ELAUNCH;
             if (nb * nc <= kFoldDecisionItems)
                 p.decide_in_draw = 1;
             else
