@@ -93,7 +93,7 @@ constexpr int kSmallPos = kWinKeys / 2;
 constexpr int kOrderPos = kWinKeys + 1;
 constexpr int kSmallCap = 2048;  // listed values below 2^-14 (not zero) per row
 
-struct NucleusShared {
+struct alignas(16) NucleusShared {
     union {
         RadixBins rx;  // radix passes
         struct {
@@ -106,9 +106,15 @@ struct NucleusShared {
     int digit;
     float rs;  // row max
     // Counting pass: tokens below 2^-14 (listed), zeros, tokens at or below
-    // -2^18; 1 + the largest order key seen, of all and of the low ones; any
-    // NaN or value at or above 2^18.
+    // -2^18; the largest order key seen (+1 for the low ones); any NaN or
+    // value at or above 2^18.
     uint32_t n_small, n_zero, n_low, max_key, low_key, odd;
+    // Thresholds from the counts: the mass of the small values, the count
+    // and mass totals per wave, the kept mass of top-k, and whether the
+    // crossing fell where the counts cannot settle it.
+    unsigned long long small_mass, kept;
+    unsigned long long wcnt[kNucWaves];
+    uint32_t unsettled, found;
 };
 
 // Visits every element of row[0, V) as fp32 (16-byte loads where aligned).
@@ -364,9 +370,12 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     if (tid == 0) {
         sh.n_small = sh.n_zero = sh.n_low = 0;
         sh.max_key = sh.low_key = sh.odd = 0;
+        sh.small_mass = 0;
+        sh.unsettled = sh.found = 0;
     }
     __syncthreads();
-    uint32_t zeros = 0, lows = 0, low_key = 0, small_key = 0, odd = 0;
+    uint32_t zeros = 0, lows = 0, low_key = 0, odd = 0;
+    u16x2 kmax = (u16x2)0;  // largest order key, per 16-bit lane
     // A token outside the window (its count, if any, is taken back by the
     // caller).
     auto rare = [&](uint32_t r) {
@@ -377,7 +386,6 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
             const uint32_t i = atomicAdd(&sh.n_small, 1u);
             if (i < (uint32_t)kSmallCap)
                 sh.win.small[i] = (unsigned short)r;
-            small_key = max(small_key, bf16_key(r) + 1u);
         } else if ((r & 0x8000u) && u <= 0x7f80u) {  // at or below -2^18, -inf included
             ++lows;
             low_key = max(low_key, bf16_key(r) + 1u);
@@ -390,35 +398,45 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     // [0x8000, 0x9000) (negative), so bits 12..14 of t are zero exactly for
     // the window, and its entry is t's low 12 bits with the sign (bit 15)
     // moved to bit 12. Every token is counted at that entry; the few outside
-    // the window are taken back.
+    // the window are taken back afterwards (see below). Returns whether the
+    // group holds any.
     const uint32_t tb2 = kTinyBits * 0x10001u;
-    auto visit_group = [&](const u32x4 &g) {
+    auto visit_group = [&](const u32x4 &g) -> bool {
         const uint32_t w[4] = {g.x, g.y, g.z, g.w};
-        uint32_t t[4], e[4], any = 0;
+        uint32_t any = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            t[j] = as_u32(as_u16x2(w[j]) - as_u16x2(tb2));
-            e[j] = (t[j] & 0x0fff0fffu) |
-                   (as_u32(as_u16x2(t[j]) >> (unsigned short)3) & 0x10001000u);
-            any |= t[j];
+            const uint32_t t = as_u32(as_u16x2(w[j]) - as_u16x2(tb2));
+            const uint32_t e =
+                (t & 0x0fff0fffu) | (as_u32(as_u16x2(t) >> (unsigned short)3) & 0x10001000u);
+            any |= t;
+            // order key: positive r -> r | 0x8000, negative r -> ~r
+            const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
+            kmax = __builtin_elementwise_max(kmax, as_u16x2(w[j] ^ (neg | 0x80008000u)));
+            atomicAdd(&sh.win.cnt[e & 0xffffu], 1u);
+            atomicAdd(&sh.win.cnt[e >> 16], 1u);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            atomicAdd(&sh.win.cnt[e[j] & 0xffffu], 1u);
-            atomicAdd(&sh.win.cnt[e[j] >> 16], 1u);
-        }
-        if (any & 0x70007000u) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int sh16 = (j & 1) * 16;
-                if ((t[j >> 1] >> sh16) & 0x7000u) {
-                    atomicSub(&sh.win.cnt[(e[j >> 1] >> sh16) & 0xffffu], 1u);
-                    rare((w[j >> 1] >> sh16) & 0xffffu);
-                }
+        return (any & 0x70007000u) != 0;
+    };
+    // The tokens outside the window of one group, read again: their counts
+    // taken back, each handled by `rare` (one copy of this code, however
+    // many groups the loop unrolls).
+    auto visit_rare_group = [&](const u32x4 *gp) {
+        const u32x4 g = *gp;
+        const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t r = (w[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+            const uint32_t t = (r - kTinyBits) & 0xffffu;
+            if (t & 0x7000u) {
+                atomicSub(&sh.win.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
+                rare(r);
             }
         }
     };
     auto visit_one = [&](uint32_t r) {
+        const uint32_t neg = (r & 0x8000u) ? 0xffffu : 0u;
+        kmax = __builtin_elementwise_max(kmax, (u16x2)(unsigned short)(r ^ (neg | 0x8000u)));
         const uint32_t t = (r - kTinyBits) & 0xffffu;
         if (t & 0x7000u)
             rare(r);
@@ -434,10 +452,16 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
             const int64_t vi = base + u * kNucThreads + tid;
             r[u] = vi < sp.ngroups ? stream_load(vrow + vi) : u32x4{0u, 0u, 0u, 0u};
         }
+        uint32_t rare_groups = 0;  // bit u: group u holds tokens outside the window
 #pragma unroll
         for (int u = 0; u < kNucTiles; ++u)
-            if (base + u * kNucThreads + tid < sp.ngroups)
-                visit_group(r[u]);
+            if (base + u * kNucThreads + tid < sp.ngroups && visit_group(r[u]))
+                rare_groups |= 1u << u;
+        while (rare_groups) {
+            const int u = __builtin_ctz(rare_groups);
+            rare_groups &= rare_groups - 1;
+            visit_rare_group(vrow + base + u * kNucThreads + tid);
+        }
     }
     if (sp.s + tid < sp.a)
         visit_one((uint32_t)__builtin_bit_cast(unsigned short, row[sp.s + tid]));
@@ -451,14 +475,8 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     }
     if (odd)
         atomicOr(&sh.odd, 1u);
-    __syncthreads();
-    // 1 + the row max key: the largest counted entry, small value, zero or
-    // low value.
-    uint32_t mk = max(small_key, sh.n_zero ? 0x8001u : 0u);
-    mk = max(mk, sh.low_key);
-    for (int q = tid; q < kWinKeys; q += kNucThreads)
-        if (sh.win.cnt[q])
-            mk = max(mk, bf16_key(entry_bits((uint32_t)q)) + 1u);
+    // The row max key (-0 may stand for +0: the same value).
+    uint32_t mk = max((uint32_t)kmax.x, (uint32_t)kmax.y);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1)
         mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, kWave));
@@ -467,145 +485,286 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     __syncthreads();
 }
 
-// One workgroup per row of a call with top-k or top-p parameters (bf16
-// logits), in place of k_rowstats. A row of a sampling sequence with a
-// filter: the counting pass, then the thresholds from the counts (or, when
-// they cannot settle them, the radix passes), with the row max. Any other
-// row: its row statistics.
-template <class D>
-__global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
+// Window entries of thread t, 16 in value order: for t < 256 the positive
+// entries 4095 - 16t - j, for t >= 256 the negative entries 16t + j
+// (j = 0..15); the small values come after thread 255's.
+__device__ inline uint32_t own_entry(int t, int j)
 {
-    static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
-    static_assert(kNucThreads == 2 * kThreads, "two row-statistics groups per workgroup");
+    return t < kNucThreads / 2 ? (uint32_t)(kWinKeys / 2 - 1 - 16 * t - j) : (uint32_t)(16 * t + j);
+}
+
+// Inclusive block scan of one pair of sums per thread (counts, masses), in
+// thread order; returns the exclusive prefixes. wsum / wcnt hold the wave
+// totals afterwards.
+__device__ inline void scan_pair(uint64_t &c, uint64_t &m, NucleusShared &sh)
+{
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    uint64_t ic = c, im = m;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint64_t oc = __shfl_up(ic, off, kWave), om = __shfl_up(im, off, kWave);
+        if (lane >= off) {
+            ic += oc;
+            im += om;
+        }
+    }
+    if (lane == kWave - 1) {
+        sh.wcnt[wave] = ic;
+        sh.wsum[wave] = im;
+    }
+    __syncthreads();
+    uint64_t bc = 0, bm = 0;
+    for (int q = 0; q < wave; ++q) {
+        bc += sh.wcnt[q];
+        bm += sh.wsum[q];
+    }
+    c = bc + ic - c;
+    m = bm + im - m;
+}
+
+// Filter record flags (the record's fourth value), written by k_filter for
+// every row and read by k_filter_fallback: settled by the counts, or nothing
+// to do; radix passes needed, with the row max in the record; radix passes
+// needed after a pass for the row max (NaN or a value at or above 2^18);
+// the row statistics of a row without a filter.
+constexpr float kSettled = 0.f, kRadix = 1.f, kRadixMax = 2.f, kRowStats = 3.f;
+
+// Per-row set-up shared by k_filter and k_filter_fallback.
+template <class D>
+struct FilterRow {
+    const typename D::Elem *row;
+    float4 *out;
+    float tau, top_p;
+    int64_t top_k;
+    bool valid, greedy, filtered, needed, p_on, k_on;
+};
+
+template <class D>
+__device__ inline FilterRow<D> filter_row(const Params &p)
+{
     using E = typename D::Elem;
-    __shared__ NucleusShared sh;
     const int k = p.k, rows = 2 * k + 1;
     const int64_t rb = blockIdx.x;
     const int slot = (int)(rb % rows);
     const int64_t b = rb / rows;
-    const int tid = threadIdx.x;
     const int L = p.draft_len ? p.draft_len[b] : k;
-    const float tau = p.temperature[b];
-    if (!valid_len(L, k) || !valid_temp(tau))
-        return;  // the decision reports the sequence
-    const bool greedy = tau == 0.f;
+    FilterRow<D> f;
+    f.tau = p.temperature[b];
+    f.valid = valid_len(L, k) && valid_temp(f.tau);  // else the decision reports it
+    f.greedy = f.tau == 0.f;
+    f.filtered = f.valid && !f.greedy && seq_filtered(p, b);
+    f.top_p = p.top_p ? p.top_p[b] : 1.f;
+    f.top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
+    f.p_on = f.top_p < 1.f;
+    f.k_on = f.top_k > 0 && f.top_k < (int64_t)p.V;
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
-    const E *row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
-                             : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
-    if (greedy || !seq_filtered(p, b)) {
-        // A row without a filter: its row statistics, as k_rowstats gives
-        // them, two chunks at a time (one per half of the workgroup).
-        if (is_target ? i > L : (greedy || i >= L))
-            return;
-        __shared__ RowShared half_sh[2];
+    // A filtered row with top_p <= 0 or NaN is never read: the decision
+    // reports the sequence.
+    f.needed = f.valid && (is_target ? i <= L : (!f.greedy && i < L)) &&
+               (!f.filtered || f.top_p > 0.f);
+    f.row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
+                      : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
+    f.out = p.nucleus + b * rows + slot;
+    return f;
+}
+
+// One workgroup per row of a call with top-k or top-p parameters (bf16
+// logits), in place of k_rowstats: for a row of a sampling sequence with a
+// filter, the counting pass and the thresholds from the counts, with the
+// row max. What the counts cannot settle, and the rows without a filter,
+// are left to k_filter_fallback (kept apart so that this kernel's
+// registers hold its loop without spilling).
+template <class D>
+__global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
+{
+    static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
+    __shared__ NucleusShared sh;
+    const FilterRow<D> f = filter_row<D>(p);
+    const int tid = threadIdx.x;
+    if (!f.filtered || !f.needed) {
+        if (tid == 0)
+            *f.out = make_float4(0.f, 0.f, 0.f, f.needed ? kRowStats : kSettled);
+        return;
+    }
+    const bool p_on = f.p_on, k_on = f.k_on;
+    const int64_t top_k = f.top_k;
+    const float top_p = f.top_p;
+    const float scale = temp_scale(f.tau);
+    const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
+    float4 *const out = f.out;
+
+    count_row<D>(f.row, p.V, sh);
+    if (sh.odd) {  // NaN or a value at or above 2^18: the row max by a pass of its own
+        if (tid == 0)
+            *out = make_float4(0.f, 0.f, 0.f, kRadixMax);
+        return;
+    }
+    const float m = key_value<D>(sh.max_key);
+    auto fixed = [&](float x) {
+        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
+    };
+    const uint32_t n_small = sh.n_small, n_zero = sh.n_zero;
+    // Settled by the counts unless the list is full, or (top-p alone) the
+    // tokens below the window weigh something.
+    if (n_small <= (uint32_t)kSmallCap &&
+        (k_on || sh.n_low == 0 || fixed(key_value<D>(sh.low_key - 1u)) == 0)) {
+        // The small values: zeros weigh one amount, the listed ones each
+        // their own.
+        if (n_small + n_zero) {
+            uint64_t part = tid == 0 ? (uint64_t)n_zero * fixed(0.f) : 0;
+            for (uint32_t q = tid; q < n_small; q += kNucThreads)
+                part += fixed(__uint_as_float((uint32_t)sh.win.small[q] << 16));
+            if (part)
+                atomicAdd(&sh.small_mass, (unsigned long long)part);
+        }
+        // This thread's 16 entries: counts and masses.
+        constexpr int kOwn = kWinKeys / kNucThreads;
+        static_assert(kOwn == 16, "16 window entries per thread");
+        const bool upper = tid < kNucThreads / 2;
+        const uint32_t lo_entry = upper ? own_entry(tid, kOwn - 1) : own_entry(tid, 0);
+        uint32_t cnt[kOwn];
+#pragma unroll
+        for (int v = 0; v < kOwn / 4; ++v) {
+            const uint4 q4 = *reinterpret_cast<const uint4 *>(&sh.win.cnt[lo_entry + 4 * v]);
+            cnt[4 * v] = q4.x;
+            cnt[4 * v + 1] = q4.y;
+            cnt[4 * v + 2] = q4.z;
+            cnt[4 * v + 3] = q4.w;
+        }
+        // Count and mass of position j (value order); the owner of a
+        // crossing computes them again rather than keep 16 masses live.
+        auto count_of = [&](int j) -> uint32_t { return upper ? cnt[kOwn - 1 - j] : cnt[j]; };
+        auto mass_of = [&](int j) -> uint64_t {
+            const uint32_t n = count_of(j);
+            return n ? (uint64_t)n * fixed(entry_value(own_entry(tid, j))) : 0;
+        };
+        uint64_t csum = 0, msum = 0;
+#pragma unroll
+        for (int j = 0; j < kOwn; ++j) {
+            csum += count_of(j);
+            msum += mass_of(j);
+        }
+        const uint64_t small_count = (uint64_t)n_small + n_zero;
+        const bool last_upper = tid == kNucThreads / 2 - 1;
+        if (last_upper)
+            csum += small_count;
+        uint64_t ec = csum, em = msum;
+        scan_pair(ec, em, sh);  // exclusive prefixes; the barrier completes small_mass
+        const uint64_t small_mass = sh.small_mass;
+        if (!upper)
+            em += small_mass;
+        uint64_t tot_m = small_mass;
+        for (int q = 0; q < kNucWaves; ++q)
+            tot_m += sh.wsum[q];
+        uint64_t kept_total = tot_m;
+        if (k_on) {
+            // The top-k threshold: the position where the running count
+            // reaches top_k (position kOwn: thread 255's small values).
+            const uint64_t need = (uint64_t)top_k;
+            if (ec < need && need <= ec + csum) {
+                uint64_t cc = ec, cm = em, kept = 0;
+                int jk = kOwn;
+#pragma unroll
+                for (int j = 0; j < kOwn; ++j) {
+                    if (jk == kOwn) {
+                        cc += count_of(j);
+                        cm += mass_of(j);
+                        if (cc >= need) {
+                            jk = j;
+                            kept = cm;
+                        }
+                    }
+                }
+                if (jk == kOwn) {
+                    sh.unsettled = 1;
+                } else {
+                    sh.kept = kept;
+                    sh.found = 1;
+                    if (!p_on)
+                        *out = make_float4(entry_value(own_entry(tid, jk)), (float)kept / fscale,
+                                           m, 0.f);
+                }
+            }
+            __syncthreads();
+            if (sh.unsettled || !sh.found)
+                goto radix;  // the top_k-th token among the small or low values
+            if (!p_on)
+                return;  // top-k alone: written
+            kept_total = sh.kept;
+        }
+        {
+            // The nucleus: the position where the running mass reaches
+            // ceil(top_p * kept_total); with top-k it lies at or above the
+            // top-k threshold.
+            const uint64_t need = mass_target(kept_total, top_p);
+            const uint64_t own = msum + (last_upper ? small_mass : 0);
+            if (em < need && need <= em + own) {
+                uint64_t cm = em, kept = 0;
+                int jm = kOwn;
+#pragma unroll
+                for (int j = 0; j < kOwn; ++j) {
+                    if (jm == kOwn) {
+                        cm += mass_of(j);
+                        if (cm >= need) {
+                            jm = j;
+                            kept = cm;
+                        }
+                    }
+                }
+                if (jm == kOwn)
+                    sh.unsettled = 1;
+                else
+                    *out = make_float4(entry_value(own_entry(tid, jm)), (float)kept / fscale, m,
+                                       0.f);
+            }
+            __syncthreads();
+            if (!sh.unsettled)
+                return;
+        }
+    }
+radix:
+    if (tid == 0)
+        *out = make_float4(0.f, 0.f, m, kRadix);
+}
+
+// One workgroup per row of a call with top-k or top-p parameters (bf16
+// logits), after k_filter: the row statistics of the rows without a filter
+// (as k_rowstats gives them, two chunks at a time, one per half of the
+// workgroup), and the radix passes for the filtered rows k_filter flagged.
+template <class D>
+__global__ __launch_bounds__(kNucThreads, 6) void k_filter_fallback(Params p)
+{
+    static_assert(kNucThreads == 2 * kThreads, "two row-statistics groups per workgroup");
+    __shared__ NucleusShared sh;
+    __shared__ RowShared half_sh[2];
+    const float4 rec = p.nucleus[blockIdx.x];
+    if (rec.w == kSettled)
+        return;  // most rows: one read
+    const FilterRow<D> f = filter_row<D>(p);
+    const int tid = threadIdx.x;
+    if (rec.w == kRowStats) {
         constexpr int64_t CH = chunk_elems<D>();
         const int half = tid / kThreads, ht = tid % kThreads;
-        const float scale = greedy ? 0.f : temp_scale(tau);
-        float2 *const part = p.partials + (b * rows + slot) * (int64_t)p.nc;
+        const float scale = f.greedy ? 0.f : temp_scale(f.tau);
+        float2 *const part = p.partials + (int64_t)blockIdx.x * p.nc;
         for (int c0 = 0; c0 < p.nc; c0 += 2) {
             const int c = c0 + half;  // past the last chunk: an empty range
             const int64_t s = min64((int64_t)c * CH, (int64_t)p.V);
-            const float2 v = chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy, scale,
-                                            half_sh[half], ht);
+            const float2 v = chunk_stats<D>(f.row, s, min64((int64_t)p.V, s + CH), f.greedy,
+                                            scale, half_sh[half], ht);
             if (ht == 0 && c < p.nc)
                 part[c] = v;
         }
         return;
     }
-    const float top_p = p.top_p ? p.top_p[b] : 1.f;
-    const int64_t top_k = p.top_k ? (int64_t)p.top_k[b] : 0;
-    if (!(top_p > 0.f))
-        return;  // the decision reports the sequence
-    const bool p_on = top_p < 1.f;
-    const bool k_on = top_k > 0 && top_k < (int64_t)p.V;
-    if (is_target ? i > L : i >= L)
-        return;
-    const float scale = temp_scale(tau);
+    const float scale = temp_scale(f.tau);
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
     const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0
-    float4 *const out = p.nucleus + b * rows + slot;
-
-    count_row<D>(row, p.V, sh);
-    if (sh.odd) {  // NaN or a value at or above 2^18: the max by its own pass
-        const float m = row_max<D>(row, p.V, sh);
-        __syncthreads();
-        radix_filter<D>(row, p.V, m, scale, fscale, zlim, k_on, top_k, p_on, top_p, out, sh);
-        return;
-    }
-    const float m = key_value<D>(sh.max_key - 1u);
-    auto fixed = [&](float x) {
-        return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
-    };
-    const uint32_t n_small = sh.n_small, n_zero = sh.n_zero;
-    bool settled = n_small <= (uint32_t)kSmallCap;
-    if (settled) {
-        // The small values: zeros weigh one amount, the listed ones each
-        // their own.
-        uint64_t mine = tid == 0 ? (uint64_t)n_zero * fixed(0.f) : 0;
-        for (uint32_t q = tid; q < n_small; q += kNucThreads)
-            mine += fixed(__uint_as_float((uint32_t)sh.win.small[q] << 16));
-        const uint64_t small_mass = block_sum(mine, sh);
-        const uint64_t small_count = (uint64_t)n_small + n_zero;
-        int last = kOrderPos - 1;  // the nucleus is taken among positions [0, last]
-        auto count_at = [&](int q) -> uint64_t {
-            if (q >= kOrderPos)
-                return 0;
-            return q == kSmallPos ? small_count : sh.win.cnt[pos_entry(q)];
-        };
-        auto mass_at = [&](int q) -> uint64_t {
-            if (q > last)
-                return 0;
-            if (q == kSmallPos)
-                return small_mass;
-            const uint32_t e = pos_entry(q), n = sh.win.cnt[e];
-            return n ? (uint64_t)n * fixed(entry_value(e)) : 0;
-        };
-        constexpr int kPer = (kOrderPos + kNucThreads - 1) / kNucThreads;
-        uint64_t total = 0;
-        if (k_on) {
-            // The top-k threshold: the position where the running count
-            // reaches top_k.
-            crossing(kOrderPos, (uint64_t)top_k, count_at, sh);
-            const int dk = sh.digit;
-            settled = dk >= 0 && dk != kSmallPos;
-            if (settled) {
-                last = dk;
-                uint64_t kept = 0;
-                for (int q = 0; q < kPer; ++q)
-                    kept += mass_at(tid * kPer + q);
-                total = block_sum(kept, sh);
-                if (!p_on) {
-                    if (tid == 0)
-                        *out = make_float4(entry_value(pos_entry(dk)), (float)total / fscale, m,
-                                           0.f);
-                    return;
-                }
-            }
-        } else {
-            // Tokens at or below -2^18 lie below the window: they must weigh 0.
-            settled = sh.n_low == 0 || fixed(key_value<D>(sh.low_key - 1u)) == 0;
-            if (settled) {
-                uint64_t all = 0;
-                for (int q = 0; q < kPer; ++q)
-                    all += mass_at(tid * kPer + q);
-                total = block_sum(all, sh);
-            }
-        }
-        if (settled) {
-            crossing(kOrderPos, mass_target(total, top_p), mass_at, sh);
-            const int d = sh.digit;
-            settled = d >= 0 && d != kSmallPos;
-            if (settled) {
-                if (tid == 0)
-                    *out = make_float4(entry_value(pos_entry(d)),
-                                       (float)(sh.above + mass_at(d)) / fscale, m, 0.f);
-                return;
-            }
-        }
-    }
-    __syncthreads();  // the radix passes reuse the shared memory
-    radix_filter<D>(row, p.V, m, scale, fscale, zlim, k_on, top_k, p_on, top_p, out, sh);
+    const float m = rec.w == kRadixMax ? row_max<D>(f.row, p.V, sh) : rec.z;
+    __syncthreads();
+    radix_filter<D>(f.row, p.V, m, scale, fscale, zlim, f.k_on, f.top_k, f.p_on, f.top_p, f.out,
+                    sh);
 }
 
 // One workgroup per fp32 row of every sampling sequence with a top-k or
@@ -653,5 +812,6 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
 
 template __global__ void k_nucleus<F32>(Params p);
 template __global__ void k_filter<BF16>(Params p);
+template __global__ void k_filter_fallback<BF16>(Params p);
 
 }  // namespace spv

@@ -52,7 +52,7 @@ struct Params {
     double *segs;         // [B][nc][2][kSegs]: segment sums of w, then of p
     const float *top_p;   // [B] or null: nucleus parameter per sequence
     const int32_t *top_k; // [B] or null: top-k parameter per sequence
-    float4 *nucleus;      // [B][2k+1]: filtered rows (threshold logit, kept mass, row max, 0)
+    float4 *nucleus;      // [B][2k+1]: filtered rows (threshold logit, kept mass, row max, flag)
     int32_t fix_bits;     // top-p: fixed-point fraction bits of the row masses
     int32_t *ee_count;    // [k+2]: early exit: length of each position's list
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
@@ -71,11 +71,14 @@ __device__ inline bool seq_filtered(const Params &p, int64_t b)
            (p.top_k && p.top_k[b] > 0 && p.top_k[b] < p.V);
 }
 
-// Kernels defined in the other sources. k_filter: bf16 rows only.
+// Kernels defined in the other sources. k_filter, k_filter_fallback: bf16
+// rows only.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p);
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p);
+template <class D>
+__global__ __launch_bounds__(kNucThreads, 6) void k_filter_fallback(Params p);
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p);
 template <class D>

@@ -776,6 +776,8 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
             if (filters && D::kKeyBits == 16) {
                 hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads),
                                    0, stream, p);
+                hipLaunchKernelGGL(k_filter_fallback<D>, dim3((unsigned)(nb * rows)),
+                                   dim3(kNucThreads), 0, stream, p);
             } else {
                 hipLaunchKernelGGL(k_rowstats<D>, dim3((unsigned)p.n_row_items), dim3(kThreads),
                                    0, stream, p);
