@@ -93,27 +93,28 @@ constexpr int kSmallPos = kWinKeys / 2;
 constexpr int kOrderPos = kWinKeys + 1;
 constexpr int kSmallCap = 2048;  // listed values below 2^-14 (not zero) per row
 
-struct alignas(16) NucleusShared {
-    union {
-        RadixBins rx;  // radix passes
-        struct {
-            uint32_t cnt[kWinKeys];            // tokens per window entry
-            unsigned short small[kSmallCap];   // bits of the values below 2^-14
-        } win;
-    };
+// LDS of the radix passes (k_nucleus, k_filter_fallback).
+struct NucleusShared {
+    RadixBins rx;
     unsigned long long wsum[kNucWaves];
     unsigned long long above;
     int digit;
     float rs;  // row max
-    // Counting pass: tokens below 2^-14 (listed), zeros, tokens at or below
-    // -2^18; the largest order key seen (+1 for the low ones); any NaN or
-    // value at or above 2^18.
+};
+
+// LDS of the counting pass (k_filter).
+struct alignas(16) CountShared {
+    uint32_t cnt[kWinKeys];           // tokens per window entry
+    unsigned short small[kSmallCap];  // bits of the values below 2^-14
+    // Tokens below 2^-14 (listed), zeros, tokens at or below -2^18; the
+    // largest order key seen (+1 for the low ones); any NaN or value at or
+    // above 2^18.
     uint32_t n_small, n_zero, n_low, max_key, low_key, odd;
     // Thresholds from the counts: the mass of the small values, the count
     // and mass totals per wave, the kept mass of top-k, and whether the
     // crossing fell where the counts cannot settle it.
     unsigned long long small_mass, kept;
-    unsigned long long wcnt[kNucWaves];
+    unsigned long long wcnt[kNucWaves], wsum[kNucWaves];
     uint32_t unsettled, found;
 };
 
@@ -362,11 +363,11 @@ __device__ inline uint32_t pos_entry(int q)
 // the zeros and low values, and the row max key, all in sh.
 template <class D>
 __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V,
-                                          NucleusShared &sh)
+                                          CountShared &sh)
 {
     const int tid = threadIdx.x;
     for (int q = tid; q < kWinKeys; q += kNucThreads)
-        sh.win.cnt[q] = 0;
+        sh.cnt[q] = 0;
     if (tid == 0) {
         sh.n_small = sh.n_zero = sh.n_low = 0;
         sh.max_key = sh.low_key = sh.odd = 0;
@@ -385,7 +386,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
         } else if (u < kTinyBits) {
             const uint32_t i = atomicAdd(&sh.n_small, 1u);
             if (i < (uint32_t)kSmallCap)
-                sh.win.small[i] = (unsigned short)r;
+                sh.small[i] = (unsigned short)r;
         } else if ((r & 0x8000u) && u <= 0x7f80u) {  // at or below -2^18, -inf included
             ++lows;
             low_key = max(low_key, bf16_key(r) + 1u);
@@ -413,8 +414,8 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
             // order key: positive r -> r | 0x8000, negative r -> ~r
             const uint32_t neg = as_u32(__builtin_bit_cast(i16x2, w[j]) >> (i16x2)15);
             kmax = __builtin_elementwise_max(kmax, as_u16x2(w[j] ^ (neg | 0x80008000u)));
-            atomicAdd(&sh.win.cnt[e & 0xffffu], 1u);
-            atomicAdd(&sh.win.cnt[e >> 16], 1u);
+            atomicAdd(&sh.cnt[e & 0xffffu], 1u);
+            atomicAdd(&sh.cnt[e >> 16], 1u);
         }
         return (any & 0x70007000u) != 0;
     };
@@ -429,7 +430,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
             const uint32_t r = (w[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
             const uint32_t t = (r - kTinyBits) & 0xffffu;
             if (t & 0x7000u) {
-                atomicSub(&sh.win.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
+                atomicSub(&sh.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
                 rare(r);
             }
         }
@@ -441,7 +442,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
         if (t & 0x7000u)
             rare(r);
         else
-            atomicAdd(&sh.win.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
+            atomicAdd(&sh.cnt[(t & 0xfffu) | ((t >> 3) & 0x1000u)], 1u);
     };
     const Span sp = make_span<D>(row, 0, V);
     const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
@@ -496,7 +497,7 @@ __device__ inline uint32_t own_entry(int t, int j)
 // Inclusive block scan of one pair of sums per thread (counts, masses), in
 // thread order; returns the exclusive prefixes. wsum / wcnt hold the wave
 // totals afterwards.
-__device__ inline void scan_pair(uint64_t &c, uint64_t &m, NucleusShared &sh)
+__device__ inline void scan_pair(uint64_t &c, uint64_t &m, CountShared &sh)
 {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     uint64_t ic = c, im = m;
@@ -579,7 +580,7 @@ template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
 {
     static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
-    __shared__ NucleusShared sh;
+    __shared__ CountShared sh;
     const FilterRow<D> f = filter_row<D>(p);
     const int tid = threadIdx.x;
     if (!f.filtered || !f.needed) {
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
         if (n_small + n_zero) {
             uint64_t part = tid == 0 ? (uint64_t)n_zero * fixed(0.f) : 0;
             for (uint32_t q = tid; q < n_small; q += kNucThreads)
-                part += fixed(__uint_as_float((uint32_t)sh.win.small[q] << 16));
+                part += fixed(__uint_as_float((uint32_t)sh.small[q] << 16));
             if (part)
                 atomicAdd(&sh.small_mass, (unsigned long long)part);
         }
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
         uint32_t cnt[kOwn];
 #pragma unroll
         for (int v = 0; v < kOwn / 4; ++v) {
-            const uint4 q4 = *reinterpret_cast<const uint4 *>(&sh.win.cnt[lo_entry + 4 * v]);
+            const uint4 q4 = *reinterpret_cast<const uint4 *>(&sh.cnt[lo_entry + 4 * v]);
             cnt[4 * v] = q4.x;
             cnt[4 * v + 1] = q4.y;
             cnt[4 * v + 2] = q4.z;
