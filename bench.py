@@ -488,7 +488,7 @@ def main() -> int:
                 "roofline": roof(alg_bytes / (tp_pass_mean * 1e-3) / 1e9,
                                  "the row pass (k_filter reads each filtered row once; "
                                  "k_rowstats skips them), HIP events"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_draw")}
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback", "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
@@ -533,7 +533,7 @@ def main() -> int:
                 "roofline": roof(alg_bytes / (tk_pass_mean * 1e-3) / 1e9,
                                  "the row pass (k_filter reads each filtered row once; "
                                  "k_rowstats skips them), HIP events"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_draw")}
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback", "k_draw")}
         if not args.no_cpu_baseline:
             import oracle
             from oracle import parity
