@@ -250,6 +250,27 @@ def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
     return res
 
 
+LOOKUP_BLOCK = 512 * 8  # candidate ends per block of the backward scan (lanes x loads)
+
+
+def lookup_scanned_bytes(ctx, lens, lw) -> int:
+    """Context bytes the lookup must read: each context is scanned from its
+    end in blocks of LOOKUP_BLOCK candidate ends and stops after the block
+    holding the latest match of size n_max (whole context if there is none)."""
+    import torch
+    import speculative_decoding_verification_11_amd as sv
+
+    _, _, mn, ms = sv.spec_prompt_lookup(ctx, lens, lw.n_min, lw.n_max, lw.k, match=True)
+    T = lens.to(torch.int64).cpu()
+    n = mn.to(torch.int64).cpu()
+    end = ms.to(torch.int64).cpu() + n - 1  # latest end of the winning match
+    e_end = torch.clamp(T - 1, min=0)
+    full = n == lw.n_max
+    blocks = torch.div(e_end - 1 - end, LOOKUP_BLOCK, rounding_mode="floor") + 1
+    ends = torch.where(full, torch.minimum(e_end, blocks * LOOKUP_BLOCK), e_end)
+    return int(ends.sum()) * 4
+
+
 def bench_lookup(K: int, W: int, cpu: bool) -> dict:
     """Prompt-lookup drafting on workload p3: contexts per second and the
     kernel's bandwidth over the context tokens (one kernel per call, timed
@@ -282,13 +303,16 @@ def bench_lookup(K: int, W: int, cpu: bool) -> dict:
     k_list = [a.elapsed_time(b) for i, (a, b) in enumerate(evs) if sampled(i)]
     k_ms = sum(k_list) / len(k_list)
     nbytes = int(lens.to(torch.int64).sum()) * 4
+    scanned = lookup_scanned_bytes(ctx, lens, lw)
     ms_step = elapsed * 1e3 / K
     res = {"entry_point": "spec_prompt_lookup", "workload": f"{lw.name}: {lw.description}",
            "value": lw.B / (ms_step * 1e-3), "unit": "contexts/s", "ms_per_step": ms_step,
-           "context_bytes": nbytes, "kernel": "k_prompt_lookup", "kernel_us_mean": k_ms * 1e3,
-           "kernel_GBps": nbytes / (k_ms * 1e-3) / 1e9,
+           "context_bytes": nbytes, "scanned_bytes": scanned, "kernel": "k_prompt_lookup",
+           "kernel_us_mean": k_ms * 1e3, "kernel_GBps": scanned / (k_ms * 1e-3) / 1e9,
            "mean_draft_len": float(out[1].float().mean()),
-           "roofline": roof(nbytes / (k_ms * 1e-3) / 1e9, "k_prompt_lookup, torch events"),
+           "roofline": roof(scanned / (k_ms * 1e-3) / 1e9,
+                            "k_prompt_lookup over the context bytes it must scan (from the end "
+                            "back to the block holding the latest full-size match), torch events"),
            "hbm_bytes_per_dispatch": read_kernel_traffic("k_prompt_lookup")}
     if cpu:
         import oracle

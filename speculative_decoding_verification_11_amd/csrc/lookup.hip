@@ -18,17 +18,23 @@ using namespace spv;
 // lane finds m(e), the number of tokens ending at e that equal the
 // context's last tokens (capped at n_max). The answer is the largest
 // (min(m(e), n_max), e) with m(e) >= n_min: the largest size that matches
-// anywhere, then its latest end.
+// anywhere, then its latest end. The candidates are scanned from the end of
+// the context in blocks of kLookupBlock ends; once a block holds a match of
+// size n_max nothing earlier can win (same size, earlier end), so the scan
+// stops there, and a context that repeats itself is read only near its end.
 // ===========================================================================
-constexpr int kLookupUnroll = 16;  // context loads in flight per lane
+constexpr int kLookupThreads = 512;  // lanes per context
+constexpr int kLookupWaves = kLookupThreads / kWave;
+constexpr int kLookupUnroll = 8;     // context loads in flight per lane
+constexpr int kLookupBlock = kLookupThreads * kLookupUnroll;
 
-__global__ __launch_bounds__(kThreads) void k_prompt_lookup(
+__global__ __launch_bounds__(kLookupThreads) void k_prompt_lookup(
     const int32_t *__restrict__ contexts, const int32_t *__restrict__ ctx_len, int32_t T_max,
     int32_t n_min, int32_t n_max, int32_t k, int32_t *__restrict__ draft_tokens,
     int32_t *__restrict__ draft_len, int32_t *__restrict__ match_n,
     int32_t *__restrict__ match_start)
 {
-    __shared__ uint64_t best_w[kWaves];
+    __shared__ uint64_t best_w[kLookupWaves];
     __shared__ int32_t tail[kMaxNgram];  // tail[j] = ctx[T - 1 - j]
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -44,17 +50,18 @@ __global__ __launch_bounds__(kThreads) void k_prompt_lookup(
     // Candidate ends e in [0, T - 2]; key = (size << 32) | e, 0 = none.
     uint64_t key = 0;
     const int e_end = valid ? T - 1 : 0;
-    for (int base = 0; base < e_end; base += kThreads * kLookupUnroll) {
+    for (int hi = e_end; hi > 0; hi -= kLookupBlock) {
+        const int lo = hi - kLookupBlock;  // ends [max(lo, 0), hi)
         int32_t c[kLookupUnroll];
 #pragma unroll
         for (int u = 0; u < kLookupUnroll; ++u) {
-            const int e = base + u * kThreads + tid;
-            c[u] = e < e_end ? ctx[e] : 0;
+            const int e = lo + u * kLookupThreads + tid;
+            c[u] = e >= 0 ? ctx[e] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kLookupUnroll; ++u) {
-            const int e = base + u * kThreads + tid;
-            if (e < e_end && c[u] == last) {
+            const int e = lo + u * kLookupThreads + tid;
+            if (e >= 0 && c[u] == last) {
                 int m = 1;
                 const int cap = min(n_max, e + 1);
                 while (m < cap && ctx[e - m] == tail[m])
@@ -65,6 +72,8 @@ __global__ __launch_bounds__(kThreads) void k_prompt_lookup(
                 }
             }
         }
+        if (__syncthreads_or((int)(key >> 32) >= n_max))
+            break;  // a full-size match: nothing earlier can win
     }
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) {
@@ -76,13 +85,15 @@ __global__ __launch_bounds__(kThreads) void k_prompt_lookup(
     __syncthreads();
     key = best_w[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
+    for (int w = 1; w < kLookupWaves; ++w)
         key = best_w[w] > key ? best_w[w] : key;
 
-    const int n = (int)(key >> 32);
+    int n = (int)(key >> 32);
     const int e = (int)(uint32_t)key;
+    if (n < n_min || n > n_max || e < 0 || e >= T - 1)
+        n = 0;  // no match (a key only ever holds n in [n_min, n_max], e in [0, T - 2])
     const int len = n > 0 ? min(k, T - 1 - e) : 0;
-    for (int j = tid; j < k; j += kThreads)
+    for (int j = tid; j < k; j += kLookupThreads)
         draft_tokens[b * (int64_t)k + j] = j < len ? ctx[e + 1 + j] : -1;
     if (tid == 0) {
         draft_len[b] = len;
@@ -111,7 +122,7 @@ extern "C" int spec_prompt_lookup(const int32_t *contexts, const int32_t *contex
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int64_t b0 = 0; b0 < B; b0 += INT32_MAX / 2) {
         const int64_t nb = std::min<int64_t>((int64_t)B - b0, INT32_MAX / 2);
-        hipLaunchKernelGGL(k_prompt_lookup, dim3((unsigned)nb), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL(k_prompt_lookup, dim3((unsigned)nb), dim3(kLookupThreads), 0, st,
                            contexts ? contexts + b0 * T_max : nullptr, context_len + b0, T_max,
                            n_min, n_max, k, draft_tokens ? draft_tokens + b0 * k : nullptr,
                            draft_len + b0, match_n ? match_n + b0 : nullptr,

@@ -69,6 +69,54 @@ def test_lookup_degenerate_contexts():
     assert list(g["draft_len"]) == [1, 0, 1] and list(g["match_n"]) == [16, 0, 16]
 
 
+BLOCK = 512 * 8  # candidate ends per block of the kernel's backward scan
+
+
+def test_lookup_backward_scan_blocks():
+    """Long contexts scanned from the end in blocks of 4096 candidate ends,
+    stopping at the first block with a full-size match. Planted cases: the
+    only full-size match several blocks back behind shorter matches in the
+    last block; full-size matches in several blocks (the latest wins);
+    matches whose n-gram straddles a block boundary; ends exactly on the
+    boundaries; no full-size match at all, and one only at the context's
+    start (the whole context is scanned)."""
+    rng = np.random.default_rng(4242)
+    n_max, k, T = 6, 7, 5 * BLOCK + 123
+    tailg = [900001, 900002, 900003, 900004, 900005, 900006]  # the last n_max tokens
+    rows, lens = [], []
+
+    def plant(row, end, n):  # the last n tokens of the tail, ending at `end`
+        row[end - n + 1:end + 1] = tailg[n_max - n:]
+
+    e_end = T - 1
+    cases = [("only early", [(e_end - 3 * BLOCK - 17, 6), (e_end - 8, 4), (e_end - 100, 5)]),
+             ("several", [(e_end - 2 * BLOCK - 3, 6), (e_end - BLOCK - 9, 6), (e_end - 9, 3)]),
+             ("straddle", [(e_end - BLOCK + 2, 6)]),
+             ("on boundary", [(e_end - BLOCK, 6), (e_end - 2 * BLOCK + 40, 6)]),
+             ("past boundary", [(e_end - BLOCK - 1, 6)]),
+             ("no full size", [(e_end - 4 * BLOCK, 5), (e_end - 10, 2)]),
+             ("only at the start", [(5, 6), (e_end - 2 * BLOCK, 4)])]
+    for label, plants in cases:
+        row = rng.integers(0, 800000, size=T).astype(np.int32)
+        for end, n in plants:  # all clear of the context's own last n_max tokens
+            assert end <= T - 1 - n_max
+            plant(row, end, n)
+        row[-n_max:] = tailg
+        rows.append(row)
+        lens.append(T)
+    ctx = np.stack(rows)
+    lens = np.array(lens, np.int32)
+    print(f"[case] lookup backward scan {len(cases)} contexts T={T}", flush=True)
+    g = run_lookup(ctx, lens, 1, n_max, k)
+    r = oracle.spec_prompt_lookup_ref(ctx, lens, 1, n_max, k)
+    assert_same(g, r, "backward scan")
+    want = [e_end - 3 * BLOCK - 17, e_end - BLOCK - 9, e_end - BLOCK + 2, e_end - BLOCK,
+            e_end - BLOCK - 1, e_end - 4 * BLOCK, 5]
+    got_end = list(g["match_s"] + g["match_n"] - 1)
+    assert got_end == want, got_end
+    assert list(g["match_n"]) == [6, 6, 6, 6, 6, 5, 6]
+
+
 def test_lookup_rejects_bad_arguments():
     c = torch.zeros((2, 8), dtype=torch.int32, device=DEV)
     ln = torch.full((2,), 8, dtype=torch.int32, device=DEV)
