@@ -296,15 +296,28 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
     const u32x4 pad = {D::kNegInfWord, D::kNegInfWord, D::kNegInfWord, D::kNegInfWord};
     float2 out = make_float2(0.f, 0.f);
 
-    if (!greedy) {
-        Soft st{-INFINITY, 0.f};
-        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
-            u32x4 r[kTiles];
+    // A full block of kThreads * kTiles groups (every chunk but a row's last)
+    // loads without per-load masking; a partial one pads with -inf, which
+    // adds exact zeros to the sums and leaves the maxima alone.
+    auto load_block = [&](int64_t base, u32x4 (&r)[kTiles]) {
+        if (base + (int64_t)kThreads * kTiles <= sp.ngroups) {
+            const u32x4 *blk = vrow + base;  // uniform; 32-bit lane offsets below
+#pragma unroll
+            for (int u = 0; u < kTiles; ++u)
+                r[u] = stream_load(blk + (uint32_t)(u * kThreads + tid));
+        } else {
 #pragma unroll
             for (int u = 0; u < kTiles; ++u) {
                 const int64_t vi = base + u * kThreads + tid;
                 r[u] = vi < sp.ngroups ? stream_load(vrow + vi) : pad;
             }
+        }
+    };
+    if (!greedy) {
+        Soft st{-INFINITY, 0.f};
+        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
+            u32x4 r[kTiles];
+            load_block(base, r);
             float x[NX];
 #pragma unroll
             for (int u = 0; u < kTiles; ++u) {
@@ -346,11 +359,7 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
         }
         for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
             u32x4 r[kTiles];
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                const int64_t vi = base + u * kThreads + tid;
-                r[u] = vi < sp.ngroups ? stream_load(vrow + vi) : pad;
-            }
+            load_block(base, r);
 #pragma unroll
             for (int u = 0; u < kTiles; ++u) {
                 float f[D::kVec];
