@@ -13,11 +13,12 @@ namespace spv {
 // Decisions, draws and RNG are those of the full step; the diagnostics of
 // rows that are never read (p_g, q_g, argmax past the stop) stay NaN / -1.
 //
-// Position 0 has its own decision launch (which also validates the inputs
-// and clears the counters). From position 1 on, the workgroup that finishes
-// the last chunk of a sequence's rows at position i takes that sequence's
-// decision at once, and a sequence that accepts is appended to the list of
-// position i + 1, so each position's launch only streams listed sequences.
+// Position 0 has its own decision launch (one wave per sequence; it also
+// validates the inputs and clears the counters). From position 1 on, the
+// workgroup that finishes the last chunk of a sequence's rows at position i
+// takes that sequence's decision at once (its first wave), and a sequence
+// that accepts is appended to the list of position i + 1, so each
+// position's launch only streams listed sequences.
 // ===========================================================================
 
 // Exchange of partials inside one launch: device-scope (write-through)
@@ -49,18 +50,19 @@ __device__ inline int ee_items(int nc, bool greedy, int i, int L)
     return nc * (1 + (!greedy && i < L ? 1 : 0));
 }
 
-// Outputs of a sequence that stops at position j (one thread). The first
-// pq_set entries of p_g / q_g and the first am_set of argmax were written
-// position by position; the rest become NaN / -1. A draw's token is left
-// to k_locate.
+// Outputs of a sequence that stops at position j, written by one wave
+// (`lane` in [0, 64); k <= SPEC_MAX_K < 64, so lane x owns position x). The
+// first pq_set entries of p_g / q_g and the first am_set of argmax were
+// written position by position; the rest become NaN / -1. A draw's token is
+// left to k_locate.
 __device__ inline void ee_stop(const Params &p, int64_t b, int j, int status,
                                const Decision &dec, bool token_here, int token, int pq_set,
-                               int am_set)
+                               int am_set, int lane)
 {
-    const int k = p.k;
-    int32_t *out = p.out_tokens + b * (k + 1);
+    const int k = p.k, x = lane;
     const bool ok = status == SPEC_SEQ_OK;
-    for (int x = 0; x <= k; ++x) {
+    if (x <= k) {
+        int32_t *out = p.out_tokens + b * (k + 1);
         if (!ok || x > j)
             out[x] = -1;
         else if (x < j)
@@ -68,15 +70,16 @@ __device__ inline void ee_stop(const Params &p, int64_t b, int j, int status,
         else if (token_here)
             out[x] = token;
     }
-    p.num_accepted[b] = ok ? j : 0;
     const AuxDev &aux = p.aux;
-    for (int x = ok ? pq_set : 0; x < k; ++x) {
+    if (x < k && x >= (ok ? pq_set : 0)) {
         if (aux.p_g) aux.p_g[b * k + x] = NAN;
         if (aux.q_g) aux.q_g[b * k + x] = NAN;
     }
-    if (aux.argmax)
-        for (int x = ok ? am_set : 0; x <= k; ++x)
-            aux.argmax[b * (k + 1) + x] = -1;
+    if (aux.argmax && x <= k && x >= (ok ? am_set : 0))
+        aux.argmax[b * (k + 1) + x] = -1;
+    if (lane != 0)
+        return;
+    p.num_accepted[b] = ok ? j : 0;
     if (aux.seq_status) aux.seq_status[b] = status;
     if (aux.draw_row) aux.draw_row[b] = ok ? j : -1;
     if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS) {
@@ -86,13 +89,16 @@ __device__ inline void ee_stop(const Params &p, int64_t b, int j, int status,
     p.decisions[b] = dec;
 }
 
-// Decision of sequence b at position i (one thread): the same folds (chunk
-// order), gathers, Philox draws and tests as the full step's decision, for
-// one position. Returns true when the sequence accepts g_i and goes on to
-// position i + 1. `published`: the partials were written in this launch.
+// Decision of sequence b at position i, by one wave (the result is the same
+// in every lane): the same folds (chunk order), gathers, Philox draws and
+// tests as the full step's decision, for one position. Lanes load the
+// partials, and every lane folds them in chunk order, so the few memory
+// round trips overlap. Returns true when the sequence accepts g_i and goes
+// on to position i + 1. `published`: the partials were written in this
+// launch.
 template <class D>
 __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float tau,
-                                 bool published)
+                                 bool published, int lane)
 {
     using E = typename D::Elem;
     const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
@@ -102,58 +108,71 @@ __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float
     const E *target = static_cast<const E *>(p.target);
     const E *draft = static_cast<const E *>(p.draft);
     const float2 *pt = p.partials + (b * rows + i) * (int64_t)nc;
+    const float2 *pd = p.partials + (b * rows + k + 1 + i) * (int64_t)nc;
     const int g = i < L ? p.draft_tokens[b * k + i] : -1;
     if (tau == 0.f) {
         ArgMax acc{-INFINITY, INT32_MAX};
-        for (int c = 0; c < nc; ++c) {
-            const float2 t = partial(pt + c);
-            acc = argmax_merge(acc, ArgMax{t.x, __float_as_int(t.y)});
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane, n = min(kWave, nc - c0);
+            const float2 t =
+                c < nc ? partial(pt + c) : make_float2(-INFINITY, __int_as_float(INT32_MAX));
+            for (int q = 0; q < n; ++q)
+                acc = argmax_merge(acc, ArgMax{__shfl(t.x, q, kWave),
+                                               __float_as_int(__shfl(t.y, q, kWave))});
         }
-        if (p.aux.argmax) p.aux.argmax[b * (k + 1) + i] = acc.i;
+        if (lane == 0 && p.aux.argmax)
+            p.aux.argmax[b * (k + 1) + i] = acc.i;
         if (i < L && acc.i == g)
             return true;
         dec.row = i;
         dec.kind = SPEC_DRAW_GREEDY;
-        ee_stop(p, b, i, SPEC_SEQ_OK, dec, true, acc.i, 0, i + 1);
+        ee_stop(p, b, i, SPEC_SEQ_OK, dec, true, acc.i, 0, i + 1, lane);
         return false;
     }
     const float scale = temp_scale(tau);
+    const bool drafted = i < L;
+    float xt = 0.f, xd = 0.f;  // the two logits of g, loaded with the partials
+    if (drafted) {
+        xt = D::at(target + (b * (k + 1) + i) * (int64_t)V, g);
+        xd = D::at(draft + (b * k + i) * (int64_t)V, g);
+    }
     Soft ts{-INFINITY, 0.f}, ds{-INFINITY, 0.f};
-    for (int c = 0; c < nc; ++c) {
-        const float2 t = partial(pt + c);
-        ts = soft_merge(ts, Soft{t.x, t.y}, scale);
+    for (int c0 = 0; c0 < nc; c0 += kWave) {
+        const int c = c0 + lane, n = min(kWave, nc - c0);
+        const float2 t = c < nc ? partial(pt + c) : make_float2(-INFINITY, 0.f);
+        const float2 d = drafted && c < nc ? partial(pd + c) : make_float2(-INFINITY, 0.f);
+        for (int q = 0; q < n; ++q) {
+            ts = soft_merge(ts, Soft{__shfl(t.x, q, kWave), __shfl(t.y, q, kWave)}, scale);
+            if (drafted)
+                ds = soft_merge(ds, Soft{__shfl(d.x, q, kWave), __shfl(d.y, q, kWave)}, scale);
+        }
     }
     const uint4 w = philox4x32_10(make_uint4((uint32_t)i, p.seq_base + (uint32_t)b, 0u, 0u),
                                   p.key0, p.key1);
     const float u = uniform24(w.x), v = uniform24(w.y);
-    if (i < L) {
-        const float2 *pd = p.partials + (b * rows + k + 1 + i) * (int64_t)nc;
-        for (int c = 0; c < nc; ++c) {
-            const float2 t = partial(pd + c);
-            ds = soft_merge(ds, Soft{t.x, t.y}, scale);
-        }
-        const float xt = D::at(target + (b * (k + 1) + i) * (int64_t)V, g);
-        const float xd = D::at(draft + (b * k + i) * (int64_t)V, g);
+    if (drafted) {
         const float pg = exp2_fast((xt - ts.m) * scale) / ts.z;
         const float qg = exp2_fast((xd - ds.m) * scale) / ds.z;
         if (!(qg > 0.f)) {
-            ee_stop(p, b, i, SPEC_SEQ_QZERO, dec, false, 0, 0, 0);
+            ee_stop(p, b, i, SPEC_SEQ_QZERO, dec, false, 0, 0, 0, lane);
             return false;
         }
-        if (p.aux.p_g) p.aux.p_g[b * k + i] = pg;
-        if (p.aux.q_g) p.aux.q_g[b * k + i] = qg;
+        if (lane == 0) {
+            if (p.aux.p_g) p.aux.p_g[b * k + i] = pg;
+            if (p.aux.q_g) p.aux.q_g[b * k + i] = qg;
+        }
         if (u < fminf(1.f, pg / qg))
             return true;
     }
     dec.row = i;
-    dec.kind = i < L ? SPEC_DRAW_RESIDUAL : SPEC_DRAW_BONUS;
+    dec.kind = drafted ? SPEC_DRAW_RESIDUAL : SPEC_DRAW_BONUS;
     dec.v = v;
     dec.scale = scale;
     dec.mt = ts.m;
     dec.zt = ts.z;
     dec.md = ds.m;
     dec.zd = ds.z;
-    ee_stop(p, b, i, SPEC_SEQ_OK, dec, false, 0, i < L ? i + 1 : L, 0);
+    ee_stop(p, b, i, SPEC_SEQ_OK, dec, false, 0, drafted ? i + 1 : L, 0, lane);
     return false;
 }
 
@@ -198,60 +217,45 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
         p.partials[(b * rows + (slot == 0 ? 0 : k + 1)) * (int64_t)nc + c] = part;
 }
 
-// Appends b to position i's list (one atomic per wave).
-__device__ inline void ee_enlist(const Params &p, int64_t b, int i, bool go)
+// Appends b to position i's list (lane 0 of the deciding wave).
+__device__ inline void ee_enlist(const Params &p, int64_t b, int i)
 {
-    const uint64_t mask = __ballot(go);
-    if (!mask)
-        return;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int leader = __ffsll((unsigned long long)mask) - 1;
-    int base = 0;
-    if (lane == leader)
-        base = counter_add(p.ee_count + i, __popcll(mask));
-    base = __shfl(base, leader, kWave);
-    if (go) {
-        const int rank = __popcll(mask & ((1ull << lane) - 1));
-        p.ee_list[(int64_t)i * p.B + base + rank] = (int32_t)b;
-    }
+    const int at = counter_add(p.ee_count + i, 1);
+    p.ee_list[(int64_t)i * p.B + at] = (int32_t)b;
 }
 
-// Position 0's decisions, one thread per sequence; also validates the
-// inputs and clears the counters of the later positions.
+// Position 0's decisions, one wave per sequence; also validates the inputs
+// and clears the counters of the later positions.
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p)
 {
-    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const bool in = b < p.B;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
     const int k = p.k, V = p.V;
     if (blockIdx.x == 0 && threadIdx.x > 1 && threadIdx.x <= k + 1)
         p.ee_count[threadIdx.x] = 0;  // positions 2..k (and k + 1, never read)
-    bool go = false;
-    if (in) {
-        for (int i = 1; i <= k; ++i)
-            p.ee_done[(int64_t)i * p.B + b] = 0;
-        const int L = p.draft_len ? p.draft_len[b] : k;
-        const float tau = p.temperature[b];
-        int status = SPEC_SEQ_OK;
-        if (!valid_len(L, k)) {
-            status = SPEC_SEQ_BAD_LEN;
-        } else if (!valid_temp(tau)) {
-            status = SPEC_SEQ_BAD_TEMP;
-        } else {
-            for (int x = 0; x < L; ++x) {
-                const int g = p.draft_tokens[b * k + x];
-                if (g < 0 || g >= V)
-                    status = SPEC_SEQ_BAD_TOKEN;
-            }
-        }
-        if (status != SPEC_SEQ_OK) {
-            const Decision dec = no_decision();
-            ee_stop(p, b, 0, status, dec, false, 0, 0, 0);
-        } else {
-            go = ee_decide<D>(p, b, 0, L, tau, false);
-        }
+    if (b >= p.B)
+        return;
+    if (lane >= 1 && lane <= k)
+        p.ee_done[(int64_t)lane * p.B + b] = 0;
+    const int L = p.draft_len ? p.draft_len[b] : k;
+    const float tau = p.temperature[b];
+    int status = SPEC_SEQ_OK;
+    if (!valid_len(L, k)) {
+        status = SPEC_SEQ_BAD_LEN;
+    } else if (!valid_temp(tau)) {
+        status = SPEC_SEQ_BAD_TEMP;
+    } else {
+        const int g = lane < L ? p.draft_tokens[b * k + lane] : 0;
+        if (__any(lane < L && (g < 0 || g >= V)))
+            status = SPEC_SEQ_BAD_TOKEN;
     }
-    ee_enlist(p, b, 1, go);
+    if (status != SPEC_SEQ_OK) {
+        ee_stop(p, b, 0, status, no_decision(), false, 0, 0, 0, lane);
+        return;
+    }
+    if (ee_decide<D>(p, b, 0, L, tau, false, lane) && lane == 0)
+        ee_enlist(p, b, 1);
 }
 
 // Position i >= 1: the sequences on position i's list. The workgroup that
@@ -273,17 +277,22 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
     if (slot == 1 && (tau == 0.f || i >= L))
         return;
     const float2 part = ee_chunk<D>(p, b, slot, c, i, tau, sh);
-    if (threadIdx.x != 0)
+    if (threadIdx.x >= kWave)
         return;
-    publish_float2(p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc + c, part);
-    drain_stores();  // the partial is visible before the count
-    const int items = ee_items(nc, tau == 0.f, i, L);
-    if (counter_add(p.ee_done + (int64_t)i * p.B + b, 1) != items - 1)
-        return;
-    if (ee_decide<D>(p, b, i, L, tau, true) && i < k) {
-        const int at = counter_add(p.ee_count + i + 1, 1);
-        p.ee_list[(int64_t)(i + 1) * p.B + at] = (int32_t)b;
+    const int lane = threadIdx.x;
+    int last = 0;
+    if (lane == 0) {
+        publish_float2(p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc + c,
+                       part);
+        drain_stores();  // the partial is visible before the count
+        const int items = ee_items(nc, tau == 0.f, i, L);
+        last = counter_add(p.ee_done + (int64_t)i * p.B + b, 1) == items - 1;
     }
+    if (!__shfl(last, 0, kWave))
+        return;
+    // The last chunk of the sequence's rows: the first wave decides.
+    if (ee_decide<D>(p, b, i, L, tau, true, lane) && i < k && lane == 0)
+        ee_enlist(p, b, i + 1);
 }
 
 // Positions P..k in one launch: every remaining row (target rows P..L,
@@ -312,17 +321,25 @@ __global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
     if (is_target ? i > L : (greedy || i >= L))
         return;
     const float2 part = ee_chunk<D>(p, b, is_target ? 0 : 1, c, i, tau, sh);
-    if (threadIdx.x != 0)
+    if (threadIdx.x >= kWave)
         return;
-    publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c, part);
-    drain_stores();  // the partial is visible before the count
-    int items = 0;
-    for (int x = P; x <= L; ++x)
-        items += ee_items(nc, greedy, x, L);
-    if (counter_add(p.ee_done + (int64_t)P * p.B + b, 1) != items - 1)
+    const int lane = threadIdx.x;
+    int last = 0;
+    if (lane == 0) {
+        publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c,
+                       part);
+        drain_stores();  // the partial is visible before the count
+        int items = 0;
+        for (int x = P; x <= L; ++x)
+            items += ee_items(nc, greedy, x, L);
+        last = counter_add(p.ee_done + (int64_t)P * p.B + b, 1) == items - 1;
+    }
+    if (!__shfl(last, 0, kWave))
         return;
+    // The last chunk of the sequence's rows: the first wave decides
+    // positions P, P + 1, ... up to the stop.
     for (int x = P; x <= L; ++x)
-        if (!ee_decide<D>(p, b, x, L, tau, true))
+        if (!ee_decide<D>(p, b, x, L, tau, true, lane))
             break;
 }
 

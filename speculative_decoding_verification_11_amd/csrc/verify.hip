@@ -795,7 +795,7 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         } else {
             hipLaunchKernelGGL(k_ee_rowstats0<D>, dim3((unsigned)(nb * 2 * nc)), dim3(kThreads),
                                0, stream, p);
-            hipLaunchKernelGGL(k_ee_decide0<D>, dim3((unsigned)((nb + kThreads - 1) / kThreads)),
+            hipLaunchKernelGGL(k_ee_decide0<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
                                dim3(kThreads), 0, stream, p);
             const int P = std::min(k + 1, kEarlyExitSingle);
             for (int i = 1; i < P; ++i)
