@@ -38,7 +38,7 @@ constexpr int kMaxNgram = SPEC_MAX_NGRAM;
 constexpr int kFoldBatch = 8;       // partial loads in flight per lane when folding
 constexpr int kDeviceVersion = 300;  // 0.3.0
 // Early exit: positions below this one get a launch each; the rest share one.
-constexpr int kEarlyExitSingle = 3;
+constexpr int kEarlyExitSingle = 4;
 // Draw grids up to this many workgroups (about 16 per CU) take their
 // decisions inside k_draw; larger ones get a k_decide launch first.
 constexpr int64_t kFoldDecisionItems = 4096;
