@@ -173,12 +173,16 @@ int spec_verify(const void *target_logits, const void *draft_logits, int32_t dty
  * inputs, seed and seq_base. The diagnostics of rows that are never read
  * differ: p_g and q_g are written only for positions up to the stop (and
  * are NaN after it), argmax only for greedy rows up to the stop (-1 after
- * it). Enqueues k + 4 kernels (one row-statistics launch per position, in
- * which the workgroup that completes a sequence's rows also decides it);
- * event_begin / event_end bracket the per-position launches.
- * Pays when rejections come early (few accepted tokens per round): it reads
- * about (1 - a^L) / (1 - a) positions per sequence instead of L + 1, at a
- * per-token acceptance rate a.
+ * it). Enqueues at most 8 kernels, whatever k: one row-statistics launch
+ * for each of positions 0..3, a decision launch after position 0 (from
+ * position 1 on, the workgroup that completes a sequence's rows decides
+ * it), one launch for all positions from 4 on (every remaining row of the
+ * sequences still accepting at position 4, read even past a later stop),
+ * and the draw (two launches). event_begin / event_end bracket the
+ * position launches.
+ * Pays when rejections come early (few accepted tokens per round): up to
+ * position 4 it reads about (1 - a^L) / (1 - a) positions per sequence
+ * instead of L + 1, at a per-token acceptance rate a.
  */
 int spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
                            const int32_t *draft_tokens, const int32_t *draft_len,
