@@ -109,13 +109,18 @@ struct alignas(16) CountShared {
     // Tokens below 2^-14 (listed), zeros, tokens at or below -2^18; the
     // largest order key seen (+1 for the low ones); any NaN or value at or
     // above 2^18.
-    uint32_t n_small, n_zero, n_low, max_key, low_key, odd;
+    uint32_t n_small, n_zero, n_low, max_key, low_key, low_min, odd;
     // Thresholds from the counts: the mass of the small values, the count
     // and mass totals per wave, the kept mass of top-k, and whether the
     // crossing fell where the counts cannot settle it.
     unsigned long long small_mass, kept;
     unsigned long long wcnt[kNucWaves], wsum[kNucWaves];
-    uint32_t unsettled, found;
+    uint32_t found;
+    // A crossing among the small values or the low ones: where (kSmall,
+    // kLow; top-k, then the nucleus), the count and mass before the small
+    // values, the level found.
+    uint32_t where, where_p, level_key;
+    unsigned long long before_c, before_m;
 };
 
 // Visits every element of row[0, V) as fp32 (16-byte loads where aligned).
@@ -371,11 +376,14 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     if (tid == 0) {
         sh.n_small = sh.n_zero = sh.n_low = 0;
         sh.max_key = sh.low_key = sh.odd = 0;
+        sh.low_min = 0xffffffffu;
         sh.small_mass = 0;
-        sh.unsettled = sh.found = 0;
+        sh.found = 0;
+        sh.where = sh.where_p = 0;
+        sh.level_key = 0;
     }
     __syncthreads();
-    uint32_t zeros = 0, lows = 0, low_key = 0, odd = 0;
+    uint32_t zeros = 0, lows = 0, low_key = 0, low_min = 0xffffffffu, odd = 0;
     u16x2 kmax = (u16x2)0;  // largest order key, per 16-bit lane
     // A token outside the window (its count, if any, is taken back by the
     // caller).
@@ -390,6 +398,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
         } else if ((r & 0x8000u) && u <= 0x7f80u) {  // at or below -2^18, -inf included
             ++lows;
             low_key = max(low_key, bf16_key(r) + 1u);
+            low_min = min(low_min, bf16_key(r) + 1u);
         } else {
             odd = 1;  // at or above 2^18, or NaN
         }
@@ -473,6 +482,7 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     if (lows) {
         atomicAdd(&sh.n_low, lows);
         atomicMax(&sh.low_key, low_key);
+        atomicMin(&sh.low_min, low_min);
     }
     if (odd)
         atomicOr(&sh.odd, 1u);
@@ -484,6 +494,26 @@ __device__ __forceinline__ void count_row(const typename D::Elem *row, int64_t V
     if ((tid & (kWave - 1)) == 0)
         atomicMax(&sh.max_key, mk);
     __syncthreads();
+}
+
+// Where a crossing fell when it is not in the window (CountShared::where).
+constexpr uint32_t kSmall = 1, kLow = 2;
+
+// Sum over the workgroup of one value per thread.
+__device__ inline uint64_t block_sum(uint64_t v, CountShared &sh)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    __syncthreads();  // wsum is free
+    if (lane == 0)
+        sh.wsum[wave] = v;
+    __syncthreads();
+    uint64_t t = 0;
+    for (int q = 0; q < kNucWaves; ++q)
+        t += sh.wsum[q];
+    return t;
 }
 
 // Window entries of thread t, 16 in value order: for t < 256 the positive
@@ -605,11 +635,16 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
     auto fixed = [&](float x) {
         return (unsigned long long)(exp2_fast((x - m) * scale) * fscale);
     };
-    const uint32_t n_small = sh.n_small, n_zero = sh.n_zero;
+    const uint32_t n_small = sh.n_small, n_zero = sh.n_zero, n_low = sh.n_low;
+    // The tokens at or below -2^18: one level (all equal, as masked tokens
+    // usually are) or several; the weight of the largest of them.
+    const bool low_one = n_low == 0 || sh.low_min == sh.low_key;
+    const float low_val = n_low ? key_value<D>(sh.low_key - 1u) : 0.f;
+    const uint64_t low_w = n_low ? fixed(low_val) : 0;
+    const uint64_t low_mass = low_one ? (uint64_t)n_low * low_w : 0;
     // Settled by the counts unless the list is full, or (top-p alone) the
-    // tokens below the window weigh something.
-    if (n_small <= (uint32_t)kSmallCap &&
-        (k_on || sh.n_low == 0 || fixed(key_value<D>(sh.low_key - 1u)) == 0)) {
+    // low tokens weigh something and hold several levels.
+    if (n_small <= (uint32_t)kSmallCap && (k_on || low_one || low_w == 0)) {
         // The small values: zeros weigh one amount, the listed ones each
         // their own.
         if (n_small + n_zero) {
@@ -655,13 +690,58 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
         const uint64_t small_mass = sh.small_mass;
         if (!upper)
             em += small_mass;
-        uint64_t tot_m = small_mass;
-        for (int q = 0; q < kNucWaves; ++q)
+        uint64_t tot_m = small_mass, tot_c = 0;  // window and small values
+        for (int q = 0; q < kNucWaves; ++q) {
             tot_m += sh.wsum[q];
-        uint64_t kept_total = tot_m;
+            tot_c += sh.wcnt[q];
+        }
+        // A crossing among the small values: the workgroup ranks the listed
+        // values (and the zeros, one level) by their order key and finds the
+        // level where the running count or mass, from the largest, reaches
+        // `need` (counted from the first small value). The window counts
+        // are no longer read, so their LDS holds the listed values' masses.
+        auto small_level = [&](bool by_count, uint64_t need) -> uint32_t {
+            uint64_t *const smass = reinterpret_cast<uint64_t *>(sh.cnt);
+            if (!by_count)
+                for (uint32_t q = tid; q < n_small; q += kNucThreads)
+                    smass[q] = fixed(__uint_as_float((uint32_t)sh.small[q] << 16));
+            if (tid == 0)
+                sh.level_key = 0;
+            __syncthreads();
+            const uint64_t zero_amt = by_count ? n_zero : (uint64_t)n_zero * fixed(0.f);
+            for (uint32_t q = tid; q < n_small + (n_zero ? 1u : 0u); q += kNucThreads) {
+                const uint32_t key = q < n_small ? bf16_key(sh.small[q]) : 0x8000u;
+                uint64_t gt = n_zero && 0x8000u > key ? zero_amt : 0;
+                uint64_t eq = q == n_small ? zero_amt : 0;
+                for (uint32_t j = 0; j < n_small; ++j) {
+                    const uint32_t kj = bf16_key(sh.small[j]);
+                    const uint64_t amt = by_count ? 1u : smass[j];
+                    gt += kj > key ? amt : 0;
+                    eq += kj == key ? amt : 0;
+                }
+                if (gt < need && need <= gt + eq)
+                    atomicMax(&sh.level_key, key + 1u);  // every value of the level agrees
+            }
+            __syncthreads();
+            return sh.level_key - 1u;
+        };
+        // The mass of the small values at or above order key `key`.
+        auto small_mass_from = [&](uint32_t key) -> uint64_t {
+            uint64_t part = tid == 0 && n_zero && 0x8000u >= key ? (uint64_t)n_zero * fixed(0.f) : 0;
+            for (uint32_t q = tid; q < n_small; q += kNucThreads)
+                if (bf16_key(sh.small[q]) >= key)
+                    part += fixed(__uint_as_float((uint32_t)sh.small[q] << 16));
+            return block_sum(part, sh);
+        };
+        auto result = [&](float thr, uint64_t kept) {
+            if (tid == 0)
+                *out = make_float4(thr, (float)kept / fscale, m, 0.f);
+        };
+        uint64_t kept_total = tot_m + low_mass;  // top-p alone: the whole row
         if (k_on) {
             // The top-k threshold: the position where the running count
-            // reaches top_k (position kOwn: thread 255's small values).
+            // reaches top_k (position kOwn: thread 255's small values;
+            // beyond the window and the small values: the low ones).
             const uint64_t need = (uint64_t)top_k;
             if (ec < need && need <= ec + csum) {
                 uint64_t cc = ec, cm = em, kept = 0;
@@ -678,7 +758,9 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
                     }
                 }
                 if (jk == kOwn) {
-                    sh.unsettled = 1;
+                    sh.where = kSmall;
+                    sh.before_c = cc;  // the count and mass before the small values
+                    sh.before_m = cm;
                 } else {
                     sh.kept = kept;
                     sh.found = 1;
@@ -687,12 +769,32 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
                                            m, 0.f);
                 }
             }
+            if (tid == 0 && tot_c < need)
+                sh.where = kLow;
             __syncthreads();
-            if (sh.unsettled || !sh.found)
-                goto radix;  // the top_k-th token among the small or low values
-            if (!p_on)
-                return;  // top-k alone: written
-            kept_total = sh.kept;
+            const uint32_t where = sh.where;
+            if (where == kSmall) {
+                const uint32_t key = small_level(true, need - sh.before_c);
+                kept_total = sh.before_m + small_mass_from(key);
+                if (!p_on) {
+                    result(key_value<D>(key), kept_total);
+                    return;
+                }
+            } else if (where == kLow) {
+                if (!low_one)
+                    goto radix;  // the top_k-th token among several low levels
+                kept_total = tot_m + low_mass;
+                if (!p_on) {
+                    result(low_val, kept_total);
+                    return;
+                }
+            } else {
+                if (!sh.found)
+                    goto radix;  // no crossing: cannot happen, kept for safety
+                if (!p_on)
+                    return;  // top-k alone: written by the owner
+                kept_total = sh.kept;
+            }
         }
         {
             // The nucleus: the position where the running mass reaches
@@ -713,15 +815,30 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
                         }
                     }
                 }
-                if (jm == kOwn)
-                    sh.unsettled = 1;
-                else
+                if (jm == kOwn) {
+                    sh.where_p = kSmall;
+                    sh.before_m = cm;  // the mass before the small values
+                } else {
                     *out = make_float4(entry_value(own_entry(tid, jm)), (float)kept / fscale, m,
                                        0.f);
+                }
             }
+            if (tid == 0 && tot_m < need)
+                sh.where_p = kLow;  // only when the low tokens weigh something
             __syncthreads();
-            if (!sh.unsettled)
+            const uint32_t where = sh.where_p;
+            if (where == kSmall) {
+                const uint32_t key = small_level(false, need - sh.before_m);
+                result(key_value<D>(key), sh.before_m + small_mass_from(key));
                 return;
+            }
+            if (where == kLow) {
+                if (!low_one)
+                    goto radix;
+                result(low_val, tot_m + low_mass);
+                return;
+            }
+            return;  // written by the owner
         }
     }
 radix:

@@ -220,6 +220,34 @@ def test_top_k_masked_rows_bf16():
         check(total, "top-k masked")
 
 
+def test_top_k_among_several_low_levels_bf16():
+    """Masked tokens at two values (-3e38 and -1e30, both below -2^18):
+    top_k ending among them cannot be settled from one low level and goes
+    through the radix passes; ending above them settles from the counts."""
+    rng = np.random.default_rng(35)
+    B, k, V = 6, 1, 20000
+    t = np.empty((B, k + 1, V), np.uint16)
+    d = np.empty((B, k, V), np.uint16)
+    for b in range(B):
+        lv = [(_bf16(2.0), 5), (_bf16(1.0), 40), (_bf16(-1e30), 3000), (_bf16(-3e38), 0)]
+        for i in range(k + 1):
+            t[b, i] = _shuffled(rng, V, lv)
+        for i in range(k):
+            d[b, i] = _shuffled(rng, V, lv)
+    g = bf16_to_f32(d).argmax(axis=2).astype(np.int32)
+    L = np.full(B, k, np.int32)
+    tau = np.full(B, 0.8, np.float32)
+    cb = raw_batch(t, d, g, L, tau)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    top_k = np.array([3, 45, 46, 2000, 4000, 12000], np.int32)
+    for top_p in (None, np.full(B, 0.9, np.float32)):
+        say(f"[case] top-k several low levels top_p={top_p is not None}")
+        g_ = run_tk(gb, 41, top_k, top_p)
+        r = parity.oracle_on(h, 41, top_k=top_k, top_p=top_p)
+        check(parity.compare(g_, r, L, tau, k), "top-k low levels")
+
+
 def _shuffled(rng, V, levels):
     r = np.full(V, levels[-1][0], np.uint16)
     at = 0

@@ -271,6 +271,22 @@ def test_top_p_window_edges_bf16(extra):
     _run_levels(t, d, tau, top_p, f"window edges {extra}")
 
 
+def test_top_p_weighty_low_levels_bf16():
+    """Two levels below -2^18 (-2^18 and -2^19) that weigh something at a
+    temperature of 1e6: the nucleus cannot be settled from one low level and
+    goes through the radix passes; with one such level it settles."""
+    rng = np.random.default_rng(61)
+    B, k, V = 6, 1, 4096
+    lo1, lo2 = _EDGE["-2^18"], 0x8000 | (_WIN_TOP + 128)  # -2^18 and -2^19
+    two = [(_bf16(1.0), 1000), (_bf16(-1.0), 1000), (lo1, 1000), (lo2, 0)]
+    one = [(_bf16(1.0), 1000), (_bf16(-1.0), 1000), (lo1, 0)]
+    t = np.concatenate([_level_rows(rng, 3, k + 1, V, two), _level_rows(rng, 3, k + 1, V, one)])
+    d = np.concatenate([_level_rows(rng, 3, k, V, two), _level_rows(rng, 3, k, V, one)])
+    tau = np.full(B, 1e6, np.float32)
+    top_p = np.array([0.4, 0.8, 0.97, 0.4, 0.7, 0.9], np.float32)
+    _run_levels(t, d, tau, top_p, "weighty low levels")
+
+
 def test_top_p_masked_rows_bf16():
     """Most of each row masked to -inf (no weight, counted apart) or to -3e38,
     the rest a few levels; crossings on each level."""
