@@ -207,8 +207,9 @@ def test_top_k_masked_rows_bf16():
     cb = raw_batch(t, d, g, L, tau)
     gb = batch_to(cb, DEV)
     h = host(cb)
-    # 1 and 20: window levels; 40 and 60: the zeros; 90: the small values;
-    # 200: -0.5; 500 and 5000: among the masked tokens
+    # levels from the top: 4.0 (3), 2.0 (30), 1e-6 (20, under 2^-14), zeros
+    # (50), -0.5 (300), the mask. 1 and 20: window levels; 40: the 1e-6
+    # level; 60 and 90: the zeros; 200: -0.5; 500 and 5000: the mask level
     top_k = np.array([1, 20, 40, 60, 90, 200, 500, 5000], np.int32)
     for top_p in (None, np.full(B, 0.9, np.float32)):
         total = parity.Report()
