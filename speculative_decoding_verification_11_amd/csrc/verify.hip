@@ -1,8 +1,9 @@
 // verify.hip -- HIP kernels and C ABI of the speculative-sampling
 // verification step on MI355X (gfx950): spec_verify, spec_verify_top_p,
 // spec_verify_top_k_top_p and spec_verify_early_exit. The top-k / top-p
-// search (k_nucleus) is in nucleus.hip, the early-exit kernels in
-// early_exit.hip; all are launched from the host side here.
+// kernels (k_filter and k_filter_fallback for bf16 rows, k_nucleus for fp32
+// rows) are in nucleus.hip, the early-exit kernels in early_exit.hip; all
+// are launched from the host side here.
 //
 // The step, per sequence b with draft length L and temperature tau
 // ("Speculative Decoding and the Art of Fast LLM Inference", "The Algorithm,
@@ -16,10 +17,11 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Three or four launches per call (with a filter, k_filter replaces
-// k_rowstats for bf16 logits; k_nucleus follows it for fp32), stream-ordered, no host synchronisation. Every hand-over between
-// workgroups crosses a launch boundary, so no workgroup ever waits for
-// another and nothing needs device-scope atomics:
+// Three or four launches per call (with a filter, k_filter and
+// k_filter_fallback replace k_rowstats for bf16 logits; k_nucleus follows
+// it for fp32), stream-ordered, no host synchronisation. Every hand-over
+// between workgroups crosses a launch boundary, so no workgroup ever waits
+// for another and nothing needs device-scope atomics:
 //
 //   k_rowstats  one workgroup per 32 KiB chunk of every logit row the step
 //               needs (b-major). Each streams its chunk once with 16-byte
@@ -28,9 +30,9 @@
 //               lowest index of it) for greedy rows. This kernel carries
 //               all of the algorithmic HBM traffic and runs at copy speed.
 //               With a top-k or top-p filter on bf16 logits, k_filter takes
-//               its place: one workgroup per row, reading each row once
-//               (the row statistics for rows without a filter, counts and
-//               thresholds for the others).
+//               its place: one workgroup per row, reading each filtered row
+//               once (counts, thresholds and the row max); k_filter_fallback
+//               then gives the rows without a filter their row statistics.
 //   k_decide    one wave per sequence: fold the partials in chunk order,
 //               gather p_i(g_i) and q_i(g_i), draw Philox, run the
 //               left-to-right test, write the accepted prefix, and record
