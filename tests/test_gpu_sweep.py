@@ -7,6 +7,12 @@ logits) and of one or several chunks, every draft length from 0 to k, k up
 to the maximum, greedy and sampling sequences in one batch, and the top-k /
 top-p filters. Every case is compared with the oracle at the usual
 tolerances.
+
+A second, wider mix draws every parameter at random (vocabularies up to
+131073, k up to 63, temperatures up to 40, logit scales 0.5 to 6, top-k and
+top-p per sequence) and also checks early exit against the full step bit
+for bit. Its first seeds are ones where the residual mass came close to
+0.008 or a top-p boundary fell on a row past the stop.
 """
 import numpy as np
 import pytest
@@ -20,6 +26,7 @@ from oracle import parity  # noqa: E402
 from test_gpu_parity import (DEV, _mixed_batch, batch_to, check, host, run_gpu,  # noqa: E402
                              say)
 from test_gpu_top_k import run_tk  # noqa: E402
+from test_gpu_early_exit import _run, assert_same_as_full  # noqa: E402
 
 SWEEP_V = {"bf16": (1, 2, 255, 16383, 16384, 16385, 32768, 40000),
            "f32": (1, 3, 8191, 8192, 8193, 16385, 24577)}
@@ -53,6 +60,41 @@ def test_shape_sweep(i):
         g = run_gpu(gb, seed)
         r = parity.oracle_on(h, seed)
     check(parity.compare(g, r, h["draft_len"], h["temperature"], k), f"sweep {i}")
+
+
+MIX_SEEDS = [50048, 50222, 50602, 51703, 52584] + list(range(60000, 60040))
+
+
+@pytest.mark.parametrize("seed0", MIX_SEEDS)
+def test_random_mix(seed0):
+    rng = np.random.default_rng(seed0)
+    dtype = ("bf16", "f32")[int(rng.integers(0, 3)) == 0]
+    V = int(rng.choice([2, 17, 300, 4097, 16384, 16385, 40001, 65536, 131073]))
+    k = int(rng.choice([0, 1, 3, 4, 7, 12, 63]))
+    B = int(rng.integers(1, 40 if k < 20 else 4))
+    taus = tuple(float(x) for x in rng.choice([0.0, 0.25, 0.7, 1.0, 1.9, 40.0], size=3))
+    sigma = float(rng.choice([0.5, 2.0, 6.0]))
+    cb = _mixed_batch(rng, B, k, V, dtype, taus=taus, sigma=sigma)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    seed = int(rng.integers(0, 2**63))
+    mode = int(rng.integers(0, 3))  # 0 plain (+ early exit), 1 top-p, 2 top-k and top-p
+    say(f"[case] mix {seed0}: B={B} k={k} V={V} {dtype} taus={taus} sigma={sigma} mode={mode}")
+    if mode == 0:
+        g = run_gpu(gb, seed)
+        r = parity.oracle_on(h, seed)
+        ee = _run(sv.spec_verify_early_exit, gb, seed)
+        assert_same_as_full(g, ee, h["draft_len"], h["temperature"], k, f"mix {seed0}")
+    else:
+        top_k = np.zeros(B, np.int32)
+        if mode == 2:
+            top_k = rng.integers(-2, V + 2, size=B).astype(np.int32)
+            if rng.random() < 0.5:
+                top_k = np.minimum(top_k, rng.integers(1, 60, size=B)).astype(np.int32)
+        top_p = rng.choice([0.05, 0.3, 0.7, 0.9, 0.99, 1.0], size=B).astype(np.float32)
+        g = run_tk(gb, seed, top_k, top_p)
+        r = parity.oracle_on(h, seed, top_k=top_k, top_p=top_p)
+    check(parity.compare(g, r, h["draft_len"], h["temperature"], k), f"mix {seed0}")
 
 
 def test_decision_in_draw_and_separate_launch_agree():
