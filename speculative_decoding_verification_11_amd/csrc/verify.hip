@@ -252,16 +252,31 @@ struct Weights {
     float w, p;
 };
 
+//
+// The specialised form below fixes, per workgroup, whether the draw is a
+// residual (Resid) and whether a filter threshold applies (Thresh); with no
+// filter the thresholds are -inf, which every finite logit passes, so both
+// forms give the same bits. Contraction stays off in both, so that no
+// product is fused into the difference in one form and not in the other.
+template <bool Resid, bool Thresh>
+__device__ inline Weights draw_weights_t(float xt, float xd, const Decision &dec, float inv_zt,
+                                         float inv_zd)
+{
+#pragma clang fp contract(off)
+    const float et = exp2_fast((xt - dec.mt) * dec.scale) * inv_zt;
+    const float pt = !Thresh || xt >= dec.tht ? et : 0.f;  // outside the target's nucleus: 0
+    if constexpr (!Resid)
+        return {pt, pt};
+    const float ed = exp2_fast((xd - dec.md) * dec.scale) * inv_zd;
+    const float pd = !Thresh || xd >= dec.thd ? ed : 0.f;
+    return {fmaxf(pt - pd, 0.f), pt};
+}
+
 __device__ inline Weights draw_weights(float xt, float xd, const Decision &dec, float inv_zt,
                                        float inv_zd, bool resid)
 {
-    const float et = exp2_fast((xt - dec.mt) * dec.scale) * inv_zt;
-    const float pt = xt >= dec.tht ? et : 0.f;  // outside the target's nucleus: 0
-    if (!resid)
-        return {pt, pt};
-    const float ed = exp2_fast((xd - dec.md) * dec.scale) * inv_zd;
-    const float pd = xd >= dec.thd ? ed : 0.f;
-    return {fmaxf(pt - pd, 0.f), pt};
+    return resid ? draw_weights_t<true, true>(xt, xd, dec, inv_zt, inv_zd)
+                 : draw_weights_t<false, true>(xt, xd, dec, inv_zt, inv_zd);
 }
 
 // Pairwise fp32 sum of one group's 8 or 4 weights (fixed association).
@@ -328,6 +343,47 @@ __device__ inline void group_weight_sums(const DrawRows<D> &r, const Span &sp, i
     gp = pairwise(pw);
 }
 
+// Group sums of one chunk with 16-byte aligned groups, kTiles groups per
+// lane: kBatch 16-byte loads per row in flight before their arithmetic.
+template <class D, bool Resid, bool Thresh>
+__device__ __forceinline__ void vec_group_sums(const DrawRows<D> &r, const Span &sp,
+                                               const Decision &dec, int tid, float (&gw)[kTiles],
+                                               float (&gp)[kTiles])
+{
+    constexpr int kBatch = kTiles / 2;
+    const u32x4 *vt = reinterpret_cast<const u32x4 *>(r.t + sp.a);
+    const u32x4 *vd = reinterpret_cast<const u32x4 *>(r.d + sp.a);
+#pragma unroll
+    for (int h = 0; h < kTiles; h += kBatch) {
+        u32x4 lt[kBatch], ld[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t gi = (int64_t)(h + u) * kThreads + tid;
+            const bool in = gi < sp.ngroups;
+            lt[u] = in ? stream_load(vt + gi) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (Resid)
+                ld[u] = in ? stream_load(vd + gi) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            float ft[D::kVec], fd[D::kVec], w[D::kVec], pw[D::kVec];
+            D::unpack(lt[u], ft);
+            if constexpr (Resid)
+                D::unpack(ld[u], fd);
+#pragma unroll
+            for (int j = 0; j < D::kVec; ++j) {
+                const Weights x = draw_weights_t<Resid, Thresh>(ft[j], Resid ? fd[j] : 0.f, dec,
+                                                                r.inv_zt, r.inv_zd);
+                w[j] = x.w;
+                pw[j] = x.p;
+            }
+            const bool in = (int64_t)(h + u) * kThreads + tid < sp.ngroups;
+            gp[h + u] = in ? pairwise(pw) : 0.f;
+            gw[h + u] = Resid ? (in ? pairwise(w) : 0.f) : gp[h + u];  // a bonus draws from p
+        }
+    }
+}
+
 // ===========================================================================
 // Sums of the draw weights over one chunk of the decided row: per segment
 // (fp64 sums of the fp32 pairwise group sums) and over the chunk, for w and
@@ -344,35 +400,18 @@ __device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, in
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     float gw[kTiles], gp[kTiles];  // this lane's group sums, tile by tile
     if (sp.vec) {
-        // kBatch 16-byte loads per row in flight before their arithmetic
-        constexpr int kBatch = kTiles / 2;
-        const u32x4 *vt = reinterpret_cast<const u32x4 *>(r.t + sp.a);
-        const u32x4 *vd = reinterpret_cast<const u32x4 *>(r.d + sp.a);
-#pragma unroll
-        for (int h = 0; h < kTiles; h += kBatch) {
-            u32x4 lt[kBatch], ld[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t gi = (int64_t)(h + u) * kThreads + tid;
-                const bool in = gi < sp.ngroups;
-                lt[u] = in ? stream_load(vt + gi) : u32x4{0u, 0u, 0u, 0u};
-                ld[u] = in && r.resid ? stream_load(vd + gi) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                float ft[D::kVec], fd[D::kVec], w[D::kVec], pw[D::kVec];
-                D::unpack(lt[u], ft);
-                D::unpack(ld[u], fd);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j) {
-                    const Weights x = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd, r.resid);
-                    w[j] = x.w;
-                    pw[j] = x.p;
-                }
-                const bool in = (int64_t)(h + u) * kThreads + tid < sp.ngroups;
-                gw[h + u] = in ? pairwise(w) : 0.f;
-                gp[h + u] = in ? pairwise(pw) : 0.f;
-            }
+        // Uniform per workgroup: pick the loop without per-token tests.
+        const bool thresh = dec.tht != -INFINITY || (r.resid && dec.thd != -INFINITY);
+        if (r.resid) {
+            if (thresh)
+                vec_group_sums<D, true, true>(r, sp, dec, tid, gw, gp);
+            else
+                vec_group_sums<D, true, false>(r, sp, dec, tid, gw, gp);
+        } else {
+            if (thresh)
+                vec_group_sums<D, false, true>(r, sp, dec, tid, gw, gp);
+            else
+                vec_group_sums<D, false, false>(r, sp, dec, tid, gw, gp);
         }
     } else {
         int unused = -1;
