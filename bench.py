@@ -437,6 +437,14 @@ def main() -> int:
     achieved = alg_bytes / (k1_mean * 1e-3) / 1e9
     n_acc = outs[0][1].to(torch.int64)
     tokens_per_round = float((n_acc + 1).float().mean())
+    # The draw re-reads the decided row of every sampled sequence: target
+    # and draft row at a rejection, the target row alone for a bonus token.
+    n_cpu = n_acc.cpu()
+    final_ok = outs[0][0].cpu().gather(1, n_cpu.view(-1, 1)).view(-1) >= 0
+    sampled_seq = (copies[0].temperature.cpu() > 0) & final_ok
+    resid_seq = sampled_seq & (n_cpu < copies[0].draft_len.cpu().to(torch.int64))
+    draw_rows = int(sampled_seq.sum()) + int(resid_seq.sum())
+    draw_bytes = draw_rows * w.V * w.elem_bytes
     log(f"[bench] {ms_per_step:.4f} ms/step; k_rowstats mean {k1_mean * 1e3:.1f} us "
         f"(median {k1_median * 1e3:.1f}, min {k1_ms[0] * 1e3:.1f}, max {k1_ms[-1] * 1e3:.1f}); "
         f"{achieved:.0f} GB/s")
@@ -604,6 +612,16 @@ def main() -> int:
             "rows_read": {"target": t_rows, "draft": d_rows},
             "algorithmic_bytes": alg_bytes,
             "effective_GBps_whole_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+            "draw_reread": {
+                "rows": draw_rows,
+                "bytes": draw_bytes,
+                "step_bytes": alg_bytes + draw_bytes,
+                "step_GBps": (alg_bytes + draw_bytes) / (ms_per_step * 1e-3) / 1e9,
+                "step_frac_of_peak": (alg_bytes + draw_bytes) / (ms_per_step * 1e-3) / 1e9
+                                     / PEAK_HBM_GBPS,
+                "note": "every row read once plus the decided row of each sampled sequence "
+                        "read again by the draw, over the wall-clock step",
+            },
             "rotating_copies": len(copies),
             "mean_tokens_per_round": tokens_per_round,
             "parallelism": "single GPU",
