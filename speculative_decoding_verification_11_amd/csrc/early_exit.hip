@@ -198,14 +198,16 @@ template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
 {
     __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x;
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     if (item == 0 && threadIdx.x == 0)
         p.ee_count[1] = 0;  // position 1's list, filled by k_ee_decide0
-    const int c = (int)(item % nc);
-    const int64_t rs = item / nc;
-    const int slot = (int)(rs % 2);
-    const int64_t b = rs / 2;
+    // 32-bit decode of the grid index (64-bit division is a long scalar
+    // sequence every workgroup would run before its first load).
+    const int c = (int)(item % (uint32_t)nc);
+    const uint32_t rs = item / (uint32_t)nc;
+    const int slot = (int)(rs % 2u);
+    const int64_t b = rs / 2u;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
     if (!(valid_len(L, k) && valid_temp(tau)))
@@ -264,13 +266,13 @@ template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
 {
     __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x;  // 32-bit decode, as in k_ee_rowstats0
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
-    const int64_t j = item / (2 * nc);
+    const int64_t j = item / (2u * (uint32_t)nc);
     if (j >= p.ee_count[i])
         return;
-    const int slot = (int)((item / nc) % 2);
-    const int c = (int)(item % nc);
+    const int slot = (int)((item / (uint32_t)nc) % 2u);
+    const int c = (int)(item % (uint32_t)nc);
     const int64_t b = p.ee_list[(int64_t)i * p.B + j];
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
@@ -304,14 +306,15 @@ template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
 {
     __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x;  // 32-bit decode, as in k_ee_rowstats0
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     const int nt = k - P + 1, R = 2 * nt - 1;  // target rows P..k, draft rows P..k-1
-    const int64_t j = item / ((int64_t)R * nc);
+    const uint32_t per_seq = (uint32_t)R * (uint32_t)nc;
+    const int64_t j = item / per_seq;
     if (j >= p.ee_count[P])
         return;
-    const int rest = (int)(item % ((int64_t)R * nc));
-    const int slot = rest / nc, c = rest % nc;
+    const uint32_t rest = item % per_seq;
+    const int slot = (int)(rest / (uint32_t)nc), c = (int)(rest % (uint32_t)nc);
     const int64_t b = p.ee_list[(int64_t)P * p.B + j];
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];

@@ -575,9 +575,9 @@ __device__ inline FilterRow<D> filter_row(const Params &p)
 {
     using E = typename D::Elem;
     const int k = p.k, rows = 2 * k + 1;
-    const int64_t rb = blockIdx.x;
-    const int slot = (int)(rb % rows);
-    const int64_t b = rb / rows;
+    const uint32_t rb = blockIdx.x;  // 32-bit decode: the grid index fits
+    const int slot = (int)(rb % (uint32_t)rows);
+    const int64_t b = rb / (uint32_t)rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
     FilterRow<D> f;
     f.tau = p.temperature[b];
@@ -893,9 +893,9 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_nucleus(Params p)
     using E = typename D::Elem;
     __shared__ NucleusShared sh;
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
-    const int64_t rb = blockIdx.x;
-    const int slot = (int)(rb % rows);
-    const int64_t b = rb / rows;
+    const uint32_t rb = blockIdx.x;  // 32-bit decode: the grid index fits
+    const int slot = (int)(rb % (uint32_t)rows);
+    const int64_t b = rb / (uint32_t)rows;
     const int tid = threadIdx.x;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];

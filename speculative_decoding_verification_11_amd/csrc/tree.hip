@@ -33,12 +33,12 @@ __global__ __launch_bounds__(kThreads) void k_tree_rowstats(TreeParams p)
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
     __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x;  // 32-bit decode: the grid index fits
     const int nc = p.nc, N = p.N;
-    const int c = (int)(item % nc);
-    const int64_t rn = item / nc;
-    const int n = (int)(rn % N);
-    const int64_t b = rn / N;
+    const int c = (int)(item % (uint32_t)nc);
+    const uint32_t rn = item / (uint32_t)nc;
+    const int n = (int)(rn % (uint32_t)N);
+    const int64_t b = rn / (uint32_t)N;
     const int nn = p.n_nodes[b];
     if (nn < 1 || nn > N || n >= nn)
         return;  // k_tree_decide reports a bad node count

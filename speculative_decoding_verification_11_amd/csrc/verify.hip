@@ -651,13 +651,14 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
     __shared__ RowShared sh;
-    const int64_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x;
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
-
-    const int c = (int)(item % nc);
-    const int64_t rs = item / nc;
-    const int slot = (int)(rs % rows);
-    const int64_t b = rs / rows;
+    // 32-bit decode of the grid index (64-bit division is a long scalar
+    // sequence every workgroup would run before its first load).
+    const int c = (int)(item % (uint32_t)nc);
+    const uint32_t rs = item / (uint32_t)nc;
+    const int slot = (int)(rs % (uint32_t)rows);
+    const int64_t b = rs / (uint32_t)rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
     if (!valid_len(L, k) || !valid_temp(tau))
