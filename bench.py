@@ -609,6 +609,7 @@ def main() -> int:
             "workload": f"{w.name}: {w.description}",
             "B": w.B, "k": w.k, "V": w.V, "logits": w.dtype,
             "valid_positions": valid_positions,
+            "valid_positions_per_s": valid_positions / (ms_per_step * 1e-3),
             "rows_read": {"target": t_rows, "draft": d_rows},
             "algorithmic_bytes": alg_bytes,
             "effective_GBps_whole_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
