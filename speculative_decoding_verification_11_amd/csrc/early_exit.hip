@@ -227,37 +227,56 @@ __device__ inline void ee_enlist(const Params &p, int64_t b, int i)
 }
 
 // Position 0's decisions, one wave per sequence; also validates the inputs
-// and clears the counters of the later positions.
+// and clears the counters of the later positions. The sequences that accept
+// are listed for position 1 with one counter add per workgroup (one per
+// sequence would queue up to B device-scope adds on one address).
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    __shared__ int accepted[kWaves];
+    __shared__ int list_at;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t b = (int64_t)blockIdx.x * kWaves + wave;
     const int k = p.k, V = p.V;
     if (blockIdx.x == 0 && threadIdx.x > 1 && threadIdx.x <= k + 1)
         p.ee_count[threadIdx.x] = 0;  // positions 2..k (and k + 1, never read)
-    if (b >= p.B)
-        return;
-    if (lane >= 1 && lane <= k)
-        p.ee_done[(int64_t)lane * p.B + b] = 0;
-    const int L = p.draft_len ? p.draft_len[b] : k;
-    const float tau = p.temperature[b];
-    int status = SPEC_SEQ_OK;
-    if (!valid_len(L, k)) {
-        status = SPEC_SEQ_BAD_LEN;
-    } else if (!valid_temp(tau)) {
-        status = SPEC_SEQ_BAD_TEMP;
-    } else {
-        const int g = lane < L ? p.draft_tokens[b * k + lane] : 0;
-        if (__any(lane < L && (g < 0 || g >= V)))
-            status = SPEC_SEQ_BAD_TOKEN;
+    bool accept = false;
+    if (b < p.B) {  // no early return: every wave reaches the barriers below
+        if (lane >= 1 && lane <= k)
+            p.ee_done[(int64_t)lane * p.B + b] = 0;
+        const int L = p.draft_len ? p.draft_len[b] : k;
+        const float tau = p.temperature[b];
+        int status = SPEC_SEQ_OK;
+        if (!valid_len(L, k)) {
+            status = SPEC_SEQ_BAD_LEN;
+        } else if (!valid_temp(tau)) {
+            status = SPEC_SEQ_BAD_TEMP;
+        } else {
+            const int g = lane < L ? p.draft_tokens[b * k + lane] : 0;
+            if (__any(lane < L && (g < 0 || g >= V)))
+                status = SPEC_SEQ_BAD_TOKEN;
+        }
+        if (status != SPEC_SEQ_OK)
+            ee_stop(p, b, 0, status, no_decision(), false, 0, 0, 0, lane);
+        else
+            accept = ee_decide<D>(p, b, 0, L, tau, false, lane);
     }
-    if (status != SPEC_SEQ_OK) {
-        ee_stop(p, b, 0, status, no_decision(), false, 0, 0, 0, lane);
-        return;
+    if (lane == 0)
+        accepted[wave] = accept ? 1 : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int w = 0; w < kWaves; ++w)
+            n += accepted[w];
+        list_at = n ? counter_add(p.ee_count + 1, n) : 0;
     }
-    if (ee_decide<D>(p, b, 0, L, tau, false, lane) && lane == 0)
-        ee_enlist(p, b, 1);
+    __syncthreads();
+    if (lane == 0 && accept) {
+        int at = list_at;
+        for (int w = 0; w < wave; ++w)
+            at += accepted[w];
+        p.ee_list[p.B + at] = (int32_t)b;  // position 1's list
+    }
 }
 
 // Position i >= 1: the sequences on position i's list. The workgroup that
