@@ -503,17 +503,19 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 {
     constexpr int64_t CH = chunk_elems<D>();
     const int nc = p.nc;
-    const Decision dec = p.decisions[b];
-    if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
-        return;  // greedy or error: the decision wrote everything
-    const DrawRows<D> r = draw_rows<D>(p, b, dec);
+    // The chunk masses are loaded with the decision, not after it: their
+    // address does not depend on it (one round trip less).
     const double *mw = reinterpret_cast<const double *>(p.masses + b * (int64_t)nc);
     const bool staged = nc <= kMaxLdsChunks / 2;
+    const Decision dec = p.decisions[b];
     if (staged) {
         for (int q = lane; q < 2 * nc; q += kWave)
             sh.cm[q] = mw[q];
         __syncthreads();
     }
+    if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
+        return;  // greedy or error: the decision wrote everything
+    const DrawRows<D> r = draw_rows<D>(p, b, dec);
 
     // Chunk level (every lane runs the same scalar loop over LDS).
     auto mass = [&](int q) { return staged ? sh.cm[q] : mw[q]; };
