@@ -358,8 +358,9 @@ def main() -> int:
     EVENT_EVERY = max(1, args.event_every)
 
     if args.gpus != 1:
-        log(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU only "
-            "(sequences shard across GPUs with no communication; see the design notes).")
+        log(f"bench.py: --gpus {args.gpus} is not supported: it measures one GPU only. "
+            "Sequences shard across GPUs with no communication: each GPU would run the same "
+            "kernels on its slice of the batch, with seq_base set to the slice's offset.")
         return 2
     import torch
 
