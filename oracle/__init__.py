@@ -101,6 +101,12 @@ def _load():
                                                ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                                ctypes.c_uint32] + [P] * 12
         lib.spec_verify_filter_ref.restype = ctypes.c_int
+        lib.spec_verify_full_ref.argtypes = [P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                             ctypes.c_uint32] + [P] * 12 + [ctypes.c_double, P]
+        lib.spec_verify_full_ref.restype = ctypes.c_int
+        lib.ref_draw_window.argtypes = [P, ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P]
+        lib.ref_draw_window.restype = None
         lib.ref_tree_greedy.argtypes = [P, P, P, ctypes.c_int, P, P]
         lib.ref_tree_greedy.restype = ctypes.c_int
         lib.spec_tree_ref.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int32, ctypes.c_int32,
@@ -161,6 +167,17 @@ def draw_inverse_cdf(w: np.ndarray, v: float):
     fb = np.zeros(1, dtype=np.int32)
     x = _load().ref_draw_inverse_cdf(_ptr(w), w.shape[0], float(v), _ptr(S), _ptr(m), _ptr(fb))
     return int(x), float(S[0]), float(m[0]), bool(fb[0])
+
+
+def draw_window(w: np.ndarray, v: float, band: float):
+    """Smallest and largest ids an inverse-CDF draw from weights ``w`` could
+    return with its uniform moved by at most ``band`` (-1, -1 if sum w <= 0)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    lo = ctypes.c_int64(0)
+    hi = ctypes.c_int64(0)
+    _load().ref_draw_window(_ptr(w), w.shape[0], float(v), float(band), ctypes.byref(lo),
+                            ctypes.byref(hi))
+    return int(lo.value), int(hi.value)
 
 
 def nucleus_row(row: np.ndarray, p: np.ndarray, top_p: float):
@@ -234,7 +251,7 @@ def round_greedy(amax, g):
 
 def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
                     draft_len, temperature, seed: int, seq_base: int = 0,
-                    nthreads: int = 1, top_p=None, top_k=None) -> dict:
+                    nthreads: int = 1, top_p=None, top_k=None, band: float = 1e-6) -> dict:
     """The whole step on host arrays (see spec_verify_ref.c for the contract).
 
     target [B, k+1, V] and draft [B, k, V] are float32 or uint16 (bf16 bits).
@@ -242,7 +259,9 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
     each slice keeps its global sequence index, so results do not change.
     ``top_p`` (fp32) and ``top_k`` (int32), scalars or [B], filter every
     sampling row (readings TP1, TK1); ``margin_nucleus`` is returned with
-    ``top_p``.
+    ``top_p``. ``draw_window`` [B, 2]: the token ids the final draw could
+    select with its uniform moved by at most ``band`` (-1 where no token was
+    sampled).
     """
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
@@ -276,6 +295,7 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         margin_draw=np.full(B, np.nan),
         draw_row=np.full(B, -1, dtype=np.int32),
         draw_kind=np.zeros(B, dtype=np.int32),
+        draw_window=np.full((B, 2), -1, dtype=np.int32),
     )
     if tp is not None:
         res["margin_nucleus"] = np.full((B, 2 * k + 1), np.nan)
@@ -285,34 +305,17 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         if b1 <= b0:
             return 0
         sl = slice(b0, b1)
-        if tk is not None:
-            mn = res["margin_nucleus"][sl] if tp is not None else None
-            outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
-                                         "argmax", "resid_mass", "margin_accept", "margin_draw")]
-            return lib.spec_verify_filter_ref(
-                _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
-                _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]), _ptr(tk[sl]),
-                _ptr(tp[sl]) if tp is not None else None, b1 - b0, k, V,
-                ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF),
-                *[_ptr(o) for o in outs], _ptr(mn) if mn is not None else None,
-                _ptr(res["draw_row"][sl]), _ptr(res["draw_kind"][sl]))
-        if tp is None:
-            outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
-                                         "argmax", "resid_mass", "margin_accept", "margin_draw",
-                                         "draw_row", "draw_kind")]
-            return lib.spec_verify_ref(
-                _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
-                _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]),
-                b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
-                ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs])
+        mn = res["margin_nucleus"][sl] if tp is not None else None
         outs = [res[n][sl] for n in ("out_tokens", "num_accepted", "seq_status", "p_g", "q_g",
-                                     "argmax", "resid_mass", "margin_accept", "margin_draw",
-                                     "margin_nucleus", "draw_row", "draw_kind")]
-        return lib.spec_verify_topp_ref(
+                                     "argmax", "resid_mass", "margin_accept", "margin_draw")]
+        return lib.spec_verify_full_ref(
             _ptr(target[sl]), _ptr(draft[sl]), dt, _ptr(tokens[sl]),
-            _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]), _ptr(tp[sl]),
+            _ptr(lens[sl]) if lens is not None else None, _ptr(temp[sl]),
+            _ptr(tk[sl]) if tk is not None else None, _ptr(tp[sl]) if tp is not None else None,
             b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
-            ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs])
+            ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs],
+            _ptr(mn) if mn is not None else None, _ptr(res["draw_row"][sl]),
+            _ptr(res["draw_kind"][sl]), float(band), _ptr(res["draw_window"][sl]))
 
     if nthreads <= 1 or B <= 1:
         rc = run(0, B)

@@ -16,6 +16,12 @@ inputs, sequence by sequence:
   band has its gathered values skipped (counted as ``boundary_values``).
   The residual mass S is compared wherever the final draw is compared,
   within ``rel`` plus the absolute ``RESID_ABS`` derived below.
+
+A flagged final draw on which the two sides part must still land inside the
+oracle's band window: the token ids that the oracle's own draw would pick
+with its uniform moved by at most ``band``. A disagreement outside that
+window is a mismatch however small the oracle's margin, so a locate error
+among low-weight tokens (whose margins are always below the band) is caught.
 """
 from __future__ import annotations
 
@@ -81,6 +87,9 @@ class Report:
     boundary_values: int = 0
     compared_tokens: int = 0
     max_disagree_margin: float = 0.0
+    resid_compared: int = 0
+    max_abs_dS: float = 0.0
+    max_rel_dS_large: float = 0.0  # over S > S_LARGE, where 1e-5 * S exceeds RESID_ABS
     band_counts: dict = field(default_factory=dict)
     mismatches: list = field(default_factory=list)
 
@@ -93,6 +102,9 @@ class Report:
         self.boundary_values += other.boundary_values
         self.compared_tokens += other.compared_tokens
         self.max_disagree_margin = max(self.max_disagree_margin, other.max_disagree_margin)
+        self.resid_compared += other.resid_compared
+        self.max_abs_dS = max(self.max_abs_dS, other.max_abs_dS)
+        self.max_rel_dS_large = max(self.max_rel_dS_large, other.max_rel_dS_large)
         for key, v in other.band_counts.items():
             self.band_counts[key] = self.band_counts.get(key, 0) + v
         self.mismatches += other.mismatches
@@ -111,6 +123,8 @@ class Report:
                 f"({self.flagged_fraction:.2e}) flagged_disagree={self.flagged_disagree} "
                 f"max_disagree_margin={self.max_disagree_margin:.2e} margins[{bands}] "
                 f"boundary_status={self.boundary_status} boundary_values={self.boundary_values} "
+                f"S_compared={self.resid_compared} max|dS|={self.max_abs_dS:.2e} "
+                f"max_rel_dS(S>{S_LARGE:.2f})={self.max_rel_dS_large:.2e} "
                 f"mismatches={len(self.mismatches)}")
         return head + ("" if not self.mismatches else "\n  " + "\n  ".join(self.mismatches[:20]))
 
@@ -133,6 +147,8 @@ def _close(a: float, b: float, rel: float, floor: float) -> bool:
 # 17 bits for V <= 131072. Two rows of (4 + 0.7 * 17) < 16 ulps each give
 # 32 ulps of fp32 epsilon 2^-24, i.e. 2^-19.
 RESID_ABS = 2.0 ** -19
+# Above this S the relative part of the tolerance (1e-5 * S) is the larger.
+S_LARGE = RESID_ABS / 1e-5
 
 
 def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel: float = 1e-5,
@@ -143,8 +159,10 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
     n_ref = ref["num_accepted"].shape[0]
     rows = list(range(n_ref)) if rows is None else [int(r) for r in rows]
 
-    def draw(margin: float, agree: bool, what: str) -> bool:
-        """Account one draw; returns False when the comparison must stop."""
+    def draw(margin: float, agree: bool, what: str, in_window: bool = True) -> bool:
+        """Account one draw; returns False when the comparison must stop.
+        ``in_window``: for a final draw, whether the GPU's token lies in the
+        oracle's band window (a flagged disagreement must)."""
         rep.draws += 1
         for b_ in BANDS:
             if margin < b_:
@@ -154,6 +172,9 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
             if not agree:
                 rep.flagged_disagree += 1
                 rep.max_disagree_margin = max(rep.max_disagree_margin, margin)
+                if not in_window:
+                    rep.mismatches.append(what + f" (flagged, margin {margin:.3e}, but outside "
+                                          "the oracle's band window)")
                 return False
             return True
         if not agree:
@@ -245,11 +266,19 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
         if int(gpu["draw_kind"][b]) != int(ref["draw_kind"][j]):
             rep.mismatches.append(f"{tag}: draw kind {gpu['draw_kind'][b]} vs {ref['draw_kind'][j]}")
         S_g, S_r = float(gpu["resid_mass"][b]), float(ref["resid_mass"][j])
+        rep.resid_compared += 1
+        dS = abs(S_g - S_r)
+        rep.max_abs_dS = max(rep.max_abs_dS, dS)
+        if S_r > S_LARGE:
+            rep.max_rel_dS_large = max(rep.max_rel_dS_large, dS / S_r)
         if not _close(S_g, S_r, rel, RESID_ABS):
             rep.mismatches.append(f"{tag}: resid_mass gpu={S_g!r} oracle={S_r!r}")
         if not np.array_equal(g_out[r_n + 1:], r_out[r_n + 1:]):
             rep.mismatches.append(f"{tag}: padding {g_out} vs {r_out}")
+        lo, hi = (int(x) for x in ref["draw_window"][j]) if "draw_window" in ref else (-1, -1)
+        in_window = "draw_window" in ref and lo <= int(g_out[r_n]) <= hi
         if draw(float(ref["margin_draw"][j]), g_out[r_n] == r_out[r_n],
-                f"{tag}: final token {g_out[r_n]} vs {r_out[r_n]}"):
+                f"{tag}: final token {g_out[r_n]} vs {r_out[r_n]} (window {lo}..{hi})",
+                in_window):
             rep.compared_tokens += 1
     return rep

@@ -353,6 +353,37 @@ int64_t ref_draw_inverse_cdf(const double *w, int64_t V, double v, double *S_out
 }
 
 /* ------------------------------------------------------------------ */
+/* The ids an inverse-CDF draw could return if its uniform were moved by */
+/* at most `band` (reading R4, with the flagging rule of the parity      */
+/* protocol: a draw whose uniform lies within `band` of a CDF boundary   */
+/* may legitimately land on the neighbouring id when the weights are     */
+/* rounded differently). Id x, of weight w(x) > 0, owns the uniforms in  */
+/* [C(x-1)/S, C(x)/S) with the same sequential C and S as               */
+/* ref_draw_inverse_cdf; *lo and *hi are the smallest and largest such x */
+/* whose interval meets [v - band, v + band]. Both are -1 when S <= 0.   */
+/* ------------------------------------------------------------------ */
+void ref_draw_window(const double *w, int64_t V, double v, double band, int64_t *lo, int64_t *hi)
+{
+    double S = 0.0;
+    for (int64_t x = 0; x < V; x++)
+        S += w[x];
+    *lo = -1;
+    *hi = -1;
+    if (!(S > 0.0))
+        return;
+    double c = 0.0;
+    for (int64_t x = 0; x < V; x++) {
+        double from = c / S;
+        c += w[x];
+        if (w[x] > 0.0 && c / S > v - band && from <= v + band) {
+            if (*lo < 0)
+                *lo = x;
+            *hi = x;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* One sampling round for one sequence, given the probability rows and  */
 /* the uniforms ([ART] steps "Accept or reject, left to right", "Stop   */
 /* at the first rejection", "Bonus token"; [TLS] P_accept, the          */
@@ -461,7 +492,7 @@ static int verify_batch(const void *target, const void *draft, int dtype,
                         int32_t *num_accepted, int32_t *seq_status, double *p_g, double *q_g,
                         int32_t *argmax, double *resid_mass, double *margin_accept,
                         double *margin_draw, double *margin_nucleus, int32_t *draw_row,
-                        int32_t *draw_kind)
+                        int32_t *draw_kind, double band, int32_t *draw_window)
 {
     const size_t esz = dtype == REF_F32 ? 4 : 2;
     double *p = malloc(sizeof(double) * (size_t)(k + 1) * (size_t)V);
@@ -499,6 +530,7 @@ static int verify_batch(const void *target, const void *draft, int dtype,
         if (margin_draw) margin_draw[b] = NAN;
         if (draw_row) draw_row[b] = -1;
         if (draw_kind) draw_kind[b] = REF_DRAW_NONE;
+        if (draw_window) draw_window[2 * (size_t)b] = draw_window[2 * (size_t)b + 1] = -1;
         num_accepted[b] = 0;
 
         /* Input checks, in this order: length, temperature, top-p, tokens.
@@ -582,6 +614,15 @@ static int verify_batch(const void *target, const void *draft, int dtype,
             if (margin_draw) margin_draw[b] = mdraw;
             if (draw_row) draw_row[b] = row;
             if (draw_kind) draw_kind[b] = kind;
+            if (draw_window) {
+                /* the weights of the final draw: the residual (still in the
+                 * scratch row w), or p at the draw row */
+                const double *wd = kind == REF_DRAW_RESIDUAL ? w : p + (size_t)row * V;
+                int64_t lo, hi;
+                ref_draw_window(wd, V, v[row], band, &lo, &hi);
+                draw_window[2 * (size_t)b] = (int32_t)lo;
+                draw_window[2 * (size_t)b + 1] = (int32_t)hi;
+            }
         }
         num_accepted[b] = n;
         if (seq_status) seq_status[b] = REF_SEQ_OK;
@@ -602,7 +643,7 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, NULL, B,
                         k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, NULL, draw_row,
-                        draw_kind);
+                        draw_kind, 0.0, NULL);
 }
 
 /* The whole step with nucleus filtering (reading TP1): top_p [B] fp32, 1  */
@@ -621,7 +662,7 @@ int spec_verify_topp_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, top_p,
                         B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
-                        draw_row, draw_kind);
+                        draw_row, draw_kind, 0.0, NULL);
 }
 
 /* The whole step with top-k and nucleus filtering (TK1 then TP1): top_k */
@@ -640,7 +681,28 @@ int spec_verify_filter_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_k, top_p,
                         B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
-                        draw_row, draw_kind);
+                        draw_row, draw_kind, 0.0, NULL);
+}
+
+/* Every option at once: spec_verify_filter_ref (top_k and top_p may be  */
+/* NULL) plus draw_window [B, 2] (may be NULL): for the final draw of a  */
+/* sampling sequence, the smallest and largest token ids a shift of its  */
+/* uniform by at most `band` could select (ref_draw_window); -1 where    */
+/* there was no sampled draw.                                            */
+int spec_verify_full_ref(const void *target, const void *draft, int dtype,
+                         const int32_t *draft_tokens, const int32_t *draft_len,
+                         const float *temperature, const int32_t *top_k, const float *top_p,
+                         int32_t B, int32_t k, int64_t V, uint64_t seed, uint32_t seq_base,
+                         int32_t *out_tokens, int32_t *num_accepted, int32_t *seq_status,
+                         double *p_g, double *q_g, int32_t *argmax, double *resid_mass,
+                         double *margin_accept, double *margin_draw, double *margin_nucleus,
+                         int32_t *draw_row, int32_t *draw_kind, double band,
+                         int32_t *draw_window)
+{
+    return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_k, top_p,
+                        B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
+                        argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
+                        draw_row, draw_kind, band, draw_window);
 }
 
 /* ------------------------------------------------------------------ */

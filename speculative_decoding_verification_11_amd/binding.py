@@ -133,6 +133,36 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def check_out(out, shapes, device, entry: str) -> tuple:
+    """Validate caller-supplied output tensors before any launch: the C ABI
+    sees only pointers, so a short, non-int32, foreign-device or strided
+    buffer would be overwritten past its end. ``shapes``: one expected shape
+    per tensor. Returns the tensors as a tuple."""
+    if not isinstance(out, (tuple, list)) or len(out) != len(shapes):
+        raise ValueError(f"{entry}: out must be a tuple of {len(shapes)} tensors")
+    for i, (t, shape) in enumerate(zip(out, shapes)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{entry}: out[{i}] must be a tensor")
+        if (tuple(t.shape) != tuple(shape) or t.dtype != torch.int32 or t.device != device
+                or not t.is_contiguous()):
+            raise ValueError(f"{entry}: out[{i}] must be contiguous {list(shape)} int32 on "
+                             f"{device}, got {list(t.shape)} {t.dtype} on {t.device}"
+                             f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+    return tuple(out)
+
+
+def check_workspace(workspace, need: int, device, entry: str):
+    """A caller's workspace must be a contiguous tensor on the call's device;
+    None, or one smaller than ``need`` bytes, is replaced by a new one."""
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device \
+                or not workspace.is_contiguous():
+            raise ValueError(f"{entry}: workspace must be a contiguous tensor on {device}")
+        if workspace.numel() * workspace.element_size() >= need:
+            return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor],
                 draft_tokens: Optional[torch.Tensor], draft_len: Optional[torch.Tensor] = None,
                 temperature: Union[float, torch.Tensor] = 1.0, seed: int = 0, *,
@@ -264,12 +294,11 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
         out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
         num_acc = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
-        out_tokens, num_acc = out
+        out_tokens, num_acc = check_out(out, ((B, k + 1), (B,)), dev, entry)
     need = int(lib.spec_verify_workspace_size(B, k, V, dt))
     if need == 0:
         raise SpecVerifyError(1, "invalid sizes for the workspace query")
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = check_workspace(workspace, need, dev, entry)
 
     aux_t = None
     aux_out = None
@@ -346,12 +375,12 @@ def spec_verify_tree(target: torch.Tensor, parents: torch.Tensor, tokens: torch.
         path_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
         num_acc = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
-        out_tokens, path_nodes, num_acc = out
+        out_tokens, path_nodes, num_acc = check_out(out, ((B, N), (B, N), (B,)), dev,
+                                                    "spec_verify_tree")
     need = int(lib.spec_verify_tree_workspace_size(B, N, V, dt))
     if need == 0:
         raise SpecVerifyError(1, "invalid sizes for the tree workspace query")
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = check_workspace(workspace, need, dev, "spec_verify_tree")
     aux_t, aux_out = None, None
     if aux or events is not None:
         aux_t = TreeAux()
@@ -394,11 +423,11 @@ def spec_prompt_lookup(contexts: torch.Tensor, context_len: torch.Tensor, n_min:
         if (tuple(t.shape) != shape or t.dtype != torch.int32 or t.device != dev
                 or not t.is_contiguous()):
             raise ValueError(f"{name} must be contiguous {list(shape)} int32 on {dev}")
-    if out is None:  # sizes are checked by the library
+    if out is None:
         draft = torch.empty((B, max(k, 0)), dtype=torch.int32, device=dev)
         dlen = torch.empty((B,), dtype=torch.int32, device=dev)
     else:
-        draft, dlen = out
+        draft, dlen = check_out(out, ((B, max(k, 0)), (B,)), dev, "spec_prompt_lookup")
     mn = ms = None
     if match:
         mn = torch.empty((B,), dtype=torch.int32, device=dev)

@@ -17,8 +17,8 @@ pytestmark = [pytest.mark.gpu,
 import speculative_decoding_verification_11_amd as sv  # noqa: E402
 from speculative_decoding_verification_11_amd import workloads as wl  # noqa: E402
 from oracle import parity  # noqa: E402
-from test_gpu_parity import (DEV, NTH, _mixed_batch, batch_to, check, host,  # noqa: E402
-                             raw_batch, say)
+from test_gpu_parity import (DEV, NTH, _mixed_batch, batch_to, check,  # noqa: E402
+                             full_size_batch, host, raw_batch, say)
 
 
 def _run(fn, batch, seed, seq_base=0):
@@ -90,13 +90,11 @@ def test_early_exit_matches_full_path_and_oracle(name):
 
 
 def test_early_exit_full_size_c5():
-    """The benchmark's batch: every sequence against the full path, a sample
-    against the oracle."""
-    w = wl.WORKLOADS["c5"]
-    gb = wl.generate(w, DEV)
-    h = host(gb)
-    rows = list(range(0, w.B, w.B // 64))
-    for seed in wl.philox_seeds("c5", 2):
+    """The benchmark's batch: every sequence against the full path and against
+    the oracle, under 4 Philox seeds."""
+    w, gb, h = full_size_batch("c5")
+    rows = list(range(w.B))
+    for seed in wl.philox_seeds("c5", 4):
         say(f"[case] early exit c5 seed={seed:#x}")
         full = _run(sv.spec_verify, gb, seed)
         ee = _run(sv.spec_verify_early_exit, gb, seed)

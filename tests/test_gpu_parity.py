@@ -1,10 +1,14 @@
 """GPU parity: the HIP library against the fp64 oracle, through the C ABI.
 
-Tolerances (the boundary's contract): p_i(g_i), q_i(g_i) and the residual
-mass S within 1e-5 relative (1e-30 absolute floor for fp32 underflow);
-statuses, greedy argmaxes, accept decisions and token ids bit-exact, except
-draws whose oracle uniform lies within 1e-6 of its threshold or CDF
-boundary, which are flagged and must stay under 1e-4 of all draws.
+Tolerances (oracle/parity.py): p_i(g_i) and q_i(g_i) within 1e-5 relative
+(1e-30 absolute floor for fp32 underflow); the residual mass S within 1e-5
+relative plus 2^-19 absolute (S is a difference of two fp32 softmax rows, so
+its rounding error scales with their total mass, not with S); statuses,
+greedy argmaxes, accept decisions and token ids bit-exact, except draws whose
+oracle uniform lies within 1e-6 of its threshold or CDF boundary. Such a draw
+is flagged; where the two sides part on it, the GPU's token must still lie in
+the oracle's band window (the ids a 1e-6 shift of the uniform reaches). The
+flagged fraction depends only on the data and is reported, not bounded.
 """
 import sys
 
@@ -94,17 +98,28 @@ def test_parity_full_batches(name):
     check(total, name)
 
 
-@pytest.mark.parametrize("name,seeds,sample", [("c4", 8, None), ("c5", 4, 128)])
-def test_parity_full_size_workloads(name, seeds, sample):
-    """Largest shapes, in the launch configuration the benchmark times; the
-    oracle checks every sequence (c4) or an evenly spaced sample (c5)."""
-    w = wl.WORKLOADS[name]
-    gb = wl.generate(w, DEV)
-    h = host(gb)
-    rows = None if sample is None else list(range(0, w.B, w.B // sample))
+_FULL = {}
+
+
+def full_size_batch(name):
+    """One GPU batch of a full-size workload and its host copy, generated once
+    per test session and shared by the test modules that import this one."""
+    if name not in _FULL:
+        w = wl.WORKLOADS[name]
+        gb = wl.generate(w, DEV)
+        _FULL[name] = (w, gb, host(gb))
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_parity_full_size_workloads(name):
+    """Largest shapes, in the launch configuration the benchmark times: every
+    sequence against the oracle under 8 Philox seeds."""
+    w, gb, h = full_size_batch(name)
+    rows = None
     total = parity.Report()
-    for seed in wl.philox_seeds(name, seeds):
-        say(f"[case] {name} seed={seed:#x} B={w.B} k={w.k} V={w.V} {w.dtype} sample={sample}")
+    for seed in wl.philox_seeds(name, 8):
+        say(f"[case] {name} seed={seed:#x} B={w.B} k={w.k} V={w.V} {w.dtype} every sequence")
         g = run_gpu(gb, seed)
         r = parity.oracle_on(h, seed, seqs=rows, nthreads=NTH)
         total.merge(parity.compare(g, r, h["draft_len"], h["temperature"], w.k, rows=rows,
@@ -324,3 +339,23 @@ def test_gpu_accepted_length_matches_printed_value():
     mean = float((gpu["num_accepted"] + 1).mean())
     say(f"[stat] mean tokens/round {mean:.5f} vs {closed:.5f} (se {se:.5f})")
     assert abs(mean - closed) < 5 * se
+
+
+def test_bad_output_tensors_are_rejected_before_any_launch():
+    w = wl.WORKLOADS["c1"]
+    gb = batch_to(wl.generate(w, "cpu"), DEV)
+    args = (gb.target, gb.draft, gb.draft_tokens, gb.draft_len, gb.temperature, 1)
+    B, k = w.B, w.k
+    good = (torch.full((B, k + 1), -7, dtype=torch.int32, device=DEV),
+            torch.full((B,), -7, dtype=torch.int32, device=DEV))
+    for out in ((good[0][:, :k], good[1]),
+                (good[0].to(torch.int64), good[1]),
+                (good[0], good[1].cpu()),
+                (torch.empty((k + 1, B), dtype=torch.int32, device=DEV).t(), good[1])):
+        with pytest.raises(ValueError):
+            sv.spec_verify(*args, out=out)
+    torch.cuda.synchronize()
+    assert (good[0] == -7).all() and (good[1] == -7).all()  # nothing was launched
+    o, n = sv.spec_verify(*args, out=good)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == good[0].data_ptr() and (good[1] >= 0).all()

@@ -18,7 +18,7 @@ pytestmark = [pytest.mark.gpu,
 import speculative_decoding_verification_11_amd as sv  # noqa: E402
 from speculative_decoding_verification_11_amd import workloads as wl  # noqa: E402
 from oracle import parity  # noqa: E402
-from test_gpu_parity import (DEV, NTH, _mixed_batch, batch_to, check, host,  # noqa: E402
+from test_gpu_parity import (DEV, NTH, _mixed_batch, batch_to, check, full_size_batch, host,  # noqa: E402,E501
                              raw_batch, run_gpu, say)
 
 
@@ -81,20 +81,20 @@ def test_top_k_parity_workloads(name, with_top_p):
     check(total, f"top-k {name}")
 
 
-@pytest.mark.parametrize("name,sample", [("c4", None), ("c5", 64)])
-def test_top_k_full_size(name, sample):
-    w = wl.WORKLOADS[name]
-    gb = wl.generate(w, DEV)
-    h = host(gb)
+@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("r", range(4))
+def test_top_k_full_size(name, r):
+    """Every sequence of the full-size batch against the oracle; one Philox
+    seed per test (4 in all)."""
+    w, gb, h = full_size_batch(name)
     top_k = _top_ks(w.B, w.V, (50, 1, 400))
     top_p = np.array([(0.9, 1.0)[b % 2] for b in range(w.B)], np.float32)
-    rows = None if sample is None else list(range(0, w.B, w.B // sample))
-    seed = wl.philox_seeds(name, 1)[0]
-    say(f"[case] top-k {name} seed={seed:#x} sample={sample}")
+    seed = wl.philox_seeds(name, 4)[r]
+    say(f"[case] top-k {name} seed={seed:#x} every sequence")
     g = run_tk(gb, seed, top_k, top_p)
-    r = parity.oracle_on(h, seed, seqs=rows, nthreads=NTH, top_k=top_k, top_p=top_p)
-    check(parity.compare(g, r, h["draft_len"], h["temperature"], w.k, rows=rows,
-                         label=f"{name}/"), f"top-k {name}")
+    ref = parity.oracle_on(h, seed, nthreads=NTH, top_k=top_k, top_p=top_p)
+    check(parity.compare(g, ref, h["draft_len"], h["temperature"], w.k, label=f"{name}/"),
+          f"top-k {name} seed {r}")
 
 
 @pytest.mark.parametrize("V,dtype", [(7, "f32"), (1001, "bf16"), (1001, "f32"), (8193, "f32"),

@@ -111,6 +111,39 @@ def test_binding_rejects_bad_tensors():
         sv.spec_verify(torch.zeros(2, 8), None, None)
 
 
+def test_binding_checks_caller_outputs_and_workspace():
+    """Output tensors the caller passes are checked before any launch: the C
+    ABI sees only pointers, so a short, int64, strided or foreign-device
+    buffer would be written past its end."""
+    import torch
+
+    from speculative_decoding_verification_11_amd.binding import check_out, check_workspace
+
+    dev = torch.device("cpu")
+    good = (torch.empty(4, 6, dtype=torch.int32), torch.empty(4, dtype=torch.int32))
+    assert check_out(good, ((4, 6), (4,)), dev, "e") == good
+    bad = [
+        (torch.empty(4, 5, dtype=torch.int32), good[1]),            # too short
+        (torch.empty(4, 6, dtype=torch.int64), good[1]),            # wrong dtype
+        (torch.empty(6, 4, dtype=torch.int32).t(), good[1]),        # not contiguous
+        (good[0],),                                                  # wrong count
+        (good[0], torch.empty(4, dtype=torch.float32)),              # float counts
+        (good[0], None),
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            check_out(out, ((4, 6), (4,)), dev, "e")
+    with pytest.raises(ValueError):  # wrong device
+        check_out(good, ((4, 6), (4,)), torch.device("meta"), "e")
+    ws = torch.empty(64, dtype=torch.uint8)
+    assert check_workspace(ws, 32, dev, "e") is ws
+    assert check_workspace(ws, 128, dev, "e").numel() == 128  # too small: a new one
+    with pytest.raises(ValueError):
+        check_workspace(torch.empty(8, 16, dtype=torch.uint8).t(), 16, dev, "e")
+    with pytest.raises(ValueError):
+        check_workspace(ws, 16, torch.device("meta"), "e")
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sv.binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):

@@ -171,6 +171,37 @@ def test_inverse_cdf_brute_force(oracle_lib):
     assert x == -1 and S == 0.0
 
 
+def test_draw_window_is_every_reachable_id(oracle_lib):
+    """ref_draw_window against brute force through the inverse CDF: with
+    exact dyadic weights, the ids returned for every uniform in [v - band,
+    v + band] (its ends, and both sides of every CDF boundary inside it) are
+    exactly the ids from lo to hi that carry weight."""
+    rng = np.random.default_rng(19)
+    for _ in range(80):
+        V = int(rng.integers(1, 10))
+        num = rng.integers(0, 5, size=V)
+        if num.sum() == 0:
+            num[int(rng.integers(V))] = 1
+        w = num / 64.0
+        S = float(num.sum()) / 64.0
+        cdf = np.cumsum(num) / num.sum()  # exact: dyadic over a small integer
+        for v in (0.0, 0.25, 0.5, float(rng.uniform(0, 1)), float(cdf[0]), 0.999):
+            for band in (1e-9, 1.0 / 64, 0.2):
+                lo, hi = oracle_lib.draw_window(w, v, band)
+                probes = [min(max(v - band, 0.0), 1 - 2**-30), min(v + band, 1 - 2**-30), v]
+                for c in cdf:
+                    for eps in (-2**-40, 0.0, 2**-40):
+                        u = float(c) + eps
+                        if v - band <= u <= v + band and 0.0 <= u < 1.0:
+                            probes.append(u)
+                seen = {oracle_lib.draw_inverse_cdf(w, u)[0] for u in probes}
+                seen.discard(-1)
+                assert lo == min(seen) and hi == max(seen), (num, v, band, lo, hi, seen)
+                assert all(num[x] > 0 for x in seen)
+    assert oracle_lib.draw_window(np.zeros(3), 0.5, 0.1) == (-1, -1)
+    assert S > 0
+
+
 # --------------------------------------------------------------------------
 # One sampling round, with the uniforms supplied (exact enumeration).
 # --------------------------------------------------------------------------

@@ -136,3 +136,32 @@ def test_status_mismatch_is_reported(run):
     gpu = copy.deepcopy(ref)
     gpu["seq_status"][b] = 2
     assert any("status" in m for m in _cmp(gpu, ref, host).mismatches)
+
+
+def test_flagged_final_draw_must_land_in_the_band_window(run):
+    """A flagged final draw may differ from the oracle's token only within the
+    oracle's band window; a token outside it is a mismatch even though the
+    oracle's margin is below the band."""
+    host, ref = run
+    b = _ok_seq(ref)
+    n = int(ref["num_accepted"][b])
+    tok = int(ref["out_tokens"][b, n])
+    ref2 = copy.deepcopy(ref)
+    ref2["margin_draw"][b] = 1e-8  # as if v sat next to a CDF boundary
+    ref2["draw_window"][b] = (tok, tok + 1)
+    gpu = copy.deepcopy(ref)
+    gpu["out_tokens"][b, n] = tok + 1  # the neighbour inside the window: allowed
+    rep = _cmp(gpu, ref2, host)
+    assert rep.ok(), rep.summary()
+    assert rep.flagged_disagree == 1
+    gpu["out_tokens"][b, n] = (tok + 7) % V  # outside the window: reported
+    rep = _cmp(gpu, ref2, host)
+    assert any("band window" in m for m in rep.mismatches), rep.summary()
+
+
+def test_oracle_window_contains_its_own_token(run):
+    host, ref = run
+    for b in range(B):
+        if ref["seq_status"][b] == parity.SEQ_OK and host["temperature"][b] > 0:
+            lo, hi = ref["draw_window"][b]
+            assert lo <= ref["out_tokens"][b, ref["num_accepted"][b]] <= hi
