@@ -1,17 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the speculative-sampling verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one spec_verify call (row statistics; decision and draw sums;
-locate: three kernels) over one batch of synthetic logits already resident
-in HBM. Prints one JSON line: verified positions per second (B*(k+1) per
-step), the roofline of the dominant kernel (k_rowstats, which reads every
-logit row once: algorithmic bytes over its own mean duration, timed with HIP
-events that the library records around it on the launch stream, on every
---event-every'th timed step: each event pair stalls the stream for a few
-microseconds, which would otherwise count in the step time), and the fp64
-CPU oracle timed on a bounded sample of the same batch on the host cores.
+A step is one spec_verify call (row statistics, decision, draw sums, locate)
+over one batch of synthetic logits already resident in HBM. The default run
+is a parent process that never touches the GPU: it starts one child process
+per workload (c3, c4, c5, in that order), each of which times K steps after
+W warm-up steps, and prints ONE JSON line. The headline is c5, the largest
+configuration; every workload reports its per-call fraction of peak HBM
+bandwidth (algorithmic bytes per step / ms per step / 8 TB/s), the row
+kernel's own fraction (k_rowstats, timed with HIP events the library records
+around it on the launch stream, on every --event-every'th timed step), and a
+CPU baseline: the fp64 oracle timed on the host cores on the same batch,
+whose outputs also give the flagged fraction of that batch's draws.
+
+    python bench.py --workload cN [--extras]
+runs one workload in this process (what each child runs; use it under a
+profiler). --extras adds the other entry points on the same batch (early
+exit always; top-p, top-k, tree and prompt lookup with --extras).
 
     python bench.py --copy-probe BYTES
 runs a plain device copy of known size (the calibration for rocprofv3 HBM
@@ -23,6 +30,7 @@ import argparse
 import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -33,8 +41,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec (B*(k+1)/s) + achieved HBM GB/s vs peak, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD specification
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "k_rowstats_c5_hbm_counters.txt")
+WORKLOADS = ("c3", "c4", "c5")  # the configurations with a bandwidth target
+HEADLINE = "c5"
+
+
 EVENT_EVERY = 4  # set from --event-every
+
+
+def counters_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"k_rowstats_{workload}_hbm_counters.txt")
 
 
 def log(msg: str) -> None:
@@ -70,11 +85,13 @@ def kernel_source_digest() -> str:
 
 def read_counter_traffic(workload: str):
     """HBM bytes per row-statistics launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+    counter summary of this workload, if it was taken on the current kernel
+    source."""
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, _, val = line.partition(":")
             kv[key.strip()] = val.strip()
@@ -86,14 +103,14 @@ def read_counter_traffic(workload: str):
         return None
 
 
-def read_kernel_traffic(*kernels: str):
+def read_kernel_traffic(*kernels: str, workload: str = HEADLINE):
     """Scaled HBM bytes (read + written) per dispatch of the named kernels
-    from the same committed counter summary (taken with bench.py's default
-    workloads), if it was taken on the current kernel source; else None."""
-    if read_counter_traffic("c5") is None:
+    from the workload's committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    if read_counter_traffic(workload) is None:
         return None
     out = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(counters_file(workload)):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) == 5 and cells[0] in kernels:
             try:
@@ -126,39 +143,59 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(batch, seed: int, nseq: int) -> dict:
-    """The oracle on the host cores: all of the batch (up to nseq sequences)
-    on up to 16 threads, and a 64-sequence slice on one thread; each the
-    median of three runs."""
+def cpu_baseline(batch, seed: int, nseq: int, gpu_out: dict) -> dict:
+    """The oracle on the host cores: the batch (up to nseq sequences) on every
+    core this process may use, up to the 16 a one-GPU machine grants each GPU,
+    and a 64-sequence slice on one thread; each the median of three runs.
+    The oracle's outputs of the first run are compared with the GPU's outputs
+    of the same batch and seed: the flagged fraction of the batch's draws
+    (oracle margin below 1e-6), how many flagged draws the two sides decided
+    differently, and whether any draw outside the band differs."""
     import oracle
     from oracle import parity
     from speculative_decoding_verification_11_amd import workloads as wl
 
     nthreads = parity.host_threads(cap=16)
+    visible = len(os.sched_getaffinity(0))
+    first = {}
 
-    def median_time(host, nt):
+    def median_time(host, nt, keep=False):
         times = []
         for _ in range(3):
             t0 = time.perf_counter()
-            oracle.spec_verify_ref(host["target"], host["draft"], host["draft_tokens"],
-                                   host["draft_len"], host["temperature"], seed, seq_base=0,
-                                   nthreads=nt)
+            res = oracle.spec_verify_ref(host["target"], host["draft"], host["draft_tokens"],
+                                         host["draft_len"], host["temperature"], seed,
+                                         seq_base=0, nthreads=nt)
             times.append(time.perf_counter() - t0)
+            if keep and not first:
+                first.update(res)
         return sorted(times)[1]
 
     sample = batch.select(range(min(nseq, batch.B)))
-    dt = median_time(wl.to_host_arrays(sample), nthreads)
+    hs = wl.to_host_arrays(sample)
+    dt = median_time(hs, nthreads, keep=True)
     positions = sample.B * (sample.k + 1)
     one = batch.select(range(min(64, batch.B)))
     dt1 = median_time(wl.to_host_arrays(one), 1)
+    rows = list(range(sample.B))
+    gpu = {key: v[:sample.B] for key, v in gpu_out.items()}
+    rep = parity.compare(gpu, first, hs["draft_len"], hs["temperature"], sample.k, rows=rows)
     return {"value": positions / dt, "unit": "positions/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {sample.B} of {batch.B} sequences of the same batch "
-                      f"({positions} positions), fp64 C oracle, {nthreads} threads, "
+                      f"({positions} positions), fp64 C oracle, {nthreads} threads "
+                      f"({visible} CPUs visible to the process; a one-GPU box grants 16), "
                       f"median of 3: {dt:.2f} s wall",
             "value_1_thread": one.B * (one.k + 1) / dt1,
             "sample_1_thread": f"first {one.B} sequences, one thread, median of 3: "
                                f"{dt1:.2f} s wall",
-            "cpu_model": cpu_model()}
+            "cpu_model": cpu_model(),
+            "parity": {"sequences": rep.sequences, "draws": rep.draws,
+                       "flagged": rep.flagged, "flagged_fraction": rep.flagged_fraction,
+                       "flagged_disagree": rep.flagged_disagree,
+                       "max_abs_dS": rep.max_abs_dS, "max_rel_dS_large": rep.max_rel_dS_large,
+                       "mismatches": len(rep.mismatches),
+                       "note": "GPU outputs of the timed batch and seed against this oracle "
+                               "run; flagged = oracle margin below 1e-6"}}
 
 
 def roof(achieved_gbps: float, what: str) -> dict:
@@ -326,18 +363,22 @@ def bench_lookup(K: int, W: int, cpu: bool) -> dict:
     return res
 
 
-def main() -> int:
+def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--event-every", type=int, default=4,
                     help="record the kernel's HIP event pair on every Nth timed step")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed calls for at least this long before the warmup steps: "
                          "after an idle spell the GPU needs ~25 ms of load to reach its "
                          "steady clocks, and the first calls run up to 4x slower")
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default=None, choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="run this one workload in this process (default: a GPU-free parent "
+                         "runs c3, c4 and c5, each in a child process)")
+    ap.add_argument("--extras", action="store_true",
+                    help="with --workload: also time top-p, top-k, tree and prompt lookup")
     ap.add_argument("--seed", type=lambda s: int(s, 0), default=None)
     ap.add_argument("--cpu-seqs", type=int, default=1024,
                     help="sequences of the batch the CPU oracle baseline runs on")
@@ -353,28 +394,26 @@ def main() -> int:
     ap.add_argument("--no-top-p", action="store_true",
                     help="skip timing the top-p entry point on the same batch")
     ap.add_argument("--copy-probe", type=int, default=0)
-    args = ap.parse_args()
-    global EVENT_EVERY
-    EVENT_EVERY = max(1, args.event_every)
+    return ap.parse_args()
 
-    if args.gpus != 1:
-        log(f"bench.py: --gpus {args.gpus} is not supported: it measures one GPU only. "
-            "Sequences shard across GPUs with no communication: each GPU would run the same "
-            "kernels on its slice of the batch, with seq_base set to the slice's offset.")
-        return 2
+
+def per_call(alg_bytes: int, ms: float) -> dict:
+    """The step's bandwidth over its algorithmic bytes (every needed row read
+    once), as a fraction of peak, and the time 70% of peak would allow."""
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    return {"step_GBps": gbps, "step_frac": gbps / PEAK_HBM_GBPS,
+            "budget_ms_at_70pct": alg_bytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3}
+
+
+def run_workload(args, name: str, extras: bool) -> dict:
+    """Time spec_verify (and, on request, the other entry points) on one
+    workload in this process; returns the JSON object of the run."""
     import torch
-
-    if not torch.cuda.is_available():
-        log("bench.py: no GPU visible")
-        return 1
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return 0
 
     import speculative_decoding_verification_11_amd as sv
     from speculative_decoding_verification_11_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
+    w = wl.WORKLOADS[name]
     seed = args.seed if args.seed is not None else wl.philox_seeds(w.name, 1)[0]
     log(f"[bench] generating {w.name}: {w.description}")
     batch = wl.generate(w, "cuda:0")
@@ -387,13 +426,11 @@ def main() -> int:
     # Footprints below the 256 MiB last-level cache would measure cache, not
     # HBM: rotate through enough copies to exceed 1 GiB.
     copies = [batch]
-    footprint = batch.target.numel() * batch.target.element_size() * 2
     n_copies = max(1, -(-(1 << 30) // max(1, alg_bytes)))
     for _ in range(n_copies - 1):
         copies.append(wl.Batch(w, batch.target.clone(), batch.draft.clone(),
                                batch.draft_tokens.clone(), batch.draft_len.clone(),
                                batch.temperature.clone()))
-    del footprint
 
     hip = hip_runtime()
     K, W = args.steps, args.warmup
@@ -413,7 +450,18 @@ def main() -> int:
     def event_ms():
         return elapsed_ms(hip, [(a.value, b.value) for a, b in ev], K)
 
-    log(f"[bench] settle {args.settle_ms:.0f} ms, then warmup {W} steps, {len(copies)} rotating copies")
+    def timed(fn=sv.spec_verify):
+        for i in range(W):
+            step(i, fn=fn)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None, fn=fn)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K, event_ms()
+
+    log(f"[bench] settle {args.settle_ms:.0f} ms, then warmup {W} steps, {len(copies)} "
+        "rotating copies")
     n_settle = 0
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
@@ -421,33 +469,31 @@ def main() -> int:
             step(n_settle)
             n_settle += 1
         torch.cuda.synchronize()
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
     log(f"[bench] timing {K} steps")
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    k1_ms = event_ms()
+    ms_per_step, k1_ms = timed()
     k1_mean = sum(k1_ms) / len(k1_ms)
     k1_median = k1_ms[len(k1_ms) // 2]
-    ms_per_step = elapsed * 1e3 / K
     achieved = alg_bytes / (k1_mean * 1e-3) / 1e9
-    n_acc = outs[0][1].to(torch.int64)
+    # outputs of the timed batch (copy 0) with diagnostics, for the CPU leg
+    out0, n0, aux0 = sv.spec_verify(batch.target, batch.draft, batch.draft_tokens,
+                                    batch.draft_len, batch.temperature, seed, aux=True)
+    torch.cuda.synchronize()
+    gpu_out = {key: v.cpu().numpy() for key, v in aux0.items()}
+    gpu_out["out_tokens"] = out0.cpu().numpy()
+    gpu_out["num_accepted"] = n0.cpu().numpy()
+    n_acc = n0.to(torch.int64)
     tokens_per_round = float((n_acc + 1).float().mean())
     # The draw re-reads the decided row of every sampled sequence: target
     # and draft row at a rejection, the target row alone for a bonus token.
     n_cpu = n_acc.cpu()
-    final_ok = outs[0][0].cpu().gather(1, n_cpu.view(-1, 1)).view(-1) >= 0
-    sampled_seq = (copies[0].temperature.cpu() > 0) & final_ok
-    resid_seq = sampled_seq & (n_cpu < copies[0].draft_len.cpu().to(torch.int64))
-    draw_rows = int(sampled_seq.sum()) + int(resid_seq.sum())
+    kind = aux0["draw_kind"].cpu()
+    draw_rows = int(((kind == sv.DRAW_RESIDUAL) | (kind == sv.DRAW_RESIDUAL_AS_P)).sum()) * 2 \
+        + int((kind == sv.DRAW_BONUS).sum())
     draw_bytes = draw_rows * w.V * w.elem_bytes
-    log(f"[bench] {ms_per_step:.4f} ms/step; k_rowstats mean {k1_mean * 1e3:.1f} us "
-        f"(median {k1_median * 1e3:.1f}, min {k1_ms[0] * 1e3:.1f}, max {k1_ms[-1] * 1e3:.1f}); "
+    pc = per_call(alg_bytes, ms_per_step)
+    log(f"[bench] {w.name}: {ms_per_step:.4f} ms/step ({pc['step_frac']:.3f} of peak on "
+        f"algorithmic bytes); k_rowstats mean {k1_mean * 1e3:.1f} us (median "
+        f"{k1_median * 1e3:.1f}, min {k1_ms[0] * 1e3:.1f}, max {k1_ms[-1] * 1e3:.1f}); "
         f"{achieved:.0f} GB/s")
 
     early = None
@@ -455,16 +501,7 @@ def main() -> int:
         # The same batch through the early-exit schedule (identical outputs;
         # only the rows up to each sequence's first rejection are read).
         log(f"[bench] early exit: warmup {W} steps, timing {K} steps")
-        for i in range(W):
-            step(i, fn=sv.spec_verify_early_exit)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None,
-                 fn=sv.spec_verify_early_exit)
-        torch.cuda.synchronize()
-        ee_elapsed = time.perf_counter() - t0
-        loop_ms = event_ms()
+        ee_ms, loop_ms = timed(sv.spec_verify_early_exit)
         loop_mean = sum(loop_ms) / len(loop_ms)
         n_ee = outs[0][1].to(torch.int64).cpu()
         L = copies[0].draft_len.to(torch.int64).cpu()
@@ -472,42 +509,33 @@ def main() -> int:
         ee_t = int((n_ee + 1).sum())
         ee_d = int(torch.minimum(n_ee + 1, L)[samp].sum())
         ee_bytes = (ee_t + ee_d) * w.V * w.elem_bytes
-        ee_ms = ee_elapsed * 1e3 / K
         early = {
             "entry_point": "spec_verify_early_exit",
             "value": positions / (ee_ms * 1e-3),
             "unit": "positions/s",
             "ms_per_step": ee_ms,
+            "faster_than_full_step": ee_ms < ms_per_step,
             "rows_read": {"target": ee_t, "draft": ee_d},
             "bytes_read_once": ee_bytes,
             "position_loop_us_mean": loop_mean * 1e3,
             "position_loop_GBps": ee_bytes / (loop_mean * 1e-3) / 1e9,
-            "outputs_identical": bool(torch.equal(n_ee, n_acc.cpu())),
+            "outputs_identical": bool(torch.equal(n_ee, n_cpu)),
             "roofline": roof(ee_bytes / (loop_mean * 1e-3) / 1e9,
                              "the position loop (rows up to each stop, read once), HIP events"),
-            "cpu_baseline": "the oracle of the top-level cpu_baseline (identical outputs)",
+            "cpu_baseline": "the oracle of this workload's cpu_baseline (identical outputs)",
             "hbm_bytes_per_dispatch": read_kernel_traffic("k_ee_rowstats0", "k_ee_rowstats",
-                                                          "k_ee_tail", "k_draw"),
+                                                          "k_ee_tail", "k_draw", workload=name),
         }
         log(f"[bench] early exit {ee_ms:.4f} ms/step; position loop {loop_mean * 1e3:.1f} us "
             f"for {ee_bytes / 1e9:.3f} GB")
-    topp = None
-    if not args.no_top_p:
+    topp = topk = tree = lookup = None
+    if extras and not args.no_top_p:
         # The same batch with top-p 0.95 on every row (the drafted tokens were
         # sampled without it, so a few land outside the draft's nucleus and
         # end their sequence with status QZERO, as the contract says).
         log(f"[bench] top-p 0.95: warmup {W} steps, timing {K} steps")
         tp = torch.full((w.B,), 0.95, dtype=torch.float32, device="cuda:0")
-        for i in range(W):
-            step(i, fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None,
-                 fn=lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
-        torch.cuda.synchronize()
-        tp_ms = (time.perf_counter() - t0) * 1e3 / K
-        tp_pass = event_ms()
+        tp_ms, tp_pass = timed(lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tp, *a[5:], **kw))
         tp_pass_mean = sum(tp_pass) / len(tp_pass)
         _, _, aux_tp = sv.spec_verify_top_p(copies[0].target, copies[0].draft,
                                             copies[0].draft_tokens, copies[0].draft_len,
@@ -521,38 +549,34 @@ def main() -> int:
                 "roofline": roof(alg_bytes / (tp_pass_mean * 1e-3) / 1e9,
                                  "the row pass (k_filter reads each filtered row once; "
                                  "k_rowstats skips them), HIP events"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback", "k_draw")}
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback",
+                                                              "k_draw", workload=name)}
+        # half the sequences unfiltered (top_p = 1): their rows go through
+        # the plain row-statistics pass
+        tph = torch.tensor([(0.95, 1.0)[b % 2] for b in range(w.B)], dtype=torch.float32,
+                           device="cuda:0")
+        tph_ms, _ = timed(lambda *a, **kw: sv.spec_verify_top_p(*a[:5], tph, *a[5:], **kw))
+        topp["mixed_half_unfiltered_ms_per_step"] = tph_ms
         if not args.no_cpu_baseline:
-            import oracle
             from oracle import parity
 
-            n_cpu = 64
-            hs = wl.to_host_arrays(batch.select(range(n_cpu)))
+            n_cpu_seq = 64
+            hs = wl.to_host_arrays(batch.select(range(n_cpu_seq)))
             topp["cpu_baseline"] = timed_oracle(
-                lambda nt: parity.oracle_on(hs, seed, nthreads=nt, top_p=np.full(n_cpu, 0.95,
-                                                                                 np.float32)),
-                n_cpu * (w.k + 1), "positions/s",
-                f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-p")
-        log(f"[bench] top-p {tp_ms:.4f} ms/step; row pass {tp_pass_mean * 1e3:.1f} us")
-    topk = None
-    if not args.no_top_k:
+                lambda nt: parity.oracle_on(hs, seed, nthreads=nt,
+                                            top_p=np.full(n_cpu_seq, 0.95, np.float32)),
+                n_cpu_seq * (w.k + 1), "positions/s",
+                f"first {n_cpu_seq} of {w.B} sequences of the same batch, fp64 C oracle with "
+                "top-p")
+        log(f"[bench] top-p {tp_ms:.4f} ms/step; row pass {tp_pass_mean * 1e3:.1f} us; "
+            f"half unfiltered {tph_ms:.4f} ms/step")
+    if extras and not args.no_top_k:
         # The same batch with top-k 50 and then top-p 0.95 on every row.
         log(f"[bench] top-k 50 + top-p 0.95: warmup {W} steps, timing {K} steps")
         tk = torch.full((w.B,), 50, dtype=torch.int32, device="cuda:0")
         tp = torch.full((w.B,), 0.95, dtype=torch.float32, device="cuda:0")
-
-        def fk(*a, **kw):
-            return sv.spec_verify_top_k_top_p(*a[:5], tk, tp, *a[5:], **kw)
-
-        for i in range(W):
-            step(i, fn=fk)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None, fn=fk)
-        torch.cuda.synchronize()
-        tk_ms = (time.perf_counter() - t0) * 1e3 / K
-        tk_pass = event_ms()
+        tk_ms, tk_pass = timed(
+            lambda *a, **kw: sv.spec_verify_top_k_top_p(*a[:5], tk, tp, *a[5:], **kw))
         tk_pass_mean = sum(tk_pass) / len(tk_pass)
         _, _, aux_tk = sv.spec_verify_top_k_top_p(copies[0].target, copies[0].draft,
                                                   copies[0].draft_tokens, copies[0].draft_len,
@@ -566,32 +590,29 @@ def main() -> int:
                 "roofline": roof(alg_bytes / (tk_pass_mean * 1e-3) / 1e9,
                                  "the row pass (k_filter reads each filtered row once; "
                                  "k_rowstats skips them), HIP events"),
-                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback", "k_draw")}
+                "hbm_bytes_per_dispatch": read_kernel_traffic("k_filter", "k_filter_fallback",
+                                                              "k_draw", workload=name)}
         if not args.no_cpu_baseline:
-            import oracle
             from oracle import parity
 
-            n_cpu = 64
-            hs = wl.to_host_arrays(batch.select(range(n_cpu)))
+            n_cpu_seq = 64
+            hs = wl.to_host_arrays(batch.select(range(n_cpu_seq)))
             topk["cpu_baseline"] = timed_oracle(
                 lambda nt: parity.oracle_on(hs, seed, nthreads=nt,
-                                            top_k=np.full(n_cpu, 50, np.int32),
-                                            top_p=np.full(n_cpu, 0.95, np.float32)),
-                n_cpu * (w.k + 1), "positions/s",
-                f"first {n_cpu} of {w.B} sequences of the same batch, fp64 C oracle with top-k "
-                "and top-p")
+                                            top_k=np.full(n_cpu_seq, 50, np.int32),
+                                            top_p=np.full(n_cpu_seq, 0.95, np.float32)),
+                n_cpu_seq * (w.k + 1), "positions/s",
+                f"first {n_cpu_seq} of {w.B} sequences of the same batch, fp64 C oracle with "
+                "top-k and top-p")
         log(f"[bench] top-k + top-p {tk_ms:.4f} ms/step; row pass {tk_pass_mean * 1e3:.1f} us")
-    tree = None
-    if not args.no_tree:
+    if extras and not args.no_tree:
         tree = bench_tree(hip, ev, K, W, not args.no_cpu_baseline)
-    lookup = None
-    if not args.no_lookup:
+    if extras and not args.no_lookup:
         lookup = bench_lookup(K, W, not args.no_cpu_baseline)
     for a, b in ev:
         hip.hipEventDestroy(a)
         hip.hipEventDestroy(b)
 
-    traffic = read_counter_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": positions / (ms_per_step * 1e-3),
@@ -613,16 +634,13 @@ def main() -> int:
             "valid_positions_per_s": valid_positions / (ms_per_step * 1e-3),
             "rows_read": {"target": t_rows, "draft": d_rows},
             "algorithmic_bytes": alg_bytes,
-            "effective_GBps_whole_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+            "per_call": pc,
             "draw_reread": {
                 "rows": draw_rows,
                 "bytes": draw_bytes,
-                "step_bytes": alg_bytes + draw_bytes,
-                "step_GBps": (alg_bytes + draw_bytes) / (ms_per_step * 1e-3) / 1e9,
-                "step_frac_of_peak": (alg_bytes + draw_bytes) / (ms_per_step * 1e-3) / 1e9
-                                     / PEAK_HBM_GBPS,
-                "note": "every row read once plus the decided row of each sampled sequence "
-                        "read again by the draw, over the wall-clock step",
+                "note": "side figure, not the step's bandwidth: the draw re-reads the decided "
+                        "row of each sampled sequence (target and draft at a rejection, target "
+                        "for a bonus); the algorithmic bytes exclude these re-reads",
             },
             "rotating_copies": len(copies),
             "mean_tokens_per_round": tokens_per_round,
@@ -635,27 +653,95 @@ def main() -> int:
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
+            "traffic": read_counter_traffic(w.name),
             "kernel_us_mean": k1_mean * 1e3,
             "kernel_us_median": k1_median * 1e3,
             "events": f"HIP event pair around k_rowstats on every {EVENT_EVERY}th of the "
                       f"{K} timed steps ({len(k1_ms)} samples)",
         },
     }
-    if early is not None:
-        result["early_exit"] = early
-    if topp is not None:
-        result["top_p"] = topp
-    if topk is not None:
-        result["top_k_top_p"] = topk
-    if tree is not None:
-        result["tree"] = tree
-    if lookup is not None:
-        result["prompt_lookup"] = lookup
+    for key, val in (("early_exit", early), ("top_p", topp), ("top_k_top_p", topk),
+                     ("tree", tree), ("prompt_lookup", lookup)):
+        if val is not None:
+            result[key] = val
     if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequences")
-        result["cpu_baseline"] = cpu_baseline(batch, seed, args.cpu_seqs)
+        log(f"[bench] CPU oracle baseline on {min(args.cpu_seqs, w.B)} sequences")
+        result["cpu_baseline"] = cpu_baseline(batch, seed, args.cpu_seqs, gpu_out)
+    return result
+
+
+def summary(res: dict) -> dict:
+    """Per-workload figures of a child's result for the parent's line."""
+    c = res["config"]
+    out = {"workload": c["workload"], "ms_per_step": res["ms_per_step"],
+           "positions_per_s": res["value"], "valid_positions_per_s": c["valid_positions_per_s"],
+           "algorithmic_bytes": c["algorithmic_bytes"], **c["per_call"],
+           "k_rowstats_us_mean": res["roofline"]["kernel_us_mean"],
+           "k_rowstats_frac": res["roofline"]["frac"],
+           "k_rowstats_traffic": res["roofline"]["traffic"],
+           "draw_reread_bytes": c["draw_reread"]["bytes"]}
+    if "early_exit" in res:
+        out["early_exit_ms_per_step"] = res["early_exit"]["ms_per_step"]
+    if "cpu_baseline" in res:
+        out["flagged"] = res["cpu_baseline"]["parity"]
+    return out
+
+
+def parent(args) -> int:
+    """Run each workload in a child process of its own and print one line.
+    This process never touches the GPU; it starts every child itself."""
+    results = {}
+    for name in WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name,
+               "--steps", str(args.steps), "--warmup", str(args.warmup),
+               "--event-every", str(args.event_every), "--settle-ms", str(args.settle_ms),
+               "--cpu-seqs", str(args.cpu_seqs)]
+        if name == HEADLINE:
+            cmd.append("--extras")
+        for flag in ("no_cpu_baseline", "no_early_exit", "no_tree", "no_lookup", "no_top_k",
+                     "no_top_p"):
+            if getattr(args, flag):
+                cmd.append("--" + flag.replace("_", "-"))
+        if args.seed is not None:
+            cmd += ["--seed", hex(args.seed)]
+        log(f"[bench] child: {' '.join(cmd[1:])}")
+        proc = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+        if proc.returncode != 0:
+            log(f"[bench] child {name} failed with status {proc.returncode}")
+            return proc.returncode or 1
+        lines = [ln for ln in proc.stdout.splitlines() if ln.startswith("{")]
+        results[name] = json.loads(lines[-1])
+    result = results[HEADLINE]
+    result["configs"] = {name: summary(res) for name, res in results.items()}
+    result["configs_note"] = (
+        "each workload timed in its own process (same steps and warm-up); step_frac = "
+        "algorithmic bytes (every needed row read once) / ms_per_step / 8 TB/s; the target is "
+        "0.7 on c3, c4 and c5; the headline value and roofline are c5's")
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def main() -> int:
+    args = parse_args()
+    global EVENT_EVERY
+    EVENT_EVERY = max(1, args.event_every)
+
+    if args.gpus != 1:
+        log(f"bench.py: --gpus {args.gpus} is not supported: it measures one GPU only. "
+            "Sequences shard across GPUs with no communication: each GPU would run the same "
+            "kernels on its slice of the batch, with seq_base set to the slice's offset.")
+        return 2
+    if args.workload is None and not args.copy_probe:
+        return parent(args)
+    import torch
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        return 1
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
+    print(json.dumps(run_workload(args, args.workload, args.extras)), flush=True)
     return 0
 
 
