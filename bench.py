@@ -77,6 +77,42 @@ def hip_runtime():
     return lib
 
 
+class HipEvents:
+    """K pairs of raw hipEvent_t handles for the library to record into,
+    owned in one place: ``close`` destroys them and drops the handles, so a
+    handle can never reach the library after its event is gone (recording
+    into a destroyed event is a use-after-free inside the HIP runtime)."""
+
+    def __init__(self, hip, K: int):
+        self.hip = hip
+        self.pairs = [(ctypes.c_void_p(), ctypes.c_void_p()) for _ in range(K)]
+        for a, b in self.pairs:
+            assert hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert hip.hipEventCreate(ctypes.byref(b)) == 0
+
+    def pair(self, i: int):
+        if self.pairs is None:
+            raise RuntimeError("HIP events used after close()")
+        a, b = self.pairs[i]
+        return a.value, b.value
+
+    def elapsed_ms(self, K: int) -> list:
+        return elapsed_ms(self.hip, [self.pair(i) for i in range(K)], K)
+
+    def close(self):
+        if self.pairs is not None:
+            for a, b in self.pairs:
+                self.hip.hipEventDestroy(a)
+                self.hip.hipEventDestroy(b)
+            self.pairs = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
 def kernel_source_digest() -> str:
     from speculative_decoding_verification_11_amd.build import source_digest
 
@@ -231,7 +267,7 @@ def elapsed_ms(hip, ev, K: int) -> list:
     return sorted(ms)
 
 
-def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
+def bench_tree(ev: HipEvents, K: int, W: int, cpu: bool) -> dict:
     """Greedy tree verification on workload t3: nodes per second, and the
     node-row kernel's bandwidth (each node row read once, HIP events)."""
     import torch
@@ -256,10 +292,10 @@ def bench_tree(hip, ev, K: int, W: int, cpu: bool) -> dict:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None)
+        step(events=ev.pair(i) if sampled(i) else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = elapsed_ms(hip, ev, K)
+    ms = ev.elapsed_ms(K)
     row_mean = sum(ms) / len(ms)
     nodes = int(tb.n_nodes.sum())
     nbytes = tb.bytes_read()
@@ -434,9 +470,7 @@ def run_workload(args, name: str, extras: bool) -> dict:
 
     hip = hip_runtime()
     K, W = args.steps, args.warmup
-    ev = [(ctypes.c_void_p(), ctypes.c_void_p()) for _ in range(K)]
-    for a, b in ev:
-        assert hip.hipEventCreate(ctypes.byref(a)) == 0 and hip.hipEventCreate(ctypes.byref(b)) == 0
+    ev = HipEvents(hip, K)  # destroyed at the end of this workload, before the CPU leg
     ws = torch.empty(sv.workspace_size(w.B, w.k, w.V, w.dtype_code), dtype=torch.uint8,
                      device="cuda:0")
     outs = [(torch.empty((w.B, w.k + 1), dtype=torch.int32, device="cuda:0"),
@@ -447,8 +481,6 @@ def run_workload(args, name: str, extras: bool) -> dict:
         fn(cb.target, cb.draft, cb.draft_tokens, cb.draft_len, cb.temperature, seed,
            workspace=ws, out=outs[i % len(copies)], events=events)
 
-    def event_ms():
-        return elapsed_ms(hip, [(a.value, b.value) for a, b in ev], K)
 
     def timed(fn=sv.spec_verify):
         for i in range(W):
@@ -456,9 +488,9 @@ def run_workload(args, name: str, extras: bool) -> dict:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i, events=(ev[i][0].value, ev[i][1].value) if sampled(i) else None, fn=fn)
+            step(i, events=ev.pair(i) if sampled(i) else None, fn=fn)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / K, event_ms()
+        return (time.perf_counter() - t0) * 1e3 / K, ev.elapsed_ms(K)
 
     log(f"[bench] settle {args.settle_ms:.0f} ms, then warmup {W} steps, {len(copies)} "
         "rotating copies")
@@ -606,12 +638,10 @@ def run_workload(args, name: str, extras: bool) -> dict:
                 "top-k and top-p")
         log(f"[bench] top-k + top-p {tk_ms:.4f} ms/step; row pass {tk_pass_mean * 1e3:.1f} us")
     if extras and not args.no_tree:
-        tree = bench_tree(hip, ev, K, W, not args.no_cpu_baseline)
+        tree = bench_tree(ev, K, W, not args.no_cpu_baseline)
     if extras and not args.no_lookup:
         lookup = bench_lookup(K, W, not args.no_cpu_baseline)
-    for a, b in ev:
-        hip.hipEventDestroy(a)
-        hip.hipEventDestroy(b)
+    ev.close()
 
     result = {
         "metric": METRIC,
