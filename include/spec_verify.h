@@ -36,8 +36,10 @@
  *
  * Memory. Every pointer argument is device memory owned by the caller,
  * except `aux` (a host struct whose members are device pointers). The
- * library allocates nothing and keeps no state between calls; calls on
- * different streams with different workspaces may run concurrently. Inputs
+ * library allocates nothing and keeps no state between calls (the one
+ * exception, spec_verify_noalloc, keeps a static device array per GPU and
+ * its address); calls on different streams with different workspaces may
+ * run concurrently. Inputs
  * are only read. All work is enqueued on `stream` (a hipStream_t, NULL for
  * the default stream); the call does not synchronise.
  *
@@ -66,7 +68,9 @@ typedef enum {
     SPEC_OK = 0,
     SPEC_EINVAL = 1,     /* bad pointer, size, dtype or alignment          */
     SPEC_EWORKSPACE = 2, /* workspace null, misaligned or too small         */
-    SPEC_ELAUNCH = 3     /* a kernel launch failed (see hipGetLastError)    */
+    SPEC_ELAUNCH = 3,    /* a kernel launch failed (see hipGetLastError)    */
+    SPEC_ESCRATCH = 4    /* spec_verify_noalloc: the sizes need more than   */
+                         /* SPEC_NOALLOC_SCRATCH_BYTES of workspace         */
 } spec_status_t;
 
 /* Per-sequence device status codes, written to aux->seq_status. */
@@ -336,6 +340,31 @@ int spec_prompt_lookup(const int32_t *contexts, const int32_t *context_len, int3
                        int32_t T_max, int32_t n_min, int32_t n_max, int32_t k,
                        int32_t *draft_tokens, int32_t *draft_len, int32_t *match_n,
                        int32_t *match_start, void *stream);
+
+/*
+ * spec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs, RNG contract and errors as spec_verify, without
+ * the workspace: the library uses a static device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES per GPU instead (part of the library's code
+ * object, held by every GPU the library runs on until the process ends), and
+ * the call allocates nothing -- no hipMalloc or hipFree, no allocating
+ * library routine. The first call on a GPU looks up that GPU's address of
+ * the array once (hipGetSymbolAddress, with the GPU that owns `stream` made
+ * current for the lookup). Sizes whose spec_verify_workspace_size() exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES return SPEC_ESCRATCH and enqueue nothing; the
+ * default covers B = 1024, k = 7, V = 128256 bf16 (5.9 MB). Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Results are bit-identical to spec_verify's for the same inputs.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+int spec_verify_noalloc(const void *target_logits, const void *draft_logits, int32_t dtype,
+                        const int32_t *draft_tokens, const int32_t *draft_len,
+                        const float *temperature, int32_t B, int32_t k, int32_t V,
+                        uint64_t seed, uint32_t seq_base, int32_t *out_tokens,
+                        int32_t *num_accepted, const spec_verify_aux_t *aux, void *stream);
 
 /* Static, human-readable text for a spec_status_t value. */
 const char *spec_verify_strerror(int status);

@@ -8,6 +8,7 @@ binding. ``workloads`` draws the seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
     BF16, F32, MAX_K, MAX_TREE, MAX_NGRAM, SpecVerifyError, spec_verify, spec_verify_early_exit,
+    spec_verify_noalloc, NOALLOC_SCRATCH_BYTES,
     spec_verify_top_p, spec_verify_top_k_top_p, spec_verify_tree, spec_prompt_lookup, strerror,
     workspace_size, tree_workspace_size, library,
     SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE, SEQ_BAD_TOP_P,

@@ -26,10 +26,12 @@ MAX_NGRAM = 16
 SEQ_OK, SEQ_BAD_TOKEN, SEQ_BAD_LEN, SEQ_BAD_TEMP, SEQ_QZERO, SEQ_BAD_TREE, SEQ_BAD_TOP_P = range(7)
 DRAW_NONE, DRAW_GREEDY, DRAW_RESIDUAL, DRAW_BONUS, DRAW_RESIDUAL_AS_P = range(5)
 
-STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH"}
+STATUS_NAMES = {0: "SPEC_OK", 1: "SPEC_EINVAL", 2: "SPEC_EWORKSPACE", 3: "SPEC_ELAUNCH",
+                4: "SPEC_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SPEC_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = ("spec_verify", "spec_verify_early_exit", "spec_verify_top_p", "spec_verify_top_k_top_p",
-            "spec_verify_workspace_size",
+            "spec_verify_workspace_size", "spec_verify_noalloc",
             "spec_verify_tree", "spec_verify_tree_workspace_size", "spec_prompt_lookup",
             "spec_verify_strerror", "spec_verify_version")
 
@@ -91,6 +93,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
             fn.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
                            ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
             fn.restype = ctypes.c_int
+        lib.spec_verify_noalloc.argtypes = [P, P, i32, P, P, P, i32, i32, i32, u64, u32, P, P,
+                                            ctypes.POINTER(Aux), P]
+        lib.spec_verify_noalloc.restype = ctypes.c_int
         lib.spec_verify_top_p.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, u64, u32, P, P,
                                           ctypes.POINTER(Aux), P, ctypes.c_size_t, P]
         lib.spec_verify_top_p.restype = ctypes.c_int
@@ -174,6 +179,21 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor],
                    seq_base, aux, workspace, out, events)
 
 
+def spec_verify_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor],
+                        draft_tokens: Optional[torch.Tensor],
+                        draft_len: Optional[torch.Tensor] = None,
+                        temperature: Union[float, torch.Tensor] = 1.0, seed: int = 0, *,
+                        seq_base: int = 0, aux: bool = False, out: Optional[tuple] = None,
+                        events: Optional[tuple] = None):
+    """spec_verify without a workspace (C entry point spec_verify_noalloc):
+    the library's static per-GPU scratch is used and nothing is allocated by
+    the call itself (pass ``out`` to allocate nothing here either). Raises
+    SpecVerifyError with SPEC_ESCRATCH when the sizes need more scratch than
+    NOALLOC_SCRATCH_BYTES."""
+    return _verify("spec_verify_noalloc", target, draft, draft_tokens, draft_len, temperature,
+                   seed, seq_base, aux, None, out, events, noalloc=True)
+
+
 def spec_verify_early_exit(target: torch.Tensor, draft: Optional[torch.Tensor],
                            draft_tokens: Optional[torch.Tensor],
                            draft_len: Optional[torch.Tensor] = None,
@@ -247,7 +267,7 @@ def spec_verify_top_k_top_p(target: torch.Tensor, draft: Optional[torch.Tensor],
 
 
 def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, seq_base, aux,
-            workspace, out, events, top_p=None, top_k=None, filters=False):
+            workspace, out, events, top_p=None, top_k=None, filters=False, noalloc=False):
     """Verify B drafted continuations on the GPU.
 
     target [B, k+1, V] and draft [B, k, V]: float32 or bfloat16, contiguous,
@@ -298,7 +318,8 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
     need = int(lib.spec_verify_workspace_size(B, k, V, dt))
     if need == 0:
         raise SpecVerifyError(1, "invalid sizes for the workspace query")
-    workspace = check_workspace(workspace, need, dev, entry)
+    if not noalloc:
+        workspace = check_workspace(workspace, need, dev, entry)
 
     aux_t = None
     aux_out = None
@@ -325,13 +346,13 @@ def _verify(entry, target, draft, draft_tokens, draft_len, temperature, seed, se
             extra = (_ptr(top_k), _ptr(top_p))
         else:
             extra = (top_p.data_ptr(),) if top_p is not None else ()
+        ws_args = () if noalloc else (workspace.data_ptr(), need)
         rc = getattr(lib, entry)(
             target.data_ptr(), _ptr(draft) if k > 0 else None, dt,
             _ptr(draft_tokens) if k > 0 else None, _ptr(draft_len), temp.data_ptr(), *extra,
             B, k, V, ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint32(seq_base & 0xFFFFFFFF),
             out_tokens.data_ptr(), num_acc.data_ptr(),
-            ctypes.byref(aux_t) if aux_t is not None else None,
-            workspace.data_ptr(), need, stream)
+            ctypes.byref(aux_t) if aux_t is not None else None, *ws_args, stream)
     if rc != 0:
         raise SpecVerifyError(rc, strerror(rc))
     if aux:

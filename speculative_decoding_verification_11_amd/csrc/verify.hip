@@ -63,6 +63,8 @@
 // by HBM bandwidth.
 #include "verify.h"
 
+#include <mutex>
+
 namespace spv {
 
 struct DrawShared {
@@ -728,6 +730,18 @@ __global__ __launch_bounds__(kWave) void k_locate(Params p)
 
 }  // namespace spv
 
+// ===========================================================================
+// Allocation-free entry: the workspace is a file-scope device array, one
+// copy per GPU, held until the process ends. Its name is a host-side stand-in
+// for that memory; host code uses only the device address that
+// hipGetSymbolAddress returns for it, looked up once per device with that
+// device current. Nothing in the step needs the workspace cleared (every
+// record is written before it is read within a call), so calls need no
+// clearing launch; calls that overlap on one GPU share the array and race.
+// ===========================================================================
+
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace spv;
@@ -861,13 +875,47 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
 }
 
 
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];  // this device's address of `scratch`, once known
+
+// Device address of `scratch` on the device that owns `stream`.
+int scratch_for_stream(hipStream_t stream, void **out)
+{
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return SPEC_ELAUNCH;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess)
+            return SPEC_EINVAL;
+    } else {
+        dev = cur;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return SPEC_EINVAL;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess)
+            return SPEC_ELAUNCH;
+        void *p = nullptr;
+        const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess)
+            return SPEC_ELAUNCH;
+        if (rc != hipSuccess || !p)
+            return SPEC_ELAUNCH;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return SPEC_OK;
+}
+
 int verify_entry(const void *target_logits, const void *draft_logits, int32_t dtype,
                  const int32_t *draft_tokens, const int32_t *draft_len, const float *temperature,
                  const int32_t *top_k, const float *top_p, int32_t B, int32_t k, int32_t V,
                  uint64_t seed,
                  uint32_t seq_base, int32_t *out_tokens, int32_t *num_accepted,
                  const spec_verify_aux_t *aux, void *workspace, size_t workspace_bytes,
-                 void *stream, bool early_exit)
+                 void *stream, bool early_exit, bool use_scratch = false)
 {
     Layout lay;
     if (!layout_for(B, k, V, dtype, &lay))
@@ -884,6 +932,15 @@ int verify_entry(const void *target_logits, const void *draft_logits, int32_t dt
         (draft_tokens && !aligned(draft_tokens, 4)) || (draft_len && !aligned(draft_len, 4)) ||
         !aligned(top_p, 4) || !aligned(top_k, 4))
         return SPEC_EINVAL;
+    if (use_scratch) {
+        // allocation-free entry: the static scratch, after every host check
+        if (lay.total > (size_t)SPEC_NOALLOC_SCRATCH_BYTES)
+            return SPEC_ESCRATCH;
+        const int rc = scratch_for_stream(static_cast<hipStream_t>(stream), &workspace);
+        if (rc != SPEC_OK)
+            return rc;
+        workspace_bytes = (size_t)SPEC_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
         return SPEC_EWORKSPACE;
 
@@ -985,6 +1042,18 @@ extern "C" int spec_verify_early_exit(const void *target_logits, const void *dra
                         workspace, workspace_bytes, stream, true);
 }
 
+extern "C" int spec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                                   int32_t dtype, const int32_t *draft_tokens,
+                                   const int32_t *draft_len, const float *temperature, int32_t B,
+                                   int32_t k, int32_t V, uint64_t seed, uint32_t seq_base,
+                                   int32_t *out_tokens, int32_t *num_accepted,
+                                   const spec_verify_aux_t *aux, void *stream)
+{
+    return verify_entry(target_logits, draft_logits, dtype, draft_tokens, draft_len, temperature,
+                        nullptr, nullptr, B, k, V, seed, seq_base, out_tokens, num_accepted, aux,
+                        nullptr, 0, stream, false, true);
+}
+
 extern "C" size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, int32_t dtype)
 {
     Layout lay;
@@ -998,6 +1067,9 @@ extern "C" const char *spec_verify_strerror(int status)
     case SPEC_EINVAL: return "invalid argument (null pointer, size, dtype or alignment)";
     case SPEC_EWORKSPACE: return "workspace null, misaligned or smaller than spec_verify_workspace_size()";
     case SPEC_ELAUNCH: return "kernel launch failed";
+    case SPEC_ESCRATCH:
+        return "sizes need more workspace than spec_verify_noalloc's static scratch "
+               "(SPEC_NOALLOC_SCRATCH_BYTES); use spec_verify with a workspace";
     default: return "unknown status";
     }
 }
