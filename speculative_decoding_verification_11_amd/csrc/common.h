@@ -282,6 +282,83 @@ struct RowShared {
 // ===========================================================================
 // Row statistics of one chunk: returns the block's partial in thread 0.
 // ===========================================================================
+// Pieces shared by the general chunk pass and the full-chunk pass from
+// preloaded registers, so that both give bit-identical partials.
+
+// The softmax update of one block of kTiles 16-byte vectors per lane.
+template <class D>
+__device__ __forceinline__ void block_soft(Soft &st, const u32x4 (&r)[kTiles], float scale)
+{
+    constexpr int NX = kTiles * D::kVec;
+    float x[NX];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+        float f[D::kVec];
+        D::unpack(r[u], f);
+#pragma unroll
+        for (int j = 0; j < D::kVec; ++j)
+            x[u * D::kVec + j] = f[j];
+    }
+    soft_update(st, x, scale);
+}
+
+// The argmax update of one block; i0 is the id of the lane's first element
+// of tile 0 (tile u starts u * kThreads vectors later).
+template <class D>
+__device__ __forceinline__ void block_argmax(ArgMax &am, const u32x4 (&r)[kTiles], int32_t i0)
+{
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+        float f[D::kVec];
+        D::unpack(r[u], f);
+        const int32_t iu = i0 + u * kThreads * D::kVec;
+#pragma unroll
+        for (int j = 0; j < D::kVec; ++j)
+            if (f[j] > am.v) am = ArgMax{f[j], iu + j};
+    }
+}
+
+// Workgroup combines (waves through LDS), result in thread 0.
+__device__ __forceinline__ float2 reduce_soft(Soft st, float scale, RowShared &sh, int tid)
+{
+    float2 out = make_float2(0.f, 0.f);
+    st = wave_soft(st, scale);
+    if ((tid & (kWave - 1)) == 0) {
+        sh.a[tid / kWave] = st.m;
+        sh.b[tid / kWave] = st.z;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        Soft acc{sh.a[0], sh.b[0]};
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            acc = soft_merge(acc, Soft{sh.a[w], sh.b[w]}, scale);
+        out = make_float2(acc.m, acc.z);
+    }
+    __syncthreads();  // sh is reused by the caller
+    return out;
+}
+
+__device__ __forceinline__ float2 reduce_argmax(ArgMax am, RowShared &sh, int tid)
+{
+    float2 out = make_float2(0.f, 0.f);
+    am = wave_argmax(am);
+    if ((tid & (kWave - 1)) == 0) {
+        sh.a[tid / kWave] = am.v;
+        sh.b[tid / kWave] = __int_as_float(am.i);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        ArgMax acc{sh.a[0], __float_as_int(sh.b[0])};
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            acc = argmax_merge(acc, ArgMax{sh.a[w], __float_as_int(sh.b[w])});
+        out = make_float2(acc.v, __int_as_float(acc.i));
+    }
+    __syncthreads();  // sh is reused by the caller
+    return out;
+}
+
 // `tid` in [0, kThreads): the lane's index among the kThreads lanes that
 // share `sh` (two such groups may share a workgroup, calling in step: the
 // function's barriers are workgroup-wide).
@@ -290,11 +367,9 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
                                               bool greedy, float scale, RowShared &sh,
                                               int tid = (int)threadIdx.x)
 {
-    constexpr int NX = kTiles * D::kVec;
     const Span sp = make_span<D>(row, s, e);
     const u32x4 *vrow = reinterpret_cast<const u32x4 *>(row + sp.a);
     const u32x4 pad = {D::kNegInfWord, D::kNegInfWord, D::kNegInfWord, D::kNegInfWord};
-    float2 out = make_float2(0.f, 0.f);
 
     // A full block of kThreads * kTiles groups (every chunk but a row's last)
     // loads without per-load masking; a partial one pads with -inf, which
@@ -318,16 +393,7 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
         for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
             u32x4 r[kTiles];
             load_block(base, r);
-            float x[NX];
-#pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                float f[D::kVec];
-                D::unpack(r[u], f);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j)
-                    x[u * D::kVec + j] = f[j];
-            }
-            soft_update(st, x, scale);
+            block_soft<D>(st, r, scale);
         }
         {
             float x[2];
@@ -337,59 +403,74 @@ __device__ __forceinline__ float2 chunk_stats(const typename D::Elem *row, int64
             if (x[0] != -INFINITY || x[1] != -INFINITY)
                 soft_update(st, x, scale);
         }
-        st = wave_soft(st, scale);
-        if ((tid & (kWave - 1)) == 0) {
-            sh.a[tid / kWave] = st.m;
-            sh.b[tid / kWave] = st.z;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            Soft acc{sh.a[0], sh.b[0]};
+        return reduce_soft(st, scale, sh, tid);
+    }
+    ArgMax am{-INFINITY, INT32_MAX};
+    // head, vectors, tail: each thread sees ascending ids
+    if (sp.s + tid < sp.a) {
+        const float x = D::at(row, sp.s + tid);
+        if (x > am.v) am = ArgMax{x, (int32_t)(sp.s + tid)};
+    }
+    for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
+        u32x4 r[kTiles];
+        load_block(base, r);
+        block_argmax<D>(am, r, (int32_t)(sp.a + (base + tid) * D::kVec));
+    }
+    if (sp.z + tid < sp.e) {
+        const float x = D::at(row, sp.z + tid);
+        if (x > am.v) am = ArgMax{x, (int32_t)(sp.z + tid)};
+    }
+    return reduce_argmax(am, sh, tid);
+}
+
+// Whether [s, e) of `row` is read by chunk_stats as one block and nothing
+// else: 16-byte aligned at s, a whole number of vectors, at most one block
+// (every chunk of a row with 16-byte aligned rows and V a multiple of kVec,
+// its last chunk included).
+template <class D>
+__device__ inline bool single_block(const typename D::Elem *row, int64_t s, int64_t e)
+{
+    return ((uintptr_t)(row + s) & 15u) == 0 && (e - s) % D::kVec == 0 &&
+           e - s <= (int64_t)kThreads * kTiles * D::kVec;
+}
+
+// The loads of such a chunk, padded with -inf past its end as chunk_stats
+// pads a partial block.
+template <class D>
+__device__ __forceinline__ void load_single_block(const typename D::Elem *row, int64_t s,
+                                                  int64_t e, int tid, u32x4 (&r)[kTiles])
+{
+    const u32x4 *blk = reinterpret_cast<const u32x4 *>(row + s);
+    const int ngroups = (int)((e - s) / D::kVec);
+    if (ngroups == kThreads * kTiles) {
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                acc = soft_merge(acc, Soft{sh.a[w], sh.b[w]}, scale);
-            out = make_float2(acc.m, acc.z);
-        }
+        for (int u = 0; u < kTiles; ++u)
+            r[u] = stream_load(blk + (uint32_t)(u * kThreads + tid));
     } else {
-        ArgMax am{-INFINITY, INT32_MAX};
-        // head, vectors, tail: each thread sees ascending ids
-        if (sp.s + tid < sp.a) {
-            const float x = D::at(row, sp.s + tid);
-            if (x > am.v) am = ArgMax{x, (int32_t)(sp.s + tid)};
-        }
-        for (int64_t base = 0; base < sp.ngroups; base += (int64_t)kThreads * kTiles) {
-            u32x4 r[kTiles];
-            load_block(base, r);
+        const u32x4 pad = {D::kNegInfWord, D::kNegInfWord, D::kNegInfWord, D::kNegInfWord};
 #pragma unroll
-            for (int u = 0; u < kTiles; ++u) {
-                float f[D::kVec];
-                D::unpack(r[u], f);
-                const int32_t i0 = (int32_t)(sp.a + (base + u * kThreads + tid) * D::kVec);
-#pragma unroll
-                for (int j = 0; j < D::kVec; ++j)
-                    if (f[j] > am.v) am = ArgMax{f[j], i0 + j};
-            }
-        }
-        if (sp.z + tid < sp.e) {
-            const float x = D::at(row, sp.z + tid);
-            if (x > am.v) am = ArgMax{x, (int32_t)(sp.z + tid)};
-        }
-        am = wave_argmax(am);
-        if ((tid & (kWave - 1)) == 0) {
-            sh.a[tid / kWave] = am.v;
-            sh.b[tid / kWave] = __int_as_float(am.i);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            ArgMax acc{sh.a[0], __float_as_int(sh.b[0])};
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                acc = argmax_merge(acc, ArgMax{sh.a[w], __float_as_int(sh.b[w])});
-            out = make_float2(acc.v, __int_as_float(acc.i));
+        for (int u = 0; u < kTiles; ++u) {
+            const int vi = u * kThreads + tid;
+            r[u] = vi < ngroups ? stream_load(blk + vi) : pad;
         }
     }
-    __syncthreads();  // sh is reused by the caller
-    return out;
+}
+
+// chunk_stats of a single-block chunk whose block is already loaded: the
+// same arithmetic (such a chunk has no head or tail elements).
+template <class D>
+__device__ __forceinline__ float2 chunk_stats_loaded(int64_t s, bool greedy, float scale,
+                                                     RowShared &sh, int tid,
+                                                     const u32x4 (&r)[kTiles])
+{
+    if (!greedy) {
+        Soft st{-INFINITY, 0.f};
+        block_soft<D>(st, r, scale);
+        return reduce_soft(st, scale, sh, tid);
+    }
+    ArgMax am{-INFINITY, INT32_MAX};
+    block_argmax<D>(am, r, (int32_t)(s + tid * D::kVec));
+    return reduce_argmax(am, sh, tid);
 }
 
 }  // namespace spv

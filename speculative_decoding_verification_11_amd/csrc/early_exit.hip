@@ -21,27 +21,30 @@ namespace spv {
 // position's launch only streams listed sequences.
 // ===========================================================================
 
-// Exchange of partials inside one launch: device-scope (write-through)
-// stores and loads, and a writer drains its stores (s_waitcnt) before the
-// relaxed device-scope count that tells the last workgroup to read them.
-// Agent-scope release/acquire would write back / invalidate the whole L2 of
-// the workgroup's XCD each time instead.
-__device__ inline void publish_float2(float2 *ptr, float2 v)
+// Partials are exchanged inside one launch with the agent-coherent accesses
+// of verify.h (st_f2<true> / ld_f2<true>, drain_stores, counter_add).
+__device__ inline void publish_float2(float2 *ptr, float2 v) { st_f2<true>(ptr, v); }
+__device__ inline float2 fetch_float2(const float2 *ptr) { return ld_f2<true>(ptr); }
+#ifndef SPEC_EE_FORMAL
+#define SPEC_EE_FORMAL 0
+#endif
+// Count of a published partial; returns the count before the add.
+__device__ inline int count_published(int32_t *ctr)
 {
-    const uint64_t bits = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(ptr), bits, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+#if SPEC_EE_FORMAL
+    const int before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    drain_stores();  // the partial is visible before the count
+    const int before = counter_add(ctr, 1);
+#endif
+    return before;
 }
-__device__ inline float2 fetch_float2(const float2 *ptr)
+// The last arriver, before it reads the others' partials.
+__device__ inline void acquire_published()
 {
-    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(ptr), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-__device__ inline void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ inline int counter_add(int32_t *ptr, int32_t v)
-{
-    return __hip_atomic_fetch_add(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#if SPEC_EE_FORMAL
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
 }
 
 // Row-statistics chunks of sequence b at position i.
@@ -172,6 +175,9 @@ __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float
     dec.zt = ts.z;
     dec.md = ds.m;
     dec.zd = ds.z;
+    if (!drafted)  // a bonus draw: its chunk from the row statistics, as in decide()
+        bonus_chunk(nc, v, ts.m, ts.z, scale, lane, [&](int c) { return partial(pt + c); },
+                    dec.chunk, dec.mass, dec.base, dec.total);
     ee_stop(p, b, i, SPEC_SEQ_OK, dec, false, 0, drafted ? i + 1 : L, 0, lane);
     return false;
 }
@@ -305,12 +311,12 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
     if (lane == 0) {
         publish_float2(p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc + c,
                        part);
-        drain_stores();  // the partial is visible before the count
         const int items = ee_items(nc, tau == 0.f, i, L);
-        last = counter_add(p.ee_done + (int64_t)i * p.B + b, 1) == items - 1;
+        last = count_published(p.ee_done + (int64_t)i * p.B + b) == items - 1;
     }
     if (!__shfl(last, 0, kWave))
         return;
+    acquire_published();
     // The last chunk of the sequence's rows: the first wave decides.
     if (ee_decide<D>(p, b, i, L, tau, true, lane) && i < k && lane == 0)
         ee_enlist(p, b, i + 1);
@@ -350,14 +356,14 @@ __global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
     if (lane == 0) {
         publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c,
                        part);
-        drain_stores();  // the partial is visible before the count
         int items = 0;
         for (int x = P; x <= L; ++x)
             items += ee_items(nc, greedy, x, L);
-        last = counter_add(p.ee_done + (int64_t)P * p.B + b, 1) == items - 1;
+        last = count_published(p.ee_done + (int64_t)P * p.B + b) == items - 1;
     }
     if (!__shfl(last, 0, kWave))
         return;
+    acquire_published();
     // The last chunk of the sequence's rows: the first wave decides
     // positions P, P + 1, ... up to the stop.
     for (int x = P; x <= L; ++x)

@@ -207,6 +207,13 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
             dec.zd = __shfl(dz, j, kWave);
             dec.tht = __shfl(tth, j, kWave);
             dec.thd = __shfl(dth, j, kWave);
+            if (dec.kind == SPEC_DRAW_BONUS && !seq_filtered(p, b)) {
+                // every lane reads the bonus row's partials and gets the same
+                const float2 *pb = p.partials + (b * rows + j) * (int64_t)nc;
+                bonus_chunk(nc, dec.v, dec.mt, dec.zt, scale, lane,
+                            [&](int c) { return pb[c]; }, dec.chunk, dec.mass, dec.base,
+                            dec.total);
+            }
             if (write && lane == 0)
                 p.num_accepted[b] = j;
         }
@@ -521,45 +528,60 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 
     // Chunk level (every lane runs the same scalar loop over LDS).
     auto mass = [&](int q) { return staged ? sh.cm[q] : mw[q]; };
-    double Sw = 0.0, Sp = 0.0;
-    for (int c = 0; c < nc; ++c) {
-        Sw += mass(2 * c);
-        Sp += mass(2 * c + 1);
-    }
     int kind = dec.kind;
     bool use_p = !r.resid;
-    if (r.resid && !(Sw > 0.0)) {  // residual mass rounded away: draw from p
-        use_p = true;
-        kind = SPEC_DRAW_RESIDUAL_AS_P;
-    }
-    const int sel = use_p ? 1 : 0;
-    const double S = use_p ? Sp : Sw;
-    const double t = (double)dec.v * S;
-    double base = 0.0;
+    double S, t, base = 0.0;
     int cs = -1;
-    for (int c = 0; c < nc; ++c) {  // first chunk whose cumulative weight exceeds t
-        const double m = mass(2 * c + sel);
-        if (base + m > t) {
-            cs = c;
-            break;
+    bool fallback = false;
+    const bool located = dec.chunk >= 0;  // a bonus draw whose chunk the decision found
+    if (located) {
+        S = dec.total;
+        t = (double)dec.v * S;
+        cs = dec.chunk;
+    } else {
+        double Sw = 0.0, Sp = 0.0;
+        for (int c = 0; c < nc; ++c) {
+            Sw += mass(2 * c);
+            Sp += mass(2 * c + 1);
         }
-        base += m;
-    }
-    bool fallback = cs < 0;
-    if (fallback) {  // no crossing: the last chunk with weight
-        cs = nc - 1;
-        for (int c = nc - 1; c >= 0; --c)
-            if (mass(2 * c + sel) > 0.0) {
+        if (r.resid && !(Sw > 0.0)) {  // residual mass rounded away: draw from p
+            use_p = true;
+            kind = SPEC_DRAW_RESIDUAL_AS_P;
+        }
+        S = use_p ? Sp : Sw;
+        t = (double)dec.v * S;
+        for (int c = 0; c < nc; ++c) {  // first chunk whose cumulative weight exceeds t
+            const double m = mass(2 * c + (use_p ? 1 : 0));
+            if (base + m > t) {
                 cs = c;
                 break;
             }
+            base += m;
+        }
+        fallback = cs < 0;
+        if (fallback) {  // no crossing: the last chunk with weight
+            cs = nc - 1;
+            for (int c = nc - 1; c >= 0; --c)
+                if (mass(2 * c + (use_p ? 1 : 0)) > 0.0) {
+                    cs = c;
+                    break;
+                }
+        }
     }
+    const int sel = use_p ? 1 : 0;
     const int64_t s = (int64_t)cs * CH, e = min64((int64_t)p.V, s + CH);
     const Span sp = make_span2<D>(r.t, r.d, s, e);
 
     // Segment level: one segment sum per lane, scanned in order.
     const double *segs = p.segs + (b * (int64_t)nc + cs) * (2 * kSegs) + sel * kSegs;
     const double sv = lane < kSegs ? segs[lane] : 0.0;
+    if (located) {
+        // the chunk's own weights, scaled to its mass from the row
+        // statistics: the crossing inside it is at (t - base) / mass of them
+        const double in = wave_sum(sv);
+        t = (t - dec.base) * (in / (double)dec.mass);
+        base = 0.0;
+    }
     const double sincl = wave_inclusive_scan(sv, lane);
     int sg = -1;
     if (!fallback) {
@@ -649,8 +671,23 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 // ===========================================================================
 // The step.
 // ===========================================================================
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
+// Two chunks of one row per workgroup (chunks 2j and 2j + 1): when both are
+// single blocks, the second one's loads are issued before the first one is
+// reduced, so the workgroup has a chunk in flight through each reduction and
+// its barriers; and the workgroups of rows the step does not need, which
+// only read the sequence's length and temperature, are half as many. Each
+// chunk's partial is the one chunk_stats gives.
+// Row-statistics grids of at least this many chunks take two chunks per
+// workgroup; smaller ones (a few rounds of the chip or less) keep one per
+// workgroup, since fewer, longer workgroups there lengthen the tail.
+constexpr int64_t kRowPairChunks = 16384;
+
+// Chunks (1 or 2) per workgroup; with 2 the kernel is compiled for at least 5
+// waves per SIMD (96 VGPRs): without that bound the compiler keeps both
+// chunks' values live at once and runs 4.
+template <class D, int Chunks>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Chunks == 2 ? 5 : 1, 8))) void k_rowstats(Params p)
 {
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
@@ -659,8 +696,9 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     // 32-bit decode of the grid index (64-bit division is a long scalar
     // sequence every workgroup would run before its first load).
-    const int c = (int)(item % (uint32_t)nc);
-    const uint32_t rs = item / (uint32_t)nc;
+    const uint32_t np = (uint32_t)(nc + Chunks - 1) / (uint32_t)Chunks;
+    const int c0 = Chunks * (int)(item % np), c1 = c0 + 1;
+    const uint32_t rs = item / np;
     const int slot = (int)(rs % (uint32_t)rows);
     const int64_t b = rs / (uint32_t)rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
@@ -675,11 +713,43 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Params p)
 
     const E *row = is_target ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
                              : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
-    const int64_t s = (int64_t)c * CH;
-    const float2 part = chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy,
-                                       greedy ? 0.f : temp_scale(tau), sh);
-    if (threadIdx.x == 0)
-        p.partials[item] = part;
+    const float scale = greedy ? 0.f : temp_scale(tau);
+    const int tid = threadIdx.x;
+    float2 *out = p.partials + (b * rows + slot) * (int64_t)nc;
+    const int64_t s0 = (int64_t)c0 * CH, e0 = min64((int64_t)p.V, s0 + CH);
+    const int64_t s1 = e0, e1 = min64((int64_t)p.V, s1 + CH);
+    const bool two = Chunks == 2 && c1 < nc;
+    if (Chunks == 2 && single_block<D>(row, s0, e0) && (!two || single_block<D>(row, s1, e1))) {
+        // chunk 0's values fold into the lane's (max, sum) or argmax; then
+        // chunk 1's loads go out, in flight through chunk 0's reduction
+        u32x4 r[kTiles];
+        load_single_block<D>(row, s0, e0, tid, r);
+        Soft st{-INFINITY, 0.f};
+        ArgMax am{-INFINITY, INT32_MAX};
+        if (greedy)
+            block_argmax<D>(am, r, (int32_t)(s0 + tid * D::kVec));
+        else
+            block_soft<D>(st, r, scale);
+        if (two)
+            load_single_block<D>(row, s1, e1, tid, r);
+        const float2 v0 = greedy ? reduce_argmax(am, sh, tid) : reduce_soft(st, scale, sh, tid);
+        if (tid == 0)
+            out[c0] = v0;
+        if (two) {
+            const float2 v1 = chunk_stats_loaded<D>(s1, greedy, scale, sh, tid, r);
+            if (tid == 0)
+                out[c1] = v1;
+        }
+        return;
+    }
+    const float2 v0 = chunk_stats<D>(row, s0, e0, greedy, scale, sh);
+    if (tid == 0)
+        out[c0] = v0;
+    if (two) {
+        const float2 v1 = chunk_stats<D>(row, s1, e1, greedy, scale, sh);
+        if (tid == 0)
+            out[c1] = v1;
+    }
 }
 
 // One wave per sequence (large batches: see kFoldDecisionItems).
@@ -717,6 +787,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p)
     }
     if (dec.kind != SPEC_DRAW_RESIDUAL && dec.kind != SPEC_DRAW_BONUS)
         return;  // greedy or error: the decision wrote everything
+    if (dec.chunk >= 0 && c != dec.chunk)
+        return;  // a located bonus draw: only its chunk is read
     chunk_weight_sums<D>(p, b, c, dec, sh);
 }
 
@@ -837,8 +909,13 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                 hipLaunchKernelGGL(k_filter_fallback<D>, dim3((unsigned)(nb * rows)),
                                    dim3(kNucThreads), 0, stream, p);
             } else {
-                hipLaunchKernelGGL(k_rowstats<D>, dim3((unsigned)p.n_row_items), dim3(kThreads),
-                                   0, stream, p);
+                if (p.n_row_items >= kRowPairChunks)
+                    hipLaunchKernelGGL((k_rowstats<D, 2>),
+                                       dim3((unsigned)(nb * rows * (int64_t)((nc + 1) / 2))),
+                                       dim3(kThreads), 0, stream, p);
+                else
+                    hipLaunchKernelGGL((k_rowstats<D, 1>), dim3((unsigned)p.n_row_items),
+                                       dim3(kThreads), 0, stream, p);
                 if (filters)
                     hipLaunchKernelGGL(k_nucleus<D>, dim3((unsigned)(nb * rows)),
                                        dim3(kNucThreads), 0, stream, p);
