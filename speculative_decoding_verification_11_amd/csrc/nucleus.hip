@@ -557,7 +557,7 @@ __device__ inline void scan_pair(uint64_t &c, uint64_t &m, CountShared &sh)
 // every row and read by k_filter_fallback: settled by the counts, or nothing
 // to do; radix passes needed, with the row max in the record; radix passes
 // needed after a pass for the row max (NaN or a value at or above 2^18);
-// the row statistics of a row without a filter.
+// a row without a filter (k_rowstats gives its row statistics).
 constexpr float kSettled = 0.f, kRadix = 1.f, kRadixMax = 2.f, kRowStats = 3.f;
 
 // Per-row set-up shared by k_filter and k_filter_fallback.
@@ -601,11 +601,11 @@ __device__ inline FilterRow<D> filter_row(const Params &p)
 }
 
 // One workgroup per row of a call with top-k or top-p parameters (bf16
-// logits), in place of k_rowstats: for a row of a sampling sequence with a
-// filter, the counting pass and the thresholds from the counts, with the
-// row max. What the counts cannot settle, and the rows without a filter,
-// are left to k_filter_fallback (kept apart so that this kernel's
-// registers hold its loop without spilling).
+// logits): for a row of a sampling sequence with a filter, the counting pass
+// and the thresholds from the counts, with the row max. What the counts
+// cannot settle is left to k_filter_fallback (kept apart so that this
+// kernel's registers hold its loop without spilling); the rows without a
+// filter are left to k_rowstats.
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
 {
@@ -847,35 +847,18 @@ radix:
 }
 
 // One workgroup per row of a call with top-k or top-p parameters (bf16
-// logits), after k_filter: the row statistics of the rows without a filter
-// (as k_rowstats gives them, two chunks at a time, one per half of the
-// workgroup), and the radix passes for the filtered rows k_filter flagged.
+// logits), after k_filter: the radix passes for the filtered rows k_filter
+// flagged. (The rows without a filter get their row statistics from
+// k_rowstats, launched after this kernel.)
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter_fallback(Params p)
 {
-    static_assert(kNucThreads == 2 * kThreads, "two row-statistics groups per workgroup");
     __shared__ NucleusShared sh;
-    __shared__ RowShared half_sh[2];
     const float4 rec = p.nucleus[blockIdx.x];
-    if (rec.w == kSettled)
-        return;  // most rows: one read
+    if (rec.w == kSettled || rec.w == kRowStats)
+        return;  // most rows: one read (k_rowstats reads the unfiltered ones)
     const FilterRow<D> f = filter_row<D>(p);
     const int tid = threadIdx.x;
-    if (rec.w == kRowStats) {
-        constexpr int64_t CH = chunk_elems<D>();
-        const int half = tid / kThreads, ht = tid % kThreads;
-        const float scale = f.greedy ? 0.f : temp_scale(f.tau);
-        float2 *const part = p.partials + (int64_t)blockIdx.x * p.nc;
-        for (int c0 = 0; c0 < p.nc; c0 += 2) {
-            const int c = c0 + half;  // past the last chunk: an empty range
-            const int64_t s = min64((int64_t)c * CH, (int64_t)p.V);
-            const float2 v = chunk_stats<D>(f.row, s, min64((int64_t)p.V, s + CH), f.greedy,
-                                            scale, half_sh[half], ht);
-            if (ht == 0 && c < p.nc)
-                part[c] = v;
-        }
-        return;
-    }
     const float scale = temp_scale(f.tau);
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
     const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0

@@ -188,6 +188,7 @@ struct Params {
     int32_t *ee_list;     // [k+1][B]: early exit: sequences to stream at each position
     int32_t *ee_done;     // [k+1][B]: early exit: chunks finished per position
     int32_t decide_in_draw;  // k_draw takes the decisions itself (small batches)
+    int32_t skip_filtered;   // k_rowstats leaves the rows k_filter reads (bf16 filter calls)
     int32_t *out_tokens, *num_accepted;
     AuxDev aux;
 };

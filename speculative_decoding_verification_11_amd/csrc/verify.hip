@@ -682,12 +682,20 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 // workgroup, since fewer, longer workgroups there lengthen the tail.
 constexpr int64_t kRowPairChunks = 16384;
 
-// Chunks (1 or 2) per workgroup; with 2 the kernel is compiled for at least 5
-// waves per SIMD (96 VGPRs): without that bound the compiler keeps both
-// chunks' values live at once and runs 4.
+// Chunks consecutive chunks of one row per workgroup (Chunks == 0: the whole
+// row). Where they are all single blocks, each chunk's values fold into the
+// lane's (max, sum) or argmax, then the next chunk's loads go out, in flight
+// through this chunk's reduction and its barriers; and the workgroups of
+// rows the step does not need, which only read the sequence's length and
+// temperature and leave, are fewer. Each chunk's partial is the one
+// chunk_stats gives. Several chunks per workgroup are compiled for at least
+// 5 waves per SIMD (96 VGPRs) for two chunks, written out; unbounded the
+// compiler keeps both chunks' values live and runs 4. The whole-row loop is
+// bounded at 4 (as a loop it spills at 5).
 template <class D, int Chunks>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Chunks == 2 ? 5 : 1, 8))) void k_rowstats(Params p)
+__attribute__((amdgpu_waves_per_eu(Chunks == 1 ? 1 : (Chunks == 2 ? 5 : 4), 8))) void
+k_rowstats(Params p)
 {
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
@@ -696,8 +704,9 @@ __attribute__((amdgpu_waves_per_eu(Chunks == 2 ? 5 : 1, 8))) void k_rowstats(Par
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     // 32-bit decode of the grid index (64-bit division is a long scalar
     // sequence every workgroup would run before its first load).
-    const uint32_t np = (uint32_t)(nc + Chunks - 1) / (uint32_t)Chunks;
-    const int c0 = Chunks * (int)(item % np), c1 = c0 + 1;
+    const int per = Chunks == 0 ? nc : Chunks;
+    const uint32_t np = (uint32_t)(nc + per - 1) / (uint32_t)per;
+    const int c0 = per * (int)(item % np), cend = min(nc, c0 + per);
     const uint32_t rs = item / np;
     const int slot = (int)(rs % (uint32_t)rows);
     const int64_t b = rs / (uint32_t)rows;
@@ -706,6 +715,8 @@ __attribute__((amdgpu_waves_per_eu(Chunks == 2 ? 5 : 1, 8))) void k_rowstats(Par
     if (!valid_len(L, k) || !valid_temp(tau))
         return;  // the decision reports the sequence
     const bool greedy = tau == 0.f;
+    if (p.skip_filtered && !greedy && seq_filtered(p, b))
+        return;  // k_filter reads this sequence's rows
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
     if (is_target ? i > L : (greedy || i >= L))
@@ -716,39 +727,57 @@ __attribute__((amdgpu_waves_per_eu(Chunks == 2 ? 5 : 1, 8))) void k_rowstats(Par
     const float scale = greedy ? 0.f : temp_scale(tau);
     const int tid = threadIdx.x;
     float2 *out = p.partials + (b * rows + slot) * (int64_t)nc;
-    const int64_t s0 = (int64_t)c0 * CH, e0 = min64((int64_t)p.V, s0 + CH);
-    const int64_t s1 = e0, e1 = min64((int64_t)p.V, s1 + CH);
-    const bool two = Chunks == 2 && c1 < nc;
-    if (Chunks == 2 && single_block<D>(row, s0, e0) && (!two || single_block<D>(row, s1, e1))) {
-        // chunk 0's values fold into the lane's (max, sum) or argmax; then
-        // chunk 1's loads go out, in flight through chunk 0's reduction
+    auto s_of = [&](int c) { return (int64_t)c * CH; };
+    auto e_of = [&](int c) { return min64((int64_t)p.V, (int64_t)(c + 1) * CH); };
+    // every chunk of the range a single block: the row 16-byte aligned, and
+    // V a whole number of vectors if the range holds the row's last chunk
+    const bool pipelined = Chunks != 1 && ((uintptr_t)row & 15u) == 0 &&
+                           (cend < nc || p.V % D::kVec == 0);
+    if (pipelined && Chunks == 2) {
+        const int c1 = c0 + 1;
+        const bool two = c1 < cend;
         u32x4 r[kTiles];
-        load_single_block<D>(row, s0, e0, tid, r);
+        load_single_block<D>(row, s_of(c0), e_of(c0), tid, r);
         Soft st{-INFINITY, 0.f};
         ArgMax am{-INFINITY, INT32_MAX};
         if (greedy)
-            block_argmax<D>(am, r, (int32_t)(s0 + tid * D::kVec));
+            block_argmax<D>(am, r, (int32_t)(s_of(c0) + tid * D::kVec));
         else
             block_soft<D>(st, r, scale);
         if (two)
-            load_single_block<D>(row, s1, e1, tid, r);
+            load_single_block<D>(row, s_of(c1), e_of(c1), tid, r);
         const float2 v0 = greedy ? reduce_argmax(am, sh, tid) : reduce_soft(st, scale, sh, tid);
         if (tid == 0)
             out[c0] = v0;
         if (two) {
-            const float2 v1 = chunk_stats_loaded<D>(s1, greedy, scale, sh, tid, r);
+            const float2 v1 = chunk_stats_loaded<D>(s_of(c1), greedy, scale, sh, tid, r);
             if (tid == 0)
                 out[c1] = v1;
         }
         return;
     }
-    const float2 v0 = chunk_stats<D>(row, s0, e0, greedy, scale, sh);
-    if (tid == 0)
-        out[c0] = v0;
-    if (two) {
-        const float2 v1 = chunk_stats<D>(row, s1, e1, greedy, scale, sh);
+    if (pipelined) {
+        u32x4 r[kTiles];
+        load_single_block<D>(row, s_of(c0), e_of(c0), tid, r);
+        for (int c = c0; c < cend; ++c) {
+            Soft st{-INFINITY, 0.f};
+            ArgMax am{-INFINITY, INT32_MAX};
+            if (greedy)
+                block_argmax<D>(am, r, (int32_t)(s_of(c) + tid * D::kVec));
+            else
+                block_soft<D>(st, r, scale);
+            if (c + 1 < cend)
+                load_single_block<D>(row, s_of(c + 1), e_of(c + 1), tid, r);
+            const float2 v = greedy ? reduce_argmax(am, sh, tid) : reduce_soft(st, scale, sh, tid);
+            if (tid == 0)
+                out[c] = v;
+        }
+        return;
+    }
+    for (int c = c0; c < cend; ++c) {
+        const float2 v = chunk_stats<D>(row, s_of(c), e_of(c), greedy, scale, sh);
         if (tid == 0)
-            out[c1] = v1;
+            out[c] = v;
     }
 }
 
@@ -904,10 +933,18 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
         if (!early_exit) {
             const bool filters = p.top_p || p.top_k;
             if (filters && D::kKeyBits == 16) {
+                // k_filter reads every filtered row; k_rowstats the others
+                // (greedy sequences, top_p >= 1 without top-k)
                 hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads),
                                    0, stream, p);
                 hipLaunchKernelGGL(k_filter_fallback<D>, dim3((unsigned)(nb * rows)),
                                    dim3(kNucThreads), 0, stream, p);
+                // one workgroup per row: with every row filtered, all of
+                // them leave at once, and there are few to dispatch
+                p.skip_filtered = 1;
+                hipLaunchKernelGGL((k_rowstats<D, 0>), dim3((unsigned)(nb * rows)),
+                                   dim3(kThreads), 0, stream, p);
+                p.skip_filtered = 0;
             } else {
                 if (p.n_row_items >= kRowPairChunks)
                     hipLaunchKernelGGL((k_rowstats<D, 2>),
