@@ -119,18 +119,24 @@ def kernel_source_digest() -> str:
     return source_digest()
 
 
+def counter_summary(workload: str) -> dict:
+    """The machine-readable lines of the workload's committed rocprofv3
+    counter summary (empty if there is none)."""
+    path = counters_file(workload)
+    kv = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith("#") and not line.startswith(" "):
+                key, _, val = line.partition(":")
+                kv[key.strip()] = val.strip()
+    return kv
+
+
 def read_counter_traffic(workload: str):
     """HBM bytes per row-statistics launch from the committed rocprofv3
     counter summary of this workload, if it was taken on the current kernel
     source."""
-    path = counters_file(workload)
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            key, _, val = line.partition(":")
-            kv[key.strip()] = val.strip()
+    kv = counter_summary(workload)
     if kv.get("kernel_source_sha256_16") != kernel_source_digest() or kv.get("workload") != workload:
         return None
     try:
@@ -678,7 +684,7 @@ def run_workload(args, name: str, extras: bool) -> dict:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_rowstats",
+            "kernel": counter_summary(w.name).get("kernel", "k_rowstats"),
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -686,8 +692,8 @@ def run_workload(args, name: str, extras: bool) -> dict:
             "traffic": read_counter_traffic(w.name),
             "kernel_us_mean": k1_mean * 1e3,
             "kernel_us_median": k1_median * 1e3,
-            "events": f"HIP event pair around k_rowstats on every {EVENT_EVERY}th of the "
-                      f"{K} timed steps ({len(k1_ms)} samples)",
+            "events": f"HIP event pair around the row-statistics launch on every "
+                      f"{EVENT_EVERY}th of the {K} timed steps ({len(k1_ms)} samples)",
         },
     }
     for key, val in (("early_exit", early), ("top_p", topp), ("top_k_top_p", topk),
