@@ -354,7 +354,9 @@ __device__ inline void group_weight_sums(const DrawRows<D> &r, const Span &sp, i
 
 // Group sums of one chunk with 16-byte aligned groups, kTiles groups per
 // lane: kBatch 16-byte loads per row in flight before their arithmetic.
-template <class D, bool Resid, bool Thresh>
+// Full: the chunk is one whole block (kTiles groups for every lane), so no
+// load is bounds-tested; a test per load costs each a branch around it.
+template <class D, bool Resid, bool Thresh, bool Full>
 __device__ __forceinline__ void vec_group_sums(const DrawRows<D> &r, const Span &sp,
                                                const Decision &dec, int tid, float (&gw)[kTiles],
                                                float (&gp)[kTiles])
@@ -368,7 +370,7 @@ __device__ __forceinline__ void vec_group_sums(const DrawRows<D> &r, const Span 
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t gi = (int64_t)(h + u) * kThreads + tid;
-            const bool in = gi < sp.ngroups;
+            const bool in = Full || gi < sp.ngroups;
             lt[u] = in ? stream_load(vt + gi) : u32x4{0u, 0u, 0u, 0u};
             if constexpr (Resid)
                 ld[u] = in ? stream_load(vd + gi) : u32x4{0u, 0u, 0u, 0u};
@@ -386,11 +388,22 @@ __device__ __forceinline__ void vec_group_sums(const DrawRows<D> &r, const Span 
                 w[j] = x.w;
                 pw[j] = x.p;
             }
-            const bool in = (int64_t)(h + u) * kThreads + tid < sp.ngroups;
+            const bool in = Full || (int64_t)(h + u) * kThreads + tid < sp.ngroups;
             gp[h + u] = in ? pairwise(pw) : 0.f;
             gw[h + u] = Resid ? (in ? pairwise(w) : 0.f) : gp[h + u];  // a bonus draws from p
         }
     }
+}
+
+template <class D, bool Resid, bool Thresh>
+__device__ __forceinline__ void vec_group_sums_of(bool full, const DrawRows<D> &r, const Span &sp,
+                                                  const Decision &dec, int tid,
+                                                  float (&gw)[kTiles], float (&gp)[kTiles])
+{
+    if (full)
+        vec_group_sums<D, Resid, Thresh, true>(r, sp, dec, tid, gw, gp);
+    else
+        vec_group_sums<D, Resid, Thresh, false>(r, sp, dec, tid, gw, gp);
 }
 
 // ===========================================================================
@@ -409,18 +422,21 @@ __device__ __forceinline__ void chunk_weight_sums(const Params &p, int64_t b, in
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     float gw[kTiles], gp[kTiles];  // this lane's group sums, tile by tile
     if (sp.vec) {
-        // Uniform per workgroup: pick the loop without per-token tests.
+        // Uniform per workgroup: pick the loop without per-token tests, and
+        // without per-load tests where the chunk is one whole block (every
+        // chunk of a row but its last, on rows of 16-byte aligned length).
         const bool thresh = dec.tht != -INFINITY || (r.resid && dec.thd != -INFINITY);
+        const bool full = sp.ngroups == (int64_t)kTiles * kThreads;
         if (r.resid) {
             if (thresh)
-                vec_group_sums<D, true, true>(r, sp, dec, tid, gw, gp);
+                vec_group_sums_of<D, true, true>(full, r, sp, dec, tid, gw, gp);
             else
-                vec_group_sums<D, true, false>(r, sp, dec, tid, gw, gp);
+                vec_group_sums_of<D, true, false>(full, r, sp, dec, tid, gw, gp);
         } else {
             if (thresh)
-                vec_group_sums<D, false, true>(r, sp, dec, tid, gw, gp);
+                vec_group_sums_of<D, false, true>(full, r, sp, dec, tid, gw, gp);
             else
-                vec_group_sums<D, false, false>(r, sp, dec, tid, gw, gp);
+                vec_group_sums_of<D, false, false>(full, r, sp, dec, tid, gw, gp);
         }
     } else {
         int unused = -1;
