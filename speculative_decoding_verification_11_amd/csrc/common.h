@@ -473,4 +473,49 @@ __device__ __forceinline__ float2 chunk_stats_loaded(int64_t s, bool greedy, flo
     return reduce_argmax(am, sh, tid);
 }
 
+// Whether chunks [c0, cend) of a row of V elements (nc chunks) are all
+// single blocks: the row 16-byte aligned, and V a whole number of vectors if
+// the range holds the row's last chunk.
+template <class D>
+__device__ inline bool chunks_single_blocks(const typename D::Elem *row, int64_t V, int nc,
+                                            int cend)
+{
+    return ((uintptr_t)row & 15u) == 0 && (cend < nc || V % D::kVec == 0);
+}
+
+// Partials of chunk c0 of a row and, when c0 + 1 < cend, of chunk c0 + 1,
+// both single blocks (chunks_single_blocks). Chunk c0's values fold into the
+// lane's (max, sum) or argmax, then chunk c0 + 1's loads go out and stay in
+// flight through chunk c0's reduction and its barriers. Each partial is the
+// one chunk_stats gives. emit(c, partial) runs in thread 0, in chunk order.
+template <class D, class Emit>
+__device__ __forceinline__ void chunk_pair_stats(const typename D::Elem *row, int64_t V, int c0,
+                                                 int cend, bool greedy, float scale,
+                                                 RowShared &sh, int tid, Emit emit)
+{
+    constexpr int64_t CH = chunk_elems<D>();
+    auto s_of = [&](int c) { return (int64_t)c * CH; };
+    auto e_of = [&](int c) { return min64(V, (int64_t)(c + 1) * CH); };
+    const int c1 = c0 + 1;
+    const bool two = c1 < cend;
+    u32x4 r[kTiles];
+    load_single_block<D>(row, s_of(c0), e_of(c0), tid, r);
+    Soft st{-INFINITY, 0.f};
+    ArgMax am{-INFINITY, INT32_MAX};
+    if (greedy)
+        block_argmax<D>(am, r, (int32_t)(s_of(c0) + tid * D::kVec));
+    else
+        block_soft<D>(st, r, scale);
+    if (two)
+        load_single_block<D>(row, s_of(c1), e_of(c1), tid, r);
+    const float2 v0 = greedy ? reduce_argmax(am, sh, tid) : reduce_soft(st, scale, sh, tid);
+    if (tid == 0)
+        emit(c0, v0);
+    if (two) {
+        const float2 v1 = chunk_stats_loaded<D>(s_of(c1), greedy, scale, sh, tid, r);
+        if (tid == 0)
+            emit(c1, v1);
+    }
+}
+
 }  // namespace spv

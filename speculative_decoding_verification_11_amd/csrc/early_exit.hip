@@ -28,14 +28,14 @@ __device__ inline float2 fetch_float2(const float2 *ptr) { return ld_f2<true>(pt
 #ifndef SPEC_EE_FORMAL
 #define SPEC_EE_FORMAL 0
 #endif
-// Count of a published partial; returns the count before the add.
-__device__ inline int count_published(int32_t *ctr)
+// Count of n published partials; returns the count before the add.
+__device__ inline int count_published(int32_t *ctr, int n)
 {
 #if SPEC_EE_FORMAL
-    const int before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const int before = __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 #else
-    drain_stores();  // the partial is visible before the count
-    const int before = counter_add(ctr, 1);
+    drain_stores();  // the partials are visible before the count
+    const int before = counter_add(ctr, n);
 #endif
     return before;
 }
@@ -182,26 +182,51 @@ __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float
     return false;
 }
 
-// Streams one chunk of target row i (slot 0) or draft row i (slot 1) of
-// sequence b; thread 0 returns the partial.
-template <class D>
-__device__ __forceinline__ float2 ee_chunk(const Params &p, int64_t b, int slot, int c, int i,
-                                           float tau, RowShared &sh)
+// Chunk c0 (Per == 1), or chunks c0 and c0 + 1 (Per == 2; the second where
+// c0 + 1 < nc), of target row i (slot 0) or draft row i (slot 1) of sequence
+// b, as in k_rowstats: where both of a pair are single blocks, the second
+// one's loads are in flight through the first one's reduction. emit(c,
+// partial) runs in thread 0, in chunk order; returns the number of chunks
+// streamed.
+template <class D, int Per, class Emit>
+__device__ __forceinline__ int ee_chunks(const Params &p, int64_t b, int slot, int c0, int i,
+                                         float tau, RowShared &sh, Emit emit)
 {
     using E = typename D::Elem;
     constexpr int64_t CH = chunk_elems<D>();
-    const int k = p.k;
+    const int k = p.k, nc = p.nc;
+    const int64_t V = p.V;
     const bool greedy = tau == 0.f;
-    const E *row = slot == 0 ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * (int64_t)p.V
-                             : static_cast<const E *>(p.draft) + (b * k + i) * (int64_t)p.V;
-    const int64_t s = (int64_t)c * CH;
-    return chunk_stats<D>(row, s, min64((int64_t)p.V, s + CH), greedy,
-                          greedy ? 0.f : temp_scale(tau), sh);
+    const float scale = greedy ? 0.f : temp_scale(tau);
+    const E *row = slot == 0 ? static_cast<const E *>(p.target) + (b * (k + 1) + i) * V
+                             : static_cast<const E *>(p.draft) + (b * k + i) * V;
+    const int cend = min(nc, c0 + Per);
+    if (Per == 2 && chunks_single_blocks<D>(row, V, nc, cend)) {
+        chunk_pair_stats<D>(row, V, c0, cend, greedy, scale, sh, (int)threadIdx.x, emit);
+    } else {
+        for (int c = c0; c < cend; ++c) {
+            const int64_t s = (int64_t)c * CH;
+            const float2 v = chunk_stats<D>(row, s, min64(V, s + CH), greedy, scale, sh);
+            if (threadIdx.x == 0)
+                emit(c, v);
+        }
+    }
+    return cend - c0;
 }
 
-// Position 0: every sequence with a valid length and temperature.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
+// Workgroups per row: one per Per chunks.
+template <int Per>
+__device__ inline int ee_groups(int nc)
+{
+    return (nc + Per - 1) / Per;
+}
+
+// Position 0: every sequence with a valid length and temperature, one
+// workgroup per Per chunks of its target and draft row. Pairs of chunks are
+// compiled for at least 5 waves per SIMD (96 VGPRs), as in k_rowstats.
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void
+k_ee_rowstats0(Params p)
 {
     __shared__ RowShared sh;
     const uint32_t item = blockIdx.x;
@@ -210,8 +235,9 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
         p.ee_count[1] = 0;  // position 1's list, filled by k_ee_decide0
     // 32-bit decode of the grid index (64-bit division is a long scalar
     // sequence every workgroup would run before its first load).
-    const int c = (int)(item % (uint32_t)nc);
-    const uint32_t rs = item / (uint32_t)nc;
+    const uint32_t np = (uint32_t)ee_groups<Per>(nc);
+    const int c0 = Per * (int)(item % np);
+    const uint32_t rs = item / np;
     const int slot = (int)(rs % 2u);
     const int64_t b = rs / 2u;
     const int L = p.draft_len ? p.draft_len[b] : k;
@@ -220,9 +246,8 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p)
         return;
     if (slot == 1 && (tau == 0.f || L == 0))
         return;
-    const float2 part = ee_chunk<D>(p, b, slot, c, 0, tau, sh);
-    if (threadIdx.x == 0)
-        p.partials[(b * rows + (slot == 0 ? 0 : k + 1)) * (int64_t)nc + c] = part;
+    float2 *out = p.partials + (b * rows + (slot == 0 ? 0 : k + 1)) * (int64_t)nc;
+    ee_chunks<D, Per>(p, b, slot, c0, 0, tau, sh, [&](int c, float2 v) { out[c] = v; });
 }
 
 // Appends b to position i's list (lane 0 of the deciding wave).
@@ -285,34 +310,37 @@ __global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p)
     }
 }
 
-// Position i >= 1: the sequences on position i's list. The workgroup that
-// completes a sequence's chunks decides it and lists it for i + 1.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
+// Position i >= 1: the sequences on position i's list, one workgroup per
+// Per chunks. The workgroup that completes a sequence's chunks decides it
+// and lists it for i + 1.
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void
+k_ee_rowstats(Params p, int i)
 {
     __shared__ RowShared sh;
     const uint32_t item = blockIdx.x;  // 32-bit decode, as in k_ee_rowstats0
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
-    const int64_t j = item / (2u * (uint32_t)nc);
+    const uint32_t np = (uint32_t)ee_groups<Per>(nc);
+    const int64_t j = item / (2u * np);
     if (j >= p.ee_count[i])
         return;
-    const int slot = (int)((item / (uint32_t)nc) % 2u);
-    const int c = (int)(item % (uint32_t)nc);
+    const int slot = (int)((item / np) % 2u);
+    const int c0 = Per * (int)(item % np);
     const int64_t b = p.ee_list[(int64_t)i * p.B + j];
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
     if (slot == 1 && (tau == 0.f || i >= L))
         return;
-    const float2 part = ee_chunk<D>(p, b, slot, c, i, tau, sh);
+    float2 *out = p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc;
+    const int n = ee_chunks<D, Per>(p, b, slot, c0, i, tau, sh,
+                                    [&](int c, float2 v) { publish_float2(out + c, v); });
     if (threadIdx.x >= kWave)
         return;
     const int lane = threadIdx.x;
     int last = 0;
     if (lane == 0) {
-        publish_float2(p.partials + (b * rows + (slot == 0 ? i : k + 1 + i)) * (int64_t)nc + c,
-                       part);
         const int items = ee_items(nc, tau == 0.f, i, L);
-        last = count_published(p.ee_done + (int64_t)i * p.B + b) == items - 1;
+        last = count_published(p.ee_done + (int64_t)i * p.B + b, n) + n == items;
     }
     if (!__shfl(last, 0, kWave))
         return;
@@ -323,23 +351,26 @@ __global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i)
 }
 
 // Positions P..k in one launch: every remaining row (target rows P..L,
-// draft rows P..L-1) of the sequences on position P's list. Once few
-// sequences are left, a launch per position costs more than reading the
-// rows after a stop that will never be used. The workgroup that completes
-// a sequence's chunks decides its positions P, P+1, ... up to the stop.
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
+// draft rows P..L-1) of the sequences on position P's list, one workgroup
+// per Per chunks. Once few sequences are left, a launch per position costs
+// more than reading the rows after a stop that will never be used. The
+// workgroup that completes a sequence's chunks decides its positions P,
+// P+1, ... up to the stop.
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void
+k_ee_tail(Params p, int P)
 {
     __shared__ RowShared sh;
     const uint32_t item = blockIdx.x;  // 32-bit decode, as in k_ee_rowstats0
     const int k = p.k, nc = p.nc, rows = 2 * k + 1;
     const int nt = k - P + 1, R = 2 * nt - 1;  // target rows P..k, draft rows P..k-1
-    const uint32_t per_seq = (uint32_t)R * (uint32_t)nc;
+    const uint32_t np = (uint32_t)ee_groups<Per>(nc);
+    const uint32_t per_seq = (uint32_t)R * np;
     const int64_t j = item / per_seq;
     if (j >= p.ee_count[P])
         return;
     const uint32_t rest = item % per_seq;
-    const int slot = (int)(rest / (uint32_t)nc), c = (int)(rest % (uint32_t)nc);
+    const int slot = (int)(rest / np), c0 = Per * (int)(rest % np);
     const int64_t b = p.ee_list[(int64_t)P * p.B + j];
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
@@ -348,18 +379,18 @@ __global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
     const int i = is_target ? P + slot : P + slot - nt;
     if (is_target ? i > L : (greedy || i >= L))
         return;
-    const float2 part = ee_chunk<D>(p, b, is_target ? 0 : 1, c, i, tau, sh);
+    float2 *out = p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc;
+    const int n = ee_chunks<D, Per>(p, b, is_target ? 0 : 1, c0, i, tau, sh,
+                                    [&](int c, float2 v) { publish_float2(out + c, v); });
     if (threadIdx.x >= kWave)
         return;
     const int lane = threadIdx.x;
     int last = 0;
     if (lane == 0) {
-        publish_float2(p.partials + (b * rows + (is_target ? i : k + 1 + i)) * (int64_t)nc + c,
-                       part);
         int items = 0;
         for (int x = P; x <= L; ++x)
             items += ee_items(nc, greedy, x, L);
-        last = count_published(p.ee_done + (int64_t)P * p.B + b) == items - 1;
+        last = count_published(p.ee_done + (int64_t)P * p.B + b, n) + n == items;
     }
     if (!__shfl(last, 0, kWave))
         return;
@@ -371,13 +402,19 @@ __global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P)
             break;
 }
 
-template __global__ void k_ee_rowstats0<F32>(Params p);
-template __global__ void k_ee_rowstats0<BF16>(Params p);
+template __global__ void k_ee_rowstats0<F32, 1>(Params p);
+template __global__ void k_ee_rowstats0<F32, 2>(Params p);
+template __global__ void k_ee_rowstats0<BF16, 1>(Params p);
+template __global__ void k_ee_rowstats0<BF16, 2>(Params p);
 template __global__ void k_ee_decide0<F32>(Params p);
 template __global__ void k_ee_decide0<BF16>(Params p);
-template __global__ void k_ee_rowstats<F32>(Params p, int i);
-template __global__ void k_ee_rowstats<BF16>(Params p, int i);
-template __global__ void k_ee_tail<F32>(Params p, int P);
-template __global__ void k_ee_tail<BF16>(Params p, int P);
+template __global__ void k_ee_rowstats<F32, 1>(Params p, int i);
+template __global__ void k_ee_rowstats<F32, 2>(Params p, int i);
+template __global__ void k_ee_rowstats<BF16, 1>(Params p, int i);
+template __global__ void k_ee_rowstats<BF16, 2>(Params p, int i);
+template __global__ void k_ee_tail<F32, 1>(Params p, int P);
+template __global__ void k_ee_tail<F32, 2>(Params p, int P);
+template __global__ void k_ee_tail<BF16, 1>(Params p, int P);
+template __global__ void k_ee_tail<BF16, 2>(Params p, int P);
 
 }  // namespace spv

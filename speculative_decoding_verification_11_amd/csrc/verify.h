@@ -210,13 +210,13 @@ template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p);
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter_fallback(Params p);
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_rowstats0(Params p);
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void k_ee_rowstats0(Params p);
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_ee_decide0(Params p);
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_rowstats(Params p, int i);
-template <class D>
-__global__ __launch_bounds__(kThreads) void k_ee_tail(Params p, int P);
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void k_ee_rowstats(Params p, int i);
+template <class D, int Per>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Per == 2 ? 5 : 1, 8))) void k_ee_tail(Params p, int P);
 
 }  // namespace spv

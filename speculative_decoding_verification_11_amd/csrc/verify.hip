@@ -745,31 +745,10 @@ k_rowstats(Params p)
     float2 *out = p.partials + (b * rows + slot) * (int64_t)nc;
     auto s_of = [&](int c) { return (int64_t)c * CH; };
     auto e_of = [&](int c) { return min64((int64_t)p.V, (int64_t)(c + 1) * CH); };
-    // every chunk of the range a single block: the row 16-byte aligned, and
-    // V a whole number of vectors if the range holds the row's last chunk
-    const bool pipelined = Chunks != 1 && ((uintptr_t)row & 15u) == 0 &&
-                           (cend < nc || p.V % D::kVec == 0);
+    const bool pipelined = Chunks != 1 && chunks_single_blocks<D>(row, p.V, nc, cend);
     if (pipelined && Chunks == 2) {
-        const int c1 = c0 + 1;
-        const bool two = c1 < cend;
-        u32x4 r[kTiles];
-        load_single_block<D>(row, s_of(c0), e_of(c0), tid, r);
-        Soft st{-INFINITY, 0.f};
-        ArgMax am{-INFINITY, INT32_MAX};
-        if (greedy)
-            block_argmax<D>(am, r, (int32_t)(s_of(c0) + tid * D::kVec));
-        else
-            block_soft<D>(st, r, scale);
-        if (two)
-            load_single_block<D>(row, s_of(c1), e_of(c1), tid, r);
-        const float2 v0 = greedy ? reduce_argmax(am, sh, tid) : reduce_soft(st, scale, sh, tid);
-        if (tid == 0)
-            out[c0] = v0;
-        if (two) {
-            const float2 v1 = chunk_stats_loaded<D>(s_of(c1), greedy, scale, sh, tid, r);
-            if (tid == 0)
-                out[c1] = v1;
-        }
+        chunk_pair_stats<D>(row, p.V, c0, cend, greedy, scale, sh, tid,
+                            [&](int c, float2 v) { out[c] = v; });
         return;
     }
     if (pipelined) {
@@ -795,6 +774,26 @@ k_rowstats(Params p)
         if (tid == 0)
             out[c] = v;
     }
+}
+
+// The early-exit schedule's row launches (positions 0..k) and position 0's
+// decisions, with Per chunks per workgroup.
+template <class D, int Per>
+void early_exit_rows(const Params &p, int64_t nb, hipStream_t stream)
+{
+    const int k = p.k;
+    const int64_t np = (p.nc + Per - 1) / Per;  // workgroups per row
+    hipLaunchKernelGGL((k_ee_rowstats0<D, Per>), dim3((unsigned)(nb * 2 * np)), dim3(kThreads),
+                       0, stream, p);
+    hipLaunchKernelGGL(k_ee_decide0<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, stream, p);
+    const int P = std::min(k + 1, kEarlyExitSingle);
+    for (int i = 1; i < P; ++i)
+        hipLaunchKernelGGL((k_ee_rowstats<D, Per>), dim3((unsigned)(nb * 2 * np)), dim3(kThreads),
+                           0, stream, p, i);
+    if (P <= k)
+        hipLaunchKernelGGL((k_ee_tail<D, Per>), dim3((unsigned)(nb * (2 * (k - P + 1) - 1) * np)),
+                           dim3(kThreads), 0, stream, p, P);
 }
 
 // One wave per sequence (large batches: see kFoldDecisionItems).
@@ -981,18 +980,12 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                 hipLaunchKernelGGL(k_decide<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
                                    dim3(kThreads), 0, stream, p);
         } else {
-            hipLaunchKernelGGL(k_ee_rowstats0<D>, dim3((unsigned)(nb * 2 * nc)), dim3(kThreads),
-                               0, stream, p);
-            hipLaunchKernelGGL(k_ee_decide0<D>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
-                               dim3(kThreads), 0, stream, p);
-            const int P = std::min(k + 1, kEarlyExitSingle);
-            for (int i = 1; i < P; ++i)
-                hipLaunchKernelGGL(k_ee_rowstats<D>, dim3((unsigned)(nb * 2 * nc)),
-                                   dim3(kThreads), 0, stream, p, i);
-            if (P <= k)
-                hipLaunchKernelGGL(k_ee_tail<D>,
-                                   dim3((unsigned)(nb * (2 * (k - P + 1) - 1) * nc)),
-                                   dim3(kThreads), 0, stream, p, P);
+            // Two chunks per workgroup on grids as large as k_rowstats
+            // pairs them on (position 0's chunks: every target and draft row).
+            if (nb * 2 * nc >= kRowPairChunks)
+                early_exit_rows<D, 2>(p, nb, stream);
+            else
+                early_exit_rows<D, 1>(p, nb, stream);
             if (ev_end && b0 == 0 && hipEventRecord(ev_end, stream) != hipSuccess)
                 return SPEC_ELAUNCH;
         }
