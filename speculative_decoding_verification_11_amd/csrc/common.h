@@ -42,6 +42,10 @@ constexpr int kEarlyExitSingle = 4;
 // Draw grids up to this many workgroups (about 16 per CU) take their
 // decisions inside k_draw; larger ones get a k_decide launch first.
 constexpr int64_t kFoldDecisionItems = 4096;
+// Row passes over at least this many chunks take two chunks per workgroup
+// (chunk_pair_stats); smaller ones (a few rounds of the chip or less) keep
+// one per workgroup, since fewer, longer workgroups there lengthen the tail.
+constexpr int64_t kRowPairChunks = 16384;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte load
 

@@ -693,10 +693,6 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
 // its barriers; and the workgroups of rows the step does not need, which
 // only read the sequence's length and temperature, are half as many. Each
 // chunk's partial is the one chunk_stats gives.
-// Row-statistics grids of at least this many chunks take two chunks per
-// workgroup; smaller ones (a few rounds of the chip or less) keep one per
-// workgroup, since fewer, longer workgroups there lengthen the tail.
-constexpr int64_t kRowPairChunks = 16384;
 
 // Chunks consecutive chunks of one row per workgroup (Chunks == 0: the whole
 // row). Where they are all single blocks, each chunk's values fold into the

@@ -90,6 +90,23 @@ def test_tree_odd_sizes_and_ragged_counts(V, dtype, N):
     assert_tree_parity(g, r, f"V={V} N={N}")
 
 
+@pytest.mark.parametrize("V,dtype,N", [(3 * 16384 - 8, "bf16", 64),  # 3 chunks: a lone last one
+                                       (50257, "bf16", 64),          # misaligned rows, short end
+                                       (3 * 8192 + 5, "f32", 33)])   # 4 fp32 chunks, 5 at the end
+def test_tree_large_grids_odd_chunk_counts(V, dtype, N):
+    """Batches of at least 16384 row chunks (grids of several rounds of the
+    chip) with odd chunk counts, short last chunks and misaligned rows."""
+    nc = -(-V // (16384 if dtype == "bf16" else 8192))
+    B = -(-16384 // (N * nc)) + 1
+    rng = np.random.default_rng(V + 3 * N)
+    nn = rng.integers(1, N + 1, size=B)
+    t, par, tok, nn = _random_trees(rng, B, N, V, dtype, nn)
+    say(f"[case] tree large V={V} {dtype} N={N} B={B} nc={nc}")
+    g = run_tree(to_dev(t), to_dev(par), to_dev(tok), to_dev(nn))
+    r = oracle.spec_tree_ref(t, par, tok, nn, nthreads=NTH)
+    assert_tree_parity(g, r, f"large V={V} N={N}")
+
+
 def test_tree_statuses():
     rng = np.random.default_rng(4)
     B, N, V = 6, 8, 64
