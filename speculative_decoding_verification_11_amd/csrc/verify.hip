@@ -17,22 +17,24 @@
 //             accepted draw a bonus token from p_L.
 //   greedy:   accept g_i while it equals argmax(target_i); emit that argmax.
 //
-// Three or four launches per call (with a filter, k_filter and
-// k_filter_fallback replace k_rowstats for bf16 logits; k_nucleus follows
-// it for fp32), stream-ordered, no host synchronisation. Every hand-over
-// between workgroups crosses a launch boundary, so no workgroup ever waits
-// for another and nothing needs device-scope atomics:
+// Three or four launches per call (with a filter on bf16 logits, k_filter
+// and k_filter_fallback come first; k_nucleus follows k_rowstats for fp32),
+// stream-ordered, no host synchronisation. Every hand-over between
+// workgroups crosses a launch boundary, so no workgroup ever waits for
+// another and nothing needs device-scope atomics:
 //
 //   k_rowstats  one workgroup per 32 KiB chunk of every logit row the step
-//               needs (b-major). Each streams its chunk once with 16-byte
-//               loads and stores an 8-byte partial: (max logit, sum
-//               2^((x - max) * log2(e)/tau)) for sampling rows, (max logit,
-//               lowest index of it) for greedy rows. This kernel carries
-//               all of the algorithmic HBM traffic and runs at copy speed.
-//               With a top-k or top-p filter on bf16 logits, k_filter takes
-//               its place: one workgroup per row, reading each filtered row
-//               once (counts, thresholds and the row max); k_filter_fallback
-//               then gives the rows without a filter their row statistics.
+//               needs (b-major), or per two chunks of a row on grids of at
+//               least kRowPairChunks chunks. Each streams its chunks once
+//               with 16-byte loads and stores an 8-byte partial per chunk:
+//               (max logit, sum 2^((x - max) * log2(e)/tau)) for sampling
+//               rows, (max logit, lowest index of it) for greedy rows. This
+//               kernel carries all of the algorithmic HBM traffic and runs
+//               at copy speed. With a top-k or top-p filter on bf16 logits,
+//               k_filter reads each filtered row once (counts, thresholds and
+//               the row max; k_filter_fallback settles the rows it flags),
+//               and k_rowstats, one workgroup per row, streams only the rows
+//               without a filter.
 //   k_decide    one wave per sequence: fold the partials in chunk order,
 //               gather p_i(g_i) and q_i(g_i), draw Philox, run the
 //               left-to-right test, write the accepted prefix, and record
@@ -43,7 +45,9 @@
 //               and this launch is skipped.
 //   k_draw      one workgroup per chunk of each sequence's draw row: sums
 //               of the draw weights w = max(0, p_j - q_j) (or p_L for a
-//               bonus) over its chunk in fp64, per segment and in all.
+//               bonus) over its chunk in fp64, per segment and in all. A
+//               bonus draw on an unfiltered row reads only the chunk that
+//               the decision located from the row statistics.
 //   k_locate    one wave per sequence: the chunk where the cumulative weight
 //               passes v * S, then the segment, the group and the element,
 //               from those sums and one read of the group.
