@@ -79,11 +79,33 @@ struct LocateShared {
     double cm[kMaxLdsChunks];  // chunk masses (w, p) of one sequence
 };
 
+// Partial q of chunk batch c0 of a row (`pp`; `pre`: its first batch,
+// loaded early), `pad` past the row's end.
+template <bool Eager>
+__device__ __forceinline__ float2 fold_part(const float2 *pp, const float2 (&pre)[kFoldBatch],
+                                            int nc, int c0, int q, float2 pad)
+{
+    if constexpr (Eager) {
+        if (c0 == 0)
+            return q < nc ? pre[q] : pad;
+    }
+    return c0 + q < nc ? pp[c0 + q] : pad;
+}
+
 // ===========================================================================
 // Decision of one sequence (one wave; `lane` in [0, 64)). Writes the
 // accepted prefix, num_accepted, diagnostics and the decision record.
+// Eager (the decision's own launch): the loads that do not depend on the
+// draft length -- the drafted tokens (lane < k), the first kFoldBatch chunk
+// partials of target row `lane` and draft row `lane`, and the two logits of
+// each drafted token whose id is in range -- go out together with the
+// length, so the decision waits on two memory round trips instead of four;
+// a bonus draw's chunk takes the bonus row's partials from the lane that
+// holds them. The values, and the order of every fold, are those of the
+// plain form, which the draw kernel's workgroups use (there the extra
+// registers would cost the draw sums their occupancy).
 // ===========================================================================
-template <class D>
+template <class D, bool Eager>
 __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane, bool write)
 {
     using E = typename D::Elem;
@@ -94,6 +116,26 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
     const float tau = p.temperature[b];
     int32_t *out = p.out_tokens + b * (k + 1);
 
+    // Eager loads (nothing here depends on L; every address is in range).
+    float2 tpre[kFoldBatch], dpre[kFoldBatch];
+    int gpre = -1;
+    float xtpre = 0.f, xdpre = 0.f;
+    if constexpr (Eager) {
+        if (lane < k)
+            gpre = p.draft_tokens[b * k + lane];
+        const float2 *pt = p.partials + (b * rows + lane) * (int64_t)nc;
+        const float2 *pd = p.partials + (b * rows + k + 1 + lane) * (int64_t)nc;
+#pragma unroll
+        for (int q = 0; q < kFoldBatch; ++q) {
+            tpre[q] = lane <= k && q < nc ? pt[q] : make_float2(0.f, 0.f);
+            dpre[q] = lane < k && q < nc ? pd[q] : make_float2(0.f, 0.f);
+        }
+        if (lane < k && gpre >= 0 && gpre < V) {
+            xtpre = D::at(target + (b * (k + 1) + lane) * (int64_t)V, gpre);
+            xdpre = D::at(draft + (b * k + lane) * (int64_t)V, gpre);
+        }
+    }
+
     int status = SPEC_SEQ_OK;
     int g = -1;
     if (!valid_len(L, k)) {
@@ -103,7 +145,7 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
     } else if (p.top_p && !(p.top_p[b] > 0.f)) {
         status = SPEC_SEQ_BAD_TOP_P;
     } else {
-        g = lane < L ? p.draft_tokens[b * k + lane] : -1;
+        g = lane < L ? (Eager ? gpre : p.draft_tokens[b * k + lane]) : -1;
         if (__any(lane < L && (g < 0 || g >= V)))
             status = SPEC_SEQ_BAD_TOKEN;
     }
@@ -121,8 +163,12 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
                 float2 t[kFoldBatch];
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
-                    t[q] = c0 + q < nc ? pp[c0 + q]
-                                       : make_float2(-INFINITY, __int_as_float(INT32_MAX));
+                    t[q] = Eager ? fold_part<Eager>(pp, tpre, nc, c0, q,
+                                                    make_float2(-INFINITY,
+                                                                __int_as_float(INT32_MAX)))
+                                 : (c0 + q < nc ? pp[c0 + q]
+                                                : make_float2(-INFINITY,
+                                                              __int_as_float(INT32_MAX)));
 #pragma unroll
                 for (int q = 0; q < kFoldBatch; ++q)
                     acc = argmax_merge(acc, ArgMax{t[q].x, __float_as_int(t[q].y)});
@@ -163,7 +209,9 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
                     float2 t[kFoldBatch];
 #pragma unroll
                     for (int q = 0; q < kFoldBatch; ++q)
-                        t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
+                        t[q] = Eager ? fold_part<Eager>(pp, tpre, nc, c0, q,
+                                                        make_float2(-INFINITY, 0.f))
+                                     : (c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f));
 #pragma unroll
                     for (int q = 0; q < kFoldBatch; ++q)
                         ts = soft_merge(ts, Soft{t[q].x, t[q].y}, scale);
@@ -175,7 +223,9 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
                     float2 t[kFoldBatch];
 #pragma unroll
                     for (int q = 0; q < kFoldBatch; ++q)
-                        t[q] = c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f);
+                        t[q] = Eager ? fold_part<Eager>(pp, dpre, nc, c0, q,
+                                                        make_float2(-INFINITY, 0.f))
+                                     : (c0 + q < nc ? pp[c0 + q] : make_float2(-INFINITY, 0.f));
 #pragma unroll
                     for (int q = 0; q < kFoldBatch; ++q)
                         ds = soft_merge(ds, Soft{t[q].x, t[q].y}, scale);
@@ -184,8 +234,8 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
         }
         const float tz = ts.z, dz = ds.z;
         if (lane < L) {
-            const float xt = D::at(target + (b * (k + 1) + lane) * (int64_t)V, g);
-            const float xd = D::at(draft + (b * k + lane) * (int64_t)V, g);
+            const float xt = Eager ? xtpre : D::at(target + (b * (k + 1) + lane) * (int64_t)V, g);
+            const float xd = Eager ? xdpre : D::at(draft + (b * k + lane) * (int64_t)V, g);
             pg = xt >= tth ? exp2_fast((xt - ts.m) * scale) / tz : 0.f;
             qg = xd >= dth ? exp2_fast((xd - ds.m) * scale) / dz : 0.f;
         }
@@ -214,9 +264,25 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
             if (dec.kind == SPEC_DRAW_BONUS && !seq_filtered(p, b)) {
                 // every lane reads the bonus row's partials and gets the same
                 const float2 *pb = p.partials + (b * rows + j) * (int64_t)nc;
-                bonus_chunk(nc, dec.v, dec.mt, dec.zt, scale, lane,
-                            [&](int c) { return pb[c]; }, dec.chunk, dec.mass, dec.base,
-                            dec.total);
+                if (Eager && nc <= kFoldBatch) {
+                    // lane j holds them all: lane c takes chunk c's (bonus_chunk
+                    // asks each lane for its own chunk, c == lane, when nc <= 64)
+                    float2 mine = make_float2(0.f, 0.f);
+#pragma unroll
+                    for (int q = 0; q < kFoldBatch; ++q) {
+                        const float2 v2 = make_float2(__shfl(tpre[q].x, j, kWave),
+                                                      __shfl(tpre[q].y, j, kWave));
+                        if (lane == q)
+                            mine = v2;
+                    }
+                    bonus_chunk(nc, dec.v, dec.mt, dec.zt, scale, lane,
+                                [&](int) { return mine; }, dec.chunk, dec.mass, dec.base,
+                                dec.total);
+                } else {
+                    bonus_chunk(nc, dec.v, dec.mt, dec.zt, scale, lane,
+                                [&](int c) { return pb[c]; }, dec.chunk, dec.mass, dec.base,
+                                dec.total);
+                }
             }
             if (write && lane == 0)
                 p.num_accepted[b] = j;
@@ -802,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p)
 {
     const int64_t b = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
     if (b < p.B)
-        decide<D>(p, b, (int)(threadIdx.x % kWave), true);
+        decide<D, true>(p, b, (int)(threadIdx.x % kWave), true);
 }
 
 // One workgroup per chunk of each sequence's draw row, sequences in reverse
@@ -820,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p)
         // Every workgroup of the sequence takes its decision (the first one
         // also writes the prefix, the counts and the record for the locate).
         if (threadIdx.x < kWave) {
-            const Decision d = decide<D>(p, b, (int)threadIdx.x, c == 0);
+            const Decision d = decide<D, false>(p, b, (int)threadIdx.x, c == 0);
             if (threadIdx.x == 0)
                 sdec = d;
         }
