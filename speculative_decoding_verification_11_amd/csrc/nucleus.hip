@@ -571,11 +571,11 @@ struct FilterRow {
 };
 
 template <class D>
-__device__ inline FilterRow<D> filter_row(const Params &p)
+__device__ inline FilterRow<D> filter_row(const Params &p, uint32_t rb)
 {
     using E = typename D::Elem;
     const int k = p.k, rows = 2 * k + 1;
-    const uint32_t rb = blockIdx.x;  // 32-bit decode: the grid index fits
+    // rb = b * rows + slot; 32-bit decode: the row index fits
     const int slot = (int)(rb % (uint32_t)rows);
     const int64_t b = rb / (uint32_t)rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kNucThreads, 6) void k_filter(Params p)
 {
     static_assert(D::kKeyBits == 16, "the counting window is for bf16 rows");
     __shared__ CountShared sh;
-    const FilterRow<D> f = filter_row<D>(p);
+    const FilterRow<D> f = filter_row<D>(p, blockIdx.x);
     const int tid = threadIdx.x;
     if (!f.filtered || !f.needed) {
         if (tid == 0)
@@ -846,26 +846,46 @@ radix:
         *out = make_float4(0.f, 0.f, m, kRadix);
 }
 
-// One workgroup per row of a call with top-k or top-p parameters (bf16
-// logits), after k_filter: the radix passes for the filtered rows k_filter
-// flagged. (The rows without a filter get their row statistics from
-// k_rowstats, launched after this kernel.)
+// After k_filter, in a call with top-k or top-p parameters (bf16 logits):
+// the radix passes for the filtered rows that k_filter flagged (a few rows a
+// call, if any; the rows without a filter get their row statistics from
+// k_rowstats, launched after this kernel). One workgroup per kFallbackRows
+// rows: each wave reads one row's flag, and the workgroup takes the flagged
+// ones in turn. With nothing to do, as in most calls, a workgroup per row
+// cost about 9 us on c5 just in launching and retiring them.
+constexpr int kFallbackRows = kNucWaves;  // the host's grid assumes kNucThreads / kWave
 template <class D>
 __global__ __launch_bounds__(kNucThreads, 6) void k_filter_fallback(Params p)
 {
     __shared__ NucleusShared sh;
-    const float4 rec = p.nucleus[blockIdx.x];
-    if (rec.w == kSettled || rec.w == kRowStats)
-        return;  // most rows: one read (k_rowstats reads the unfiltered ones)
-    const FilterRow<D> f = filter_row<D>(p);
-    const int tid = threadIdx.x;
-    const float scale = temp_scale(f.tau);
+    __shared__ uint32_t todo;
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const uint32_t nrows = (uint32_t)p.B * (uint32_t)(2 * p.k + 1);
+    const uint32_t r0 = blockIdx.x * (uint32_t)kFallbackRows;  // 32-bit: the row index fits
+    if (tid == 0)
+        todo = 0;
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0 && r0 + wave < nrows) {
+        const float w = p.nucleus[r0 + wave].w;
+        if (!(w == kSettled || w == kRowStats))
+            atomicOr(&todo, 1u << wave);
+    }
+    __syncthreads();
+    uint32_t mask = todo;  // the same in every thread
     const float fscale = __uint_as_float((uint32_t)(127 + p.fix_bits) << 23);  // 2^fix_bits
     const float zlim = -(float)(p.fix_bits + 2);  // (x - m) * scale below this: weight 0
-    const float m = rec.w == kRadixMax ? row_max<D>(f.row, p.V, sh) : rec.z;
-    __syncthreads();
-    radix_filter<D>(f.row, p.V, m, scale, fscale, zlim, f.k_on, f.top_k, f.p_on, f.top_p, f.out,
-                    sh);
+    while (mask) {
+        const uint32_t rb = r0 + (uint32_t)__builtin_ctz(mask);
+        mask &= mask - 1;
+        const float4 rec = p.nucleus[rb];
+        const FilterRow<D> f = filter_row<D>(p, rb);
+        const float scale = temp_scale(f.tau);
+        const float m = rec.w == kRadixMax ? row_max<D>(f.row, p.V, sh) : rec.z;
+        __syncthreads();
+        radix_filter<D>(f.row, p.V, m, scale, fscale, zlim, f.k_on, f.top_k, f.p_on, f.top_p,
+                        f.out, sh);
+        __syncthreads();  // sh is reused by the next flagged row
+    }
 }
 
 // One workgroup per fp32 row of every sampling sequence with a top-k or

@@ -794,11 +794,22 @@ k_rowstats(Params p)
     const int64_t b = rs / (uint32_t)rows;
     const int L = p.draft_len ? p.draft_len[b] : k;
     const float tau = p.temperature[b];
+    // In a filtered call (whole rows; most workgroups leave here) the filter
+    // parameters are loaded with the length, not after it.
+    float top_p = 1.f;
+    int32_t top_k = 0;
+    if (Chunks == 0 && p.skip_filtered) {
+        if (p.top_p)
+            top_p = p.top_p[b];
+        if (p.top_k)
+            top_k = p.top_k[b];
+    }
     if (!valid_len(L, k) || !valid_temp(tau))
         return;  // the decision reports the sequence
     const bool greedy = tau == 0.f;
-    if (p.skip_filtered && !greedy && seq_filtered(p, b))
-        return;  // k_filter reads this sequence's rows
+    if (Chunks == 0 && p.skip_filtered && !greedy &&
+        (top_p < 1.f || (top_k > 0 && top_k < p.V)))
+        return;  // k_filter reads this sequence's rows (seq_filtered)
     const bool is_target = slot <= k;
     const int i = is_target ? slot : slot - (k + 1);
     if (is_target ? i > L : (greedy || i >= L))
@@ -1018,7 +1029,10 @@ int launch_all(const Params &base, const spec_verify_aux_t *aux, const Layout &l
                 // (greedy sequences, top_p >= 1 without top-k)
                 hipLaunchKernelGGL(k_filter<D>, dim3((unsigned)(nb * rows)), dim3(kNucThreads),
                                    0, stream, p);
-                hipLaunchKernelGGL(k_filter_fallback<D>, dim3((unsigned)(nb * rows)),
+                // eight rows per workgroup (one wave reads each row's flag)
+                constexpr int64_t fb_rows = kNucThreads / kWave;
+                hipLaunchKernelGGL(k_filter_fallback<D>,
+                                   dim3((unsigned)((nb * rows + fb_rows - 1) / fb_rows)),
                                    dim3(kNucThreads), 0, stream, p);
                 // one workgroup per row: with every row filtered, all of
                 // them leave at once, and there are few to dispatch
