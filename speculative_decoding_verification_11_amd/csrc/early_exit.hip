@@ -182,6 +182,95 @@ __device__ inline bool ee_decide(const Params &p, int64_t b, int i, int L, float
     return false;
 }
 
+// Decisions of sequence b at positions P..L at once, by one wave: lane x
+// takes position x (its rows' partials folded in chunk order, its gathers
+// and Philox draws, as ee_decide does for one position), and the first
+// position that rejects (or the bonus at L) ends the round. Bit-identical
+// to calling ee_decide for P, P + 1, ... until it stops, in one memory round
+// trip for the partials instead of one per position. Requires P <= L.
+template <class D>
+__device__ inline void ee_decide_range(const Params &p, int64_t b, int P, int L, float tau,
+                                       int lane)
+{
+    using E = typename D::Elem;
+    const int k = p.k, V = p.V, nc = p.nc, rows = 2 * k + 1;
+    const int x = lane;                       // this lane's position
+    const bool mine = x >= P && x <= L;       // a position this call decides
+    const bool drafted = mine && x < L;
+    const int g = drafted ? p.draft_tokens[b * k + x] : -1;
+    const float2 *pt = p.partials + (b * rows + (mine ? x : 0)) * (int64_t)nc;
+    const float2 *pd = p.partials + (b * rows + k + 1 + (drafted ? x : 0)) * (int64_t)nc;
+    Decision dec = no_decision();
+    if (tau == 0.f) {
+        ArgMax acc{-INFINITY, INT32_MAX};
+        if (mine)
+            for (int c = 0; c < nc; ++c) {
+                const float2 t = fetch_float2(pt + c);
+                acc = argmax_merge(acc, ArgMax{t.x, __float_as_int(t.y)});
+            }
+        const uint64_t stop = __ballot(mine && !(x < L && acc.i == g));
+        const int j = __ffsll((unsigned long long)stop) - 1;  // L stops at the latest
+        if (mine && x <= j && p.aux.argmax)
+            p.aux.argmax[b * (k + 1) + x] = acc.i;
+        dec.row = j;
+        dec.kind = SPEC_DRAW_GREEDY;
+        ee_stop(p, b, j, SPEC_SEQ_OK, dec, true, __shfl(acc.i, j, kWave), 0, j + 1, lane);
+        return;
+    }
+    const float scale = temp_scale(tau);
+    float xt = 0.f, xd = 0.f;
+    if (drafted) {
+        xt = D::at(static_cast<const E *>(p.target) + (b * (k + 1) + x) * (int64_t)V, g);
+        xd = D::at(static_cast<const E *>(p.draft) + (b * k + x) * (int64_t)V, g);
+    }
+    Soft ts{-INFINITY, 0.f}, ds{-INFINITY, 0.f};
+    if (mine)
+        for (int c = 0; c < nc; ++c) {
+            const float2 t = fetch_float2(pt + c);
+            ts = soft_merge(ts, Soft{t.x, t.y}, scale);
+            if (drafted) {
+                const float2 d = fetch_float2(pd + c);
+                ds = soft_merge(ds, Soft{d.x, d.y}, scale);
+            }
+        }
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)x, p.seq_base + (uint32_t)b, 0u, 0u),
+                                  p.key0, p.key1);
+    const float u = uniform24(w.x), v = uniform24(w.y);
+    float pg = 0.f, qg = 0.f;
+    if (drafted) {
+        pg = exp2_fast((xt - ts.m) * scale) / ts.z;
+        qg = exp2_fast((xd - ds.m) * scale) / ds.z;
+    }
+    const bool qzero = drafted && !(qg > 0.f);
+    const bool reject = drafted && !qzero && !(u < fminf(1.f, pg / qg));
+    const uint64_t stop = __ballot(mine && (qzero || reject || x == L));
+    const int j = __ffsll((unsigned long long)stop) - 1;
+    if (__shfl((int)qzero, j, kWave)) {
+        ee_stop(p, b, j, SPEC_SEQ_QZERO, dec, false, 0, 0, 0, lane);
+        return;
+    }
+    if (drafted && x <= j) {  // the accepted positions and the one that rejects
+        if (p.aux.p_g) p.aux.p_g[b * k + x] = pg;
+        if (p.aux.q_g) p.aux.q_g[b * k + x] = qg;
+    }
+    const bool bonus = j == L;
+    dec.row = j;
+    dec.kind = bonus ? SPEC_DRAW_BONUS : SPEC_DRAW_RESIDUAL;
+    dec.v = __shfl(v, j, kWave);
+    dec.scale = scale;
+    dec.mt = __shfl(ts.m, j, kWave);
+    dec.zt = __shfl(ts.z, j, kWave);
+    dec.md = __shfl(ds.m, j, kWave);
+    dec.zd = __shfl(ds.z, j, kWave);
+    if (bonus) {  // its chunk from the row statistics, as in decide()
+        const float2 *pj = p.partials + (b * rows + j) * (int64_t)nc;
+        bonus_chunk(nc, dec.v, dec.mt, dec.zt, scale, lane,
+                    [&](int c) { return fetch_float2(pj + c); }, dec.chunk, dec.mass, dec.base,
+                    dec.total);
+    }
+    ee_stop(p, b, j, SPEC_SEQ_OK, dec, false, 0, bonus ? L : j + 1, 0, lane);
+}
+
 // Chunk c0 (Per == 1), or chunks c0 and c0 + 1 (Per == 2; the second where
 // c0 + 1 < nc), of target row i (slot 0) or draft row i (slot 1) of sequence
 // b, as in k_rowstats: where both of a pair are single blocks, the second
@@ -396,10 +485,8 @@ k_ee_tail(Params p, int P)
         return;
     acquire_published();
     // The last chunk of the sequence's rows: the first wave decides
-    // positions P, P + 1, ... up to the stop.
-    for (int x = P; x <= L; ++x)
-        if (!ee_decide<D>(p, b, x, L, tau, true, lane))
-            break;
+    // positions P, P + 1, ... up to the stop, all at once.
+    ee_decide_range<D>(p, b, P, L, tau, lane);
 }
 
 template __global__ void k_ee_rowstats0<F32, 1>(Params p);
