@@ -187,8 +187,8 @@ def cpu_model() -> str:
 
 def cpu_baseline(batch, seed: int, nseq: int, gpu_out: dict) -> dict:
     """The oracle on the host cores: the batch (up to nseq sequences) on every
-    core this process may use, up to the 16 a one-GPU machine grants each GPU,
-    and a 64-sequence slice on one thread; each the median of three runs.
+    core this process may use (at most 16 threads), and a 64-sequence slice
+    on one thread; each the median of three runs.
     The oracle's outputs of the first run are compared with the GPU's outputs
     of the same batch and seed: the flagged fraction of the batch's draws
     (oracle margin below 1e-6), how many flagged draws the two sides decided
@@ -225,7 +225,7 @@ def cpu_baseline(batch, seed: int, nseq: int, gpu_out: dict) -> dict:
     return {"value": positions / dt, "unit": "positions/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {sample.B} of {batch.B} sequences of the same batch "
                       f"({positions} positions), fp64 C oracle, {nthreads} threads "
-                      f"({visible} CPUs visible to the process; a one-GPU box grants 16), "
+                      f"({visible} CPUs visible to the process), "
                       f"median of 3: {dt:.2f} s wall",
             "value_1_thread": one.B * (one.k + 1) / dt1,
             "sample_1_thread": f"first {one.B} sequences, one thread, median of 3: "
