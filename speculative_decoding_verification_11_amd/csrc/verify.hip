@@ -45,7 +45,8 @@
 //               and this launch is skipped.
 //   k_draw      one workgroup per chunk of each sequence's draw row: sums
 //               of the draw weights w = max(0, p_j - q_j) (or p_L for a
-//               bonus) over its chunk in fp64, per segment and in all. A
+//               bonus), scaled by the target row's normaliser, over its
+//               chunk in fp64, per segment and in all. A
 //               bonus draw on an unfiltered row reads only the chunk that
 //               the decision located from the row statistics.
 //   k_locate    one wave per sequence: the chunk where the cumulative weight
@@ -322,11 +323,14 @@ __device__ __forceinline__ Decision decide(const Params &p, int64_t b, int lane,
     return dec;
 }
 
-// Draw weight of one token: w = max(0, p - q) for a residual (p alone for a
-// bonus), and p itself (for the rounding fallback), in fp32. The difference
-// is exact whenever p and q are within a factor of two (Sterbenz) and off by
-// at most half an ulp of a large difference otherwise. Every reader of a
-// weight goes through here, so all of them see bit-identical values.
+// Draw weight of one token, in units of the target row's normaliser z_t
+// (the sums and the cut point v * S scale alike, so the token drawn is the
+// same): w = z_t max(0, p - q) = max(0, e_t - e_d (z_t / z_d)) for a residual
+// (e = 2^((x - m) * scale), the unnormalised softmax terms), e_t alone for a
+// bonus, and z_t p = e_t itself (for the rounding fallback), in fp32. The
+// difference is one fused multiply-add: e_t - e_d (z_t / z_d) exactly, then
+// one rounding. Every reader of a weight goes through here, so all of them
+// see bit-identical values.
 struct Weights {
     float w, p;
 };
@@ -335,27 +339,26 @@ struct Weights {
 // The specialised form below fixes, per workgroup, whether the draw is a
 // residual (Resid) and whether a filter threshold applies (Thresh); with no
 // filter the thresholds are -inf, which every finite logit passes, so both
-// forms give the same bits. Contraction stays off in both, so that no
-// product is fused into the difference in one form and not in the other.
+// forms give the same bits. Contraction stays off in both, so that the only
+// fused product is the explicit one, in both forms.
 template <bool Resid, bool Thresh>
-__device__ inline Weights draw_weights_t(float xt, float xd, const Decision &dec, float inv_zt,
-                                         float inv_zd)
+__device__ inline Weights draw_weights_t(float xt, float xd, const Decision &dec, float ratio)
 {
 #pragma clang fp contract(off)
-    const float et = exp2_fast((xt - dec.mt) * dec.scale) * inv_zt;
+    const float et = exp2_fast((xt - dec.mt) * dec.scale);
     const float pt = !Thresh || xt >= dec.tht ? et : 0.f;  // outside the target's nucleus: 0
     if constexpr (!Resid)
         return {pt, pt};
-    const float ed = exp2_fast((xd - dec.md) * dec.scale) * inv_zd;
+    const float ed = exp2_fast((xd - dec.md) * dec.scale);
     const float pd = !Thresh || xd >= dec.thd ? ed : 0.f;
-    return {fmaxf(pt - pd, 0.f), pt};
+    return {fmaxf(fmaf(-pd, ratio, pt), 0.f), pt};
 }
 
-__device__ inline Weights draw_weights(float xt, float xd, const Decision &dec, float inv_zt,
-                                       float inv_zd, bool resid)
+__device__ inline Weights draw_weights(float xt, float xd, const Decision &dec, float ratio,
+                                       bool resid)
 {
-    return resid ? draw_weights_t<true, true>(xt, xd, dec, inv_zt, inv_zd)
-                 : draw_weights_t<false, true>(xt, xd, dec, inv_zt, inv_zd);
+    return resid ? draw_weights_t<true, true>(xt, xd, dec, ratio)
+                 : draw_weights_t<false, true>(xt, xd, dec, ratio);
 }
 
 // Pairwise fp32 sum of one group's 8 or 4 weights (fixed association).
@@ -372,7 +375,7 @@ __device__ inline float pairwise(const float (&v)[N])
 template <class D>
 struct DrawRows {
     const typename D::Elem *t, *d;
-    float inv_zt, inv_zd;
+    float ratio;  // z_t / z_d (residual draws)
     bool resid;
 };
 
@@ -384,8 +387,7 @@ __device__ inline DrawRows<D> draw_rows(const Params &p, int64_t b, const Decisi
     r.resid = dec.kind == SPEC_DRAW_RESIDUAL;
     r.t = static_cast<const E *>(p.target) + (b * (p.k + 1) + dec.row) * (int64_t)p.V;
     r.d = r.resid ? static_cast<const E *>(p.draft) + (b * p.k + dec.row) * (int64_t)p.V : r.t;
-    r.inv_zt = 1.f / dec.zt;
-    r.inv_zd = r.resid ? 1.f / dec.zd : 0.f;
+    r.ratio = r.resid ? dec.zt / dec.zd : 0.f;
     return r;
 }
 
@@ -393,8 +395,7 @@ __device__ inline DrawRows<D> draw_rows(const Params &p, int64_t b, const Decisi
 template <class D>
 __device__ inline Weights elem_weight(const DrawRows<D> &r, int64_t x, const Decision &dec)
 {
-    return draw_weights(D::at(r.t, x), r.resid ? D::at(r.d, x) : 0.f, dec, r.inv_zt, r.inv_zd,
-                        r.resid);
+    return draw_weights(D::at(r.t, x), r.resid ? D::at(r.d, x) : 0.f, dec, r.ratio, r.resid);
 }
 
 // Pairwise fp32 sums (w and p) of the weights of one group of kVec
@@ -411,8 +412,7 @@ __device__ inline void group_weight_sums(const DrawRows<D> &r, const Span &sp, i
     float w[D::kVec], pw[D::kVec];
 #pragma unroll
     for (int j = 0; j < D::kVec; ++j) {
-        const Weights x = draw_weights(ft[j], r.resid ? fd[j] : 0.f, dec, r.inv_zt, r.inv_zd,
-                                       r.resid);
+        const Weights x = draw_weights(ft[j], r.resid ? fd[j] : 0.f, dec, r.ratio, r.resid);
         w[j] = x.w;
         pw[j] = x.p;
         if ((use_p ? x.p : x.w) > 0.f)
@@ -454,7 +454,7 @@ __device__ __forceinline__ void vec_group_sums(const DrawRows<D> &r, const Span 
 #pragma unroll
             for (int j = 0; j < D::kVec; ++j) {
                 const Weights x = draw_weights_t<Resid, Thresh>(ft[j], Resid ? fd[j] : 0.f, dec,
-                                                                r.inv_zt, r.inv_zd);
+                                                                r.ratio);
                 w[j] = x.w;
                 pw[j] = x.p;
             }
@@ -717,7 +717,7 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
         float w[D::kVec];
 #pragma unroll
         for (int j = 0; j < D::kVec; ++j) {
-            const Weights y = draw_weights(ft[j], fd[j], dec, r.inv_zt, r.inv_zd, r.resid);
+            const Weights y = draw_weights(ft[j], fd[j], dec, r.ratio, r.resid);
             w[j] = in ? (use_p ? y.p : y.w) : 0.f;
         }
         const float gsum = pairwise(w);
@@ -749,7 +749,9 @@ __device__ __forceinline__ void locate(const Params &p, int64_t b, int lane, Loc
     }
     if (lane == 0) {
         p.out_tokens[b * (p.k + 1) + dec.row] = tok >= 0 ? tok : (int)s;
-        if (p.aux.resid_mass) p.aux.resid_mass[b] = (float)S;
+        // S of a located draw is the row statistics' (a probability mass);
+        // otherwise it is the draw weights' sum, in units of z_t.
+        if (p.aux.resid_mass) p.aux.resid_mass[b] = (float)(located ? S : S / (double)dec.zt);
         if (p.aux.draw_kind) p.aux.draw_kind[b] = kind;
     }
 }
