@@ -44,6 +44,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD specification
 WORKLOADS = ("c3", "c4", "c5")  # the configurations with a bandwidth target
 SMALL_STEPS = 100  # timed steps at least, for the workloads other than the headline
 HEADLINE = "c5"
+CHUNK_BYTES = 32 * 1024  # the library's row-statistics chunk (one k_draw workgroup)
 
 
 EVENT_EVERY = 4  # set from --event-every
@@ -523,12 +524,15 @@ def run_workload(args, name: str, extras: bool) -> dict:
     n_acc = n0.to(torch.int64)
     tokens_per_round = float((n_acc + 1).float().mean())
     # The draw re-reads the decided row of every sampled sequence: target
-    # and draft row at a rejection, the target row alone for a bonus token.
+    # and draft row at a rejection. A bonus token's chunk is located from the
+    # row statistics, so the draw re-reads that one 32 KiB chunk of the
+    # target row (on these unfiltered rows every bonus row has mass).
     n_cpu = n_acc.cpu()
     kind = aux0["draw_kind"].cpu()
-    draw_rows = int(((kind == sv.DRAW_RESIDUAL) | (kind == sv.DRAW_RESIDUAL_AS_P)).sum()) * 2 \
-        + int((kind == sv.DRAW_BONUS).sum())
-    draw_bytes = draw_rows * w.V * w.elem_bytes
+    n_resid = int(((kind == sv.DRAW_RESIDUAL) | (kind == sv.DRAW_RESIDUAL_AS_P)).sum())
+    n_bonus = int((kind == sv.DRAW_BONUS).sum())
+    draw_rows = n_resid * 2 + n_bonus
+    draw_bytes = n_resid * 2 * w.V * w.elem_bytes + n_bonus * min(w.V * w.elem_bytes, CHUNK_BYTES)
     pc = per_call(alg_bytes, ms_per_step)
     log(f"[bench] {w.name}: {ms_per_step:.4f} ms/step ({pc['step_frac']:.3f} of peak on "
         f"algorithmic bytes); k_rowstats mean {k1_mean * 1e3:.1f} us (median "
@@ -676,8 +680,9 @@ def run_workload(args, name: str, extras: bool) -> dict:
                 "rows": draw_rows,
                 "bytes": draw_bytes,
                 "note": "side figure, not the step's bandwidth: the draw re-reads the decided "
-                        "row of each sampled sequence (target and draft at a rejection, target "
-                        "for a bonus); the algorithmic bytes exclude these re-reads",
+                        "rows of each sampled sequence (target and draft at a rejection; for a "
+                        "bonus, the one 32 KiB chunk of the target row that holds it); the "
+                        "algorithmic bytes exclude these re-reads",
             },
             "rotating_copies": len(copies),
             "mean_tokens_per_round": tokens_per_round,
