@@ -186,7 +186,13 @@ int spec_verify(const void *target_logits, const void *draft_logits, int32_t dty
  * position launches.
  * Pays when rejections come early (few accepted tokens per round): up to
  * position 4 it reads about (1 - a^L) / (1 - a) positions per sequence
- * instead of L + 1, at a per-token acceptance rate a.
+ * instead of L + 1, at a per-token acceptance rate a. Each position costs
+ * a launch and a decision (roughly 10 us on MI355X whatever its size), so
+ * it pays only when the rows it skips outweigh that, which needs large
+ * batches: measured on MI355X with bf16 logits, B=1024 k=7 V=128256 at 1.4
+ * tokens per round took 0.34 ms against 0.43 ms for spec_verify, while
+ * B=256 k=4 V=152064 took 0.12 ms against 0.095 ms and B=64 k=5 V=128256
+ * 0.077 ms against 0.049 ms.
  */
 int spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
                            const int32_t *draft_tokens, const int32_t *draft_len,
