@@ -1,5 +1,5 @@
 /*
- * oracle_driver.c -- runs every entry of the C oracle (oracle/spec_verify_ref.c)
+ * oracle_runner.c -- runs every entry of the C oracle (oracle/spec_verify_ref.c)
  * on small seeded batches, for builds with AddressSanitizer and
  * UndefinedBehaviorSanitizer, or ThreadSanitizer (`threads` > 1: disjoint
  * slices of each batch on parallel threads, as the Python wrapper does).
@@ -9,7 +9,7 @@
  * an allocation failure or an output leaves its documented range; the
  * sanitizers abort on their own findings.
  *
- *   oracle_driver [threads]
+ *   oracle_runner [threads]
  */
 #include <pthread.h>
 #include <stdint.h>
@@ -250,6 +250,6 @@ int main(int argc, char **argv)
     lcg_state = 0x9e3779b97f4a7c15ull;
     int bad = run_verify(threads < 1 ? 1 : (threads > 64 ? 64 : threads));
     bad |= run_tree_and_lookup();
-    printf("oracle driver: %s\n", bad ? "FAILED" : "ok");
+    printf("oracle runner: %s\n", bad ? "FAILED" : "ok");
     return bad ? 1 : 0;
 }

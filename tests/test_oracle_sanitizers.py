@@ -1,6 +1,6 @@
 """The C oracle under the compiler's sanitizers (CPU only).
 
-tests/sanitize/oracle_driver.c runs every oracle entry (the plain step, top-p,
+tests/sanitize/oracle_runner.c runs every oracle entry (the plain step, top-p,
 top-k with top-p, candidate trees, prompt lookup) on small seeded batches with
 ragged lengths, greedy and sampling sequences and planted input errors. It is
 built with gcc twice: AddressSanitizer + UndefinedBehaviorSanitizer (any
@@ -16,7 +16,7 @@ import pytest
 from conftest import ROOT
 
 SRC = [os.path.join(ROOT, "oracle", "spec_verify_ref.c"),
-       os.path.join(ROOT, "tests", "sanitize", "oracle_driver.c")]
+       os.path.join(ROOT, "tests", "sanitize", "oracle_runner.c")]
 BASE = ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-omit-frame-pointer"]
 
 pytestmark = pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -33,7 +33,7 @@ def _build_and_run(tmp_path, name, flags, threads, env_extra):
     run = subprocess.run([exe, str(threads)], capture_output=True, text=True, env=env,
                          timeout=300)
     assert run.returncode == 0, run.stdout + run.stderr[-4000:]
-    assert "oracle driver: ok" in run.stdout
+    assert "oracle runner: ok" in run.stdout
 
 
 def test_oracle_under_address_and_undefined_behaviour_sanitizers(tmp_path):
