@@ -410,7 +410,10 @@ def bench_lookup(K: int, W: int, cpu: bool) -> dict:
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # 100 calls of c5 take about 43 ms: the host's start and end of the timed
+    # region (first launch, final synchronisation) then add well under 1 us
+    # per call, where 20 calls carried about 1-2 us each.
+    ap.add_argument("--steps", type=int, default=SMALL_STEPS)
     ap.add_argument("--event-every", type=int, default=4,
                     help="record the kernel's HIP event pair on every Nth timed step")
     ap.add_argument("--warmup", type=int, default=5)
@@ -735,13 +738,13 @@ def parent(args) -> int:
     results = {}
     for name in WORKLOADS:
         # The headline times exactly the steps asked for. The smaller
-        # workloads time at least SMALL_STEPS, with the kernel's event pairs
-        # on about five of them: an event pair stalls the stream for a few
-        # microseconds, a measurable share of a step of 50-100 us.
+        # workloads time at least SMALL_STEPS. Each takes the kernel's event
+        # pairs on about five of its steps: an event pair stalls the stream
+        # for a microsecond or two, a measurable share of a step of 50-100 us.
         steps, every = args.steps, args.event_every
         if name != HEADLINE:
             steps = max(steps, SMALL_STEPS)
-            every = max(every, steps // 5)
+        every = max(every, steps // 5)
         cmd = [sys.executable, os.path.abspath(__file__), "--workload", name,
                "--steps", str(steps), "--warmup", str(args.warmup),
                "--event-every", str(every), "--settle-ms", str(args.settle_ms),

@@ -45,7 +45,7 @@ def test_counter_traffic_only_for_the_sources_it_was_taken_on(workload, monkeypa
 def test_parent_runs_every_workload_in_a_child(monkeypatch, capsys):
     """The parent starts one child per workload: the headline with the steps
     asked for and the extra entry points, the others on at least SMALL_STEPS
-    steps with about five event pairs; it prints one JSON line."""
+    steps, each with about five event pairs; it prints one JSON line."""
     calls = []
 
     def fake_run(cmd, stdout=None, text=None, timeout=None):
@@ -78,3 +78,11 @@ def test_parent_runs_every_workload_in_a_child(monkeypatch, capsys):
     line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
     assert set(line["configs"]) == set(bench.WORKLOADS)
     assert line["steps"] == 20
+    # with the default steps the headline too samples about five steps
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    calls.clear()
+    assert bench.parent(bench.parse_args()) == 0
+    head = next(c for c in calls if c[c.index("--workload") + 1] == bench.HEADLINE)
+    steps = int(head[head.index("--steps") + 1])
+    every = int(head[head.index("--event-every") + 1])
+    assert steps == bench.SMALL_STEPS and steps // every == 5
