@@ -1,0 +1,75 @@
+"""Degenerate inputs of the plain step against the oracle: rows with masked
+tokens (logit -inf, weight 0), logits quantised to a coarse grid so that the
+row maximum is tied between several tokens, and temperatures from 1e-3
+(the softmax nearly one-hot, or uniform over the tied maxima; most other
+weights underflow fp32) to 100 (nearly uniform), next to greedy sequences.
+Drafted tokens come from the draft's own distribution, so some are masked in
+the target (p(g) = 0: a certain rejection) and the residual often keeps a
+single token. Early exit must give the full step's outputs bit for bit."""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from conftest import bf16_bits, bf16_to_f32
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+import speculative_decoding_verification_11_amd as sv  # noqa: E402
+from oracle import parity  # noqa: E402
+from test_gpu_parity import DEV, batch_to, check, host, raw_batch, run_gpu, say  # noqa: E402
+
+TAUS = (1e-3, 0.05, 1.0, 0.0, 30.0, 100.0)
+
+
+def _edge_batch(rng, B, k, V, dtype, mask_frac):
+    t = np.round(rng.standard_normal((B, k + 1, V)) * 3.0 * 2) / 2   # steps of 0.5: ties
+    d = np.round((t[:, :k] + rng.standard_normal((B, k, V))) * 2) / 2
+    t[rng.random(t.shape) < mask_frac] = -np.inf
+    d[rng.random(d.shape) < mask_frac] = -np.inf
+    t[:, :, 0] = np.maximum(t[:, :, 0], -5.0)  # every row keeps a finite logit
+    d[:, :, 0] = np.maximum(d[:, :, 0], -5.0)
+    t, d = t.astype(np.float32), d.astype(np.float32)
+    if dtype == "bf16":
+        t, d = bf16_bits(t), bf16_bits(d)
+        dv = bf16_to_f32(d)
+    else:
+        dv = d
+    tau = np.array([TAUS[b % len(TAUS)] for b in range(B)], np.float32)
+    L = rng.integers(0, k + 1, size=B).astype(np.int32)
+    g = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        for i in range(L[b]):
+            if tau[b] == 0:
+                g[b, i] = int(np.argmax(dv[b, i]))
+            else:
+                q = scipy.special.softmax(dv[b, i].astype(np.float64) / float(tau[b]))
+                g[b, i] = int(rng.choice(V, p=q))
+    return raw_batch(t, d, g, L, tau)
+
+
+@pytest.mark.parametrize("V,dtype,mask_frac", [(20000, "bf16", 0.4), (9000, "f32", 0.4),
+                                               (3000, "bf16", 0.97)])
+def test_masked_tied_and_extreme_temperatures(V, dtype, mask_frac):
+    rng = np.random.default_rng(V + int(mask_frac * 100))
+    B, k = 48, 5
+    cb = _edge_batch(rng, B, k, V, dtype, mask_frac)
+    gb = batch_to(cb, DEV)
+    h = host(cb)
+    total = parity.Report()
+    for seed in (5, 0xABCDEF):
+        say(f"[case] edges V={V} {dtype} masked {mask_frac} seed={seed:#x}")
+        g = run_gpu(gb, seed)
+        r = parity.oracle_on(h, seed)
+        total.merge(parity.compare(g, r, h["draft_len"], h["temperature"], k))
+        ee = sv.spec_verify_early_exit(gb.target, gb.draft, gb.draft_tokens, gb.draft_len,
+                                       gb.temperature, seed, aux=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(ee[0].cpu().numpy(), g["out_tokens"])
+        assert np.array_equal(ee[1].cpu().numpy(), g["num_accepted"])
+        for key in ("seq_status", "draw_kind", "draw_row"):
+            assert np.array_equal(ee[2][key].cpu().numpy(), g[key]), key
+        kinds = set(g["draw_kind"].tolist())
+        assert sv.DRAW_RESIDUAL in kinds and sv.DRAW_GREEDY in kinds, kinds
+    check(total, f"edges V={V} {dtype}")
