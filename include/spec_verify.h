@@ -47,8 +47,9 @@
  * dtype, misaligned pointer, workspace too small) return a status at once
  * and enqueue nothing. Problems in device data are reported per sequence in
  * aux->seq_status (SPEC_SEQ_*); such a sequence gets num_accepted = 0 and
- * out_tokens all -1. Logits must be finite; non-finite logits give
- * unspecified (but memory-safe) results.
+ * out_tokens all -1. Logits may be -inf (a masked token: weight 0) as long
+ * as every row the call reads holds a finite logit; NaN, +inf or a row of
+ * -inf alone give unspecified (but memory-safe) results.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
