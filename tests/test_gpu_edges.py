@@ -5,7 +5,9 @@ row maximum is tied between several tokens, and temperatures from 1e-3
 weights underflow fp32) to 100 (nearly uniform), next to greedy sequences.
 Drafted tokens come from the draft's own distribution, so some are masked in
 the target (p(g) = 0: a certain rejection) and the residual often keeps a
-single token. Early exit must give the full step's outputs bit for bit."""
+single token; a few are then masked in the draft as well (q(g) = 0: status
+QZERO once the scan reaches them). Early exit must give the full step's
+outputs bit for bit."""
 import numpy as np
 import pytest
 import scipy.special
@@ -46,6 +48,11 @@ def _edge_batch(rng, B, k, V, dtype, mask_frac):
             else:
                 q = scipy.special.softmax(dv[b, i].astype(np.float64) / float(tau[b]))
                 g[b, i] = int(rng.choice(V, p=q))
+    # A drafted token the draft row masks (q(g) = 0 exactly): status QZERO
+    # once the scan reaches it, on both sides.
+    for b in range(2, B, 9):
+        if tau[b] > 0 and L[b] > 0 and g[b, 0] != 0:
+            d[b, 0, g[b, 0]] = 0xFF80 if dtype == "bf16" else -np.inf
     return raw_batch(t, d, g, L, tau)
 
 
@@ -72,4 +79,5 @@ def test_masked_tied_and_extreme_temperatures(V, dtype, mask_frac):
             assert np.array_equal(ee[2][key].cpu().numpy(), g[key]), key
         kinds = set(g["draw_kind"].tolist())
         assert sv.DRAW_RESIDUAL in kinds and sv.DRAW_GREEDY in kinds, kinds
+        assert (g["seq_status"] == sv.SEQ_QZERO).any()
     check(total, f"edges V={V} {dtype}")
