@@ -103,8 +103,10 @@ def _load():
         lib.spec_verify_filter_ref.restype = ctypes.c_int
         lib.spec_verify_full_ref.argtypes = [P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
-                                             ctypes.c_uint32] + [P] * 12 + [ctypes.c_double, P]
+                                             ctypes.c_uint32] + [P] * 12 + [ctypes.c_double, P, P]
         lib.spec_verify_full_ref.restype = ctypes.c_int
+        lib.ref_draw_band.argtypes = [P, P, ctypes.c_int64, ctypes.c_double, ctypes.c_double]
+        lib.ref_draw_band.restype = ctypes.c_double
         lib.ref_draw_window.argtypes = [P, ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P]
         lib.ref_draw_window.restype = None
         lib.ref_tree_greedy.argtypes = [P, P, P, ctypes.c_int, P, P]
@@ -178,6 +180,16 @@ def draw_window(w: np.ndarray, v: float, band: float):
     _load().ref_draw_window(_ptr(w), w.shape[0], float(v), float(band), ctypes.byref(lo),
                             ctypes.byref(hi))
     return int(lo.value), int(hi.value)
+
+
+def draw_band(p: np.ndarray, q, S: float, band: float) -> float:
+    """Flag band of a draw from max(0, p - q) (q None: from p) of mass S:
+    ``band``, or 8 * 2^-24 * sqrt(sum max(p, q)^2) / S where that is larger
+    (the fp32 resolution of the draw's CDF)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    qq = None if q is None else np.ascontiguousarray(q, dtype=np.float64)
+    return float(_load().ref_draw_band(_ptr(p), None if qq is None else _ptr(qq), p.shape[0],
+                                       float(S), float(band)))
 
 
 def nucleus_row(row: np.ndarray, p: np.ndarray, top_p: float):
@@ -259,9 +271,11 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
     each slice keeps its global sequence index, so results do not change.
     ``top_p`` (fp32) and ``top_k`` (int32), scalars or [B], filter every
     sampling row (readings TP1, TK1); ``margin_nucleus`` is returned with
-    ``top_p``. ``draw_window`` [B, 2]: the token ids the final draw could
-    select with its uniform moved by at most ``band`` (-1 where no token was
-    sampled).
+    ``top_p``. ``band_draw`` [B]: the final draw's flag band, ``band`` or
+    wider where fp32 weights cannot resolve the draw (ref_draw_band; NaN
+    where no token was sampled). ``draw_window`` [B, 2]: the token ids the
+    final draw could select with its uniform moved by at most that band (-1
+    where no token was sampled).
     """
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
@@ -296,6 +310,7 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
         draw_row=np.full(B, -1, dtype=np.int32),
         draw_kind=np.zeros(B, dtype=np.int32),
         draw_window=np.full((B, 2), -1, dtype=np.int32),
+        band_draw=np.full(B, np.nan),
     )
     if tp is not None:
         res["margin_nucleus"] = np.full((B, 2 * k + 1), np.nan)
@@ -315,7 +330,8 @@ def spec_verify_ref(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndar
             b1 - b0, k, V, ctypes.c_uint64(seed & (2**64 - 1)),
             ctypes.c_uint32((seq_base + b0) & 0xFFFFFFFF), *[_ptr(o) for o in outs],
             _ptr(mn) if mn is not None else None, _ptr(res["draw_row"][sl]),
-            _ptr(res["draw_kind"][sl]), float(band), _ptr(res["draw_window"][sl]))
+            _ptr(res["draw_kind"][sl]), float(band), _ptr(res["draw_window"][sl]),
+            _ptr(res["band_draw"][sl]))
 
     if nthreads <= 1 or B <= 1:
         rc = run(0, B)

@@ -17,11 +17,21 @@ inputs, sequence by sequence:
   The residual mass S is compared wherever the final draw is compared,
   within ``rel`` plus the absolute ``RESID_ABS`` derived below.
 
+A final draw's band is ``band`` or, where that is larger, the fp32
+resolution of the CDF it scans (``band_draw`` from the oracle: 8 * 2^-24 *
+sqrt(sum max(p, q)^2) / S). It exceeds ``band`` only when S is small against
+the largest weights the kernel rounds, as when two nearly equal rows put
+almost all their mass on one token; such draws are counted in
+``flagged_wide``. Where it reaches 1 and one side's fp32 residual rounded to
+nothing (kind RESIDUAL against RESIDUAL_AS_P), the draw is unresolved and
+counted as one flagged draw.
+
 A flagged final draw on which the two sides part must still land inside the
 oracle's band window: the token ids that the oracle's own draw would pick
-with its uniform moved by at most ``band``. A disagreement outside that
-window is a mismatch however small the oracle's margin, so a locate error
-among low-weight tokens (whose margins are always below the band) is caught.
+with its uniform moved by at most the draw's band. A disagreement outside
+that window is a mismatch however small the oracle's margin, so a locate
+error among low-weight tokens (whose margins are always below the band) is
+caught.
 """
 from __future__ import annotations
 
@@ -31,7 +41,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import DRAW_GREEDY, SEQ_OK, SEQ_QZERO, spec_verify_ref
+from . import DRAW_GREEDY, DRAW_RESIDUAL, DRAW_RESIDUAL_AS_P, SEQ_OK, SEQ_QZERO, spec_verify_ref
 
 FLT_MIN = float(np.finfo(np.float32).tiny)
 
@@ -83,6 +93,7 @@ class Report:
     draws: int = 0
     flagged: int = 0
     flagged_disagree: int = 0
+    flagged_wide: int = 0  # flagged only by a final draw's band wider than `band`
     boundary_status: int = 0
     boundary_values: int = 0
     compared_tokens: int = 0
@@ -98,6 +109,7 @@ class Report:
         self.draws += other.draws
         self.flagged += other.flagged
         self.flagged_disagree += other.flagged_disagree
+        self.flagged_wide += other.flagged_wide
         self.boundary_status += other.boundary_status
         self.boundary_values += other.boundary_values
         self.compared_tokens += other.compared_tokens
@@ -120,7 +132,8 @@ class Report:
     def summary(self) -> str:
         bands = " ".join(f"<{b:g}:{n}" for b, n in sorted(self.band_counts.items(), reverse=True))
         head = (f"sequences={self.sequences} draws={self.draws} flagged={self.flagged} "
-                f"({self.flagged_fraction:.2e}) flagged_disagree={self.flagged_disagree} "
+                f"({self.flagged_fraction:.2e}) flagged_wide={self.flagged_wide} "
+                f"flagged_disagree={self.flagged_disagree} "
                 f"max_disagree_margin={self.max_disagree_margin:.2e} margins[{bands}] "
                 f"boundary_status={self.boundary_status} boundary_values={self.boundary_values} "
                 f"S_compared={self.resid_compared} max|dS|={self.max_abs_dS:.2e} "
@@ -159,16 +172,21 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
     n_ref = ref["num_accepted"].shape[0]
     rows = list(range(n_ref)) if rows is None else [int(r) for r in rows]
 
-    def draw(margin: float, agree: bool, what: str, in_window: bool = True) -> bool:
+    def draw(margin: float, agree: bool, what: str, in_window: bool = True,
+             band_here: float = band) -> bool:
         """Account one draw; returns False when the comparison must stop.
         ``in_window``: for a final draw, whether the GPU's token lies in the
-        oracle's band window (a flagged disagreement must)."""
+        oracle's band window (a flagged disagreement must). ``band_here``:
+        the draw's own flag band (a final draw's may be wider than ``band``
+        where fp32 weights cannot resolve it)."""
         rep.draws += 1
         for b_ in BANDS:
             if margin < b_:
                 rep.band_counts[b_] += 1
-        if margin < band:
+        if margin < band_here:
             rep.flagged += 1
+            if not margin < band:
+                rep.flagged_wide += 1
             if not agree:
                 rep.flagged_disagree += 1
                 rep.max_disagree_margin = max(rep.max_disagree_margin, margin)
@@ -263,7 +281,16 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
         if g_n != r_n:
             rep.mismatches.append(f"{tag}: accepted count {g_n} vs {r_n}")
             continue
-        if int(gpu["draw_kind"][b]) != int(ref["draw_kind"][j]):
+        # the final draw's flag band: the oracle's (ref_draw_band), at least `band`
+        bd = float(ref["band_draw"][j]) if "band_draw" in ref else float("nan")
+        band_here = max(band, bd) if np.isfinite(bd) else band
+        kinds = {int(gpu["draw_kind"][b]), int(ref["draw_kind"][j])}
+        if band_here >= 1.0 and kinds == {DRAW_RESIDUAL, DRAW_RESIDUAL_AS_P}:
+            # a residual that fp32 cannot tell from zero on one side: its
+            # mass, kind and token are all unresolved; one flagged draw
+            draw(0.0, False, f"{tag}: unresolved residual", True, band_here)
+            continue
+        if len(kinds) > 1:
             rep.mismatches.append(f"{tag}: draw kind {gpu['draw_kind'][b]} vs {ref['draw_kind'][j]}")
         S_g, S_r = float(gpu["resid_mass"][b]), float(ref["resid_mass"][j])
         rep.resid_compared += 1
@@ -279,6 +306,6 @@ def compare(gpu: dict, ref: dict, draft_len, temperature, k: int, rows=None, rel
         in_window = "draw_window" in ref and lo <= int(g_out[r_n]) <= hi
         if draw(float(ref["margin_draw"][j]), g_out[r_n] == r_out[r_n],
                 f"{tag}: final token {g_out[r_n]} vs {r_out[r_n]} (window {lo}..{hi})",
-                in_window):
+                in_window, band_here):
             rep.compared_tokens += 1
     return rep

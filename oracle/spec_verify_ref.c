@@ -384,6 +384,31 @@ void ref_draw_window(const double *w, int64_t V, double v, double band, int64_t 
 }
 
 /* ------------------------------------------------------------------ */
+/* Flag band of a final draw (parity protocol, not the method). The     */
+/* kernel forms each draw weight in fp32 from p(x) and, for a residual, */
+/* q(x): a few roundings of relative size 2^-24 of the larger of the    */
+/* two. Relative to S the CDF it scans is then uncertain by about       */
+/* 2^-24 sqrt(sum_x m(x)^2) / S for independent roundings, with m(x) =  */
+/* max(p(x), q(x)) (p(x) alone when q is NULL). A uniform within 8 times */
+/* that of a CDF boundary is as undecided in fp32 as one within `band`; */
+/* the larger of the two is returned. Where two nearly equal rows put   */
+/* almost all their mass on one token, S is tiny against that token's   */
+/* weight and the band exceeds 1: the draw is not resolved in fp32.     */
+/* ------------------------------------------------------------------ */
+double ref_draw_band(const double *p, const double *q, int64_t V, double S, double band)
+{
+    if (!(S > 0.0))
+        return band;
+    double m2 = 0.0;
+    for (int64_t x = 0; x < V; x++) {
+        const double m = q && q[x] > p[x] ? q[x] : p[x];
+        m2 += m * m;
+    }
+    const double e = 8.0 * 0x1p-24 * sqrt(m2) / S;
+    return e > band ? e : band;
+}
+
+/* ------------------------------------------------------------------ */
 /* One sampling round for one sequence, given the probability rows and  */
 /* the uniforms ([ART] steps "Accept or reject, left to right", "Stop   */
 /* at the first rejection", "Bonus token"; [TLS] P_accept, the          */
@@ -492,7 +517,8 @@ static int verify_batch(const void *target, const void *draft, int dtype,
                         int32_t *num_accepted, int32_t *seq_status, double *p_g, double *q_g,
                         int32_t *argmax, double *resid_mass, double *margin_accept,
                         double *margin_draw, double *margin_nucleus, int32_t *draw_row,
-                        int32_t *draw_kind, double band, int32_t *draw_window)
+                        int32_t *draw_kind, double band, int32_t *draw_window,
+                        double *band_draw)
 {
     const size_t esz = dtype == REF_F32 ? 4 : 2;
     double *p = malloc(sizeof(double) * (size_t)(k + 1) * (size_t)V);
@@ -531,6 +557,7 @@ static int verify_batch(const void *target, const void *draft, int dtype,
         if (draw_row) draw_row[b] = -1;
         if (draw_kind) draw_kind[b] = REF_DRAW_NONE;
         if (draw_window) draw_window[2 * (size_t)b] = draw_window[2 * (size_t)b + 1] = -1;
+        if (band_draw) band_draw[b] = NAN;
         num_accepted[b] = 0;
 
         /* Input checks, in this order: length, temperature, top-p, tokens.
@@ -614,14 +641,21 @@ static int verify_batch(const void *target, const void *draft, int dtype,
             if (margin_draw) margin_draw[b] = mdraw;
             if (draw_row) draw_row[b] = row;
             if (draw_kind) draw_kind[b] = kind;
-            if (draw_window) {
+            if (draw_window || band_draw) {
                 /* the weights of the final draw: the residual (still in the
-                 * scratch row w), or p at the draw row */
-                const double *wd = kind == REF_DRAW_RESIDUAL ? w : p + (size_t)row * V;
-                int64_t lo, hi;
-                ref_draw_window(wd, V, v[row], band, &lo, &hi);
-                draw_window[2 * (size_t)b] = (int32_t)lo;
-                draw_window[2 * (size_t)b + 1] = (int32_t)hi;
+                 * scratch row w), or p at the draw row; the window is taken
+                 * over the draw's own flag band */
+                const int resid = kind == REF_DRAW_RESIDUAL;
+                const double *wd = resid ? w : p + (size_t)row * V;
+                const double be = ref_draw_band(p + (size_t)row * V,
+                                                resid ? q + (size_t)row * V : NULL, V, S, band);
+                if (band_draw) band_draw[b] = be;
+                if (draw_window) {
+                    int64_t lo, hi;
+                    ref_draw_window(wd, V, v[row], be, &lo, &hi);
+                    draw_window[2 * (size_t)b] = (int32_t)lo;
+                    draw_window[2 * (size_t)b + 1] = (int32_t)hi;
+                }
             }
         }
         num_accepted[b] = n;
@@ -643,7 +677,7 @@ int spec_verify_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, NULL, B,
                         k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, NULL, draw_row,
-                        draw_kind, 0.0, NULL);
+                        draw_kind, 0.0, NULL, NULL);
 }
 
 /* The whole step with nucleus filtering (reading TP1): top_p [B] fp32, 1  */
@@ -662,7 +696,7 @@ int spec_verify_topp_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, NULL, top_p,
                         B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
-                        draw_row, draw_kind, 0.0, NULL);
+                        draw_row, draw_kind, 0.0, NULL, NULL);
 }
 
 /* The whole step with top-k and nucleus filtering (TK1 then TP1): top_k */
@@ -681,14 +715,16 @@ int spec_verify_filter_ref(const void *target, const void *draft, int dtype,
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_k, top_p,
                         B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
-                        draw_row, draw_kind, 0.0, NULL);
+                        draw_row, draw_kind, 0.0, NULL, NULL);
 }
 
 /* Every option at once: spec_verify_filter_ref (top_k and top_p may be  */
-/* NULL) plus draw_window [B, 2] (may be NULL): for the final draw of a  */
-/* sampling sequence, the smallest and largest token ids a shift of its  */
-/* uniform by at most `band` could select (ref_draw_window); -1 where    */
-/* there was no sampled draw.                                            */
+/* NULL) plus, for the final draw of a sampling sequence, band_draw [B]  */
+/* (may be NULL): its flag band (ref_draw_band: `band`, or wider where   */
+/* fp32 weights cannot resolve the draw; NaN where there was no sampled  */
+/* draw), and draw_window [B, 2] (may be NULL): the smallest and largest */
+/* token ids a shift of its uniform by at most that band could select    */
+/* (ref_draw_window); -1 where there was no sampled draw.                */
 int spec_verify_full_ref(const void *target, const void *draft, int dtype,
                          const int32_t *draft_tokens, const int32_t *draft_len,
                          const float *temperature, const int32_t *top_k, const float *top_p,
@@ -697,12 +733,12 @@ int spec_verify_full_ref(const void *target, const void *draft, int dtype,
                          double *p_g, double *q_g, int32_t *argmax, double *resid_mass,
                          double *margin_accept, double *margin_draw, double *margin_nucleus,
                          int32_t *draw_row, int32_t *draw_kind, double band,
-                         int32_t *draw_window)
+                         int32_t *draw_window, double *band_draw)
 {
     return verify_batch(target, draft, dtype, draft_tokens, draft_len, temperature, top_k, top_p,
                         B, k, V, seed, seq_base, out_tokens, num_accepted, seq_status, p_g, q_g,
                         argmax, resid_mass, margin_accept, margin_draw, margin_nucleus,
-                        draw_row, draw_kind, band, draw_window);
+                        draw_row, draw_kind, band, draw_window, band_draw);
 }
 
 /* ------------------------------------------------------------------ */

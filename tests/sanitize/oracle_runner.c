@@ -25,7 +25,7 @@ int spec_verify_full_ref(const void *target, const void *draft, int dtype,
                          double *p_g, double *q_g, int32_t *argmax, double *resid_mass,
                          double *margin_accept, double *margin_draw, double *margin_nucleus,
                          int32_t *draw_row, int32_t *draw_kind, double band,
-                         int32_t *draw_window);
+                         int32_t *draw_window, double *band_draw);
 int spec_tree_ref(const void *target, int dtype, const int32_t *parents, const int32_t *tokens,
                   const int32_t *n_nodes, int32_t B, int32_t N, int64_t V, int32_t *out_tokens,
                   int32_t *path_nodes, int32_t *num_accepted, int32_t *seq_status,
@@ -162,7 +162,7 @@ static void *run_slice(void *arg)
         bt->qg + (size_t)b0 * k, bt->amax + (size_t)b0 * (k + 1), bt->S + b0,
         bt->macc + (size_t)b0 * k, bt->mdraw + b0,
         s->filters >= 1 ? bt->mnuc + (size_t)b0 * (2 * k + 1) : NULL, bt->drow + b0,
-        bt->dkind + b0, 1e-6, bt->win + 2 * (size_t)b0);
+        bt->dkind + b0, 1e-6, bt->win + 2 * (size_t)b0, NULL);
     return NULL;
 }
 

@@ -2,7 +2,8 @@
 
 The oracle's own outputs stand in for the GPU's; planted deviations must be
 reported as mismatches, and only the documented exceptions (a nucleus
-boundary within the band, fp32 rounding of the residual mass) excused.
+boundary within the band, fp32 rounding of the residual mass, a final draw
+that fp32 weights cannot resolve) excused.
 """
 import copy
 
@@ -165,3 +166,80 @@ def test_oracle_window_contains_its_own_token(run):
         if ref["seq_status"][b] == parity.SEQ_OK and host["temperature"][b] > 0:
             lo, hi = ref["draw_window"][b]
             assert lo <= ref["out_tokens"][b, ref["num_accepted"][b]] <= hi
+
+
+# ---------------------------------------------------------------------------
+# A final draw's band widens with the fp32 resolution of its CDF.
+# ---------------------------------------------------------------------------
+
+def test_draw_band_closed_form(oracle_lib):
+    import oracle
+    eps = 2.0 ** -24
+    # p = q uniform over n ids: sqrt(sum max(p, q)^2) = 1 / sqrt(n)
+    for n, S in ((4, 0.5), (64, 1e-3), (1000, 1e-9)):
+        p = np.full(n, 1.0 / n)
+        want = max(1e-6, 8 * eps / np.sqrt(n) / S)
+        assert oracle.draw_band(p, p.copy(), S, 1e-6) == pytest.approx(want, rel=1e-12)
+    # without q the scale is p's alone; the larger of p and q counts per id
+    p = np.array([0.5, 0.25, 0.25])
+    q = np.array([0.25, 0.5, 0.25])
+    m = np.array([0.5, 0.5, 0.25])
+    assert oracle.draw_band(p, q, 1e-4, 1e-6) == pytest.approx(
+        8 * eps * np.sqrt((m ** 2).sum()) / 1e-4, rel=1e-12)
+    assert oracle.draw_band(p, None, 1e-4, 1e-6) == pytest.approx(
+        8 * eps * np.sqrt((p ** 2).sum()) / 1e-4, rel=1e-12)
+    # never below the base band, and the base band where there is no mass
+    assert oracle.draw_band(p, q, 1.0, 1e-3) == 1e-3
+    assert oracle.draw_band(p, q, 0.0, 1e-6) == 1e-6
+
+
+def _dominant_case():
+    """Target and draft nearly one-hot on the same id at a low temperature,
+    and a drafted token from the far tail: a certain rejection whose
+    residual mass (about 2.6e-10) is far below fp32's resolution of the
+    dominant id's weight."""
+    t = np.array([[-1.6796875, -4.0, -2.625, -2.375, 1.25, -0.67578125, 6.625],
+                  [-7.4375, 6.1875, 2.140625, -0.80859375, 4.28125, 4.875, -5.71875]],
+                 np.float32)[None]
+    d = np.array([[-2.65625, -3.71875, -2.59375, -1.859375, 0.84765625, -0.78515625, 6.21875]],
+                 np.float32)[None]
+    host = {"target": t, "draft": d, "draft_tokens": np.array([[2]], np.int32),
+            "draft_len": np.array([1], np.int32), "temperature": np.array([0.3], np.float32)}
+    return host
+
+
+def test_unresolved_residual_is_flagged_not_compared(oracle_lib):
+    host = _dominant_case()
+    seed = 2558530382594599338
+    ref = parity.oracle_on(host, seed)
+    assert ref["num_accepted"][0] == 0 and ref["draw_kind"][0] == parity.DRAW_RESIDUAL
+    assert ref["resid_mass"][0] < 1e-9 and ref["band_draw"][0] > 1.0
+    lo, hi = ref["draw_window"][0]
+    assert (lo, hi) == (0, 6)  # a band of 1 or more covers every id with weight
+    # another id with residual weight (p > q there): flagged, not a mismatch
+    gpu = copy.deepcopy(ref)
+    gpu["out_tokens"][0, 0] = 0
+    gpu["resid_mass"][0] = 8.1e-13
+    rep = parity.compare(gpu, ref, host["draft_len"], host["temperature"], 1)
+    assert rep.ok(), rep.summary()
+    assert rep.flagged == 1 and rep.flagged_wide == 1 and rep.flagged_disagree == 1
+    # the fp32 residual rounded to nothing: drawn from p instead, still flagged
+    gpu2 = copy.deepcopy(gpu)
+    gpu2["draw_kind"][0] = parity.DRAW_RESIDUAL_AS_P
+    gpu2["resid_mass"][0] = 1.0
+    rep2 = parity.compare(gpu2, ref, host["draft_len"], host["temperature"], 1)
+    assert rep2.ok() and rep2.flagged == 1, rep2.summary()
+
+
+def test_resolved_draws_keep_the_base_band(run, oracle_lib):
+    """Where the weights resolve the draw its band is the base band, and the
+    same disagreement as above (a large margin) is a mismatch."""
+    host, ref = run
+    ok = [b for b in range(B) if ref["seq_status"][b] == parity.SEQ_OK
+          and ref["band_draw"][b] == 1e-6 and ref["margin_draw"][b] > 1e-3]
+    assert ok
+    b = ok[0]
+    n = int(ref["num_accepted"][b])
+    gpu = copy.deepcopy(ref)
+    gpu["out_tokens"][b, n] = (gpu["out_tokens"][b, n] + 1) % V
+    assert any("final token" in m for m in _cmp(gpu, ref, host).mismatches)
