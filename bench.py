@@ -193,8 +193,9 @@ def cpu_baseline(batch, seed: int, nseq: int, gpu_out: dict) -> dict:
     on one thread; each the median of three runs.
     The oracle's outputs of the first run are compared with the GPU's outputs
     of the same batch and seed: the flagged fraction of the batch's draws
-    (oracle margin below 1e-6), how many flagged draws the two sides decided
-    differently, and whether any draw outside the band differs."""
+    (oracle margin below 1e-6, or below a final draw's wider fp32-resolution
+    band), how many flagged draws the two sides decided differently, and
+    whether any draw outside the band differs."""
     import oracle
     from oracle import parity
     from speculative_decoding_verification_11_amd import workloads as wl
@@ -235,11 +236,14 @@ def cpu_baseline(batch, seed: int, nseq: int, gpu_out: dict) -> dict:
             "cpu_model": cpu_model(),
             "parity": {"sequences": rep.sequences, "draws": rep.draws,
                        "flagged": rep.flagged, "flagged_fraction": rep.flagged_fraction,
+                       "flagged_wide": rep.flagged_wide,
                        "flagged_disagree": rep.flagged_disagree,
                        "max_abs_dS": rep.max_abs_dS, "max_rel_dS_large": rep.max_rel_dS_large,
                        "mismatches": len(rep.mismatches),
                        "note": "GPU outputs of the timed batch and seed against this oracle "
-                               "run; flagged = oracle margin below 1e-6"}}
+                               "run; flagged = oracle margin below 1e-6, or below a final "
+                               "draw's fp32-resolution band where that is wider "
+                               "(flagged_wide)"}}
 
 
 def roof(achieved_gbps: float, what: str) -> dict:
