@@ -81,3 +81,22 @@ def test_masked_tied_and_extreme_temperatures(V, dtype, mask_frac):
         assert sv.DRAW_RESIDUAL in kinds and sv.DRAW_GREEDY in kinds, kinds
         assert (g["seq_status"] == sv.SEQ_QZERO).any()
     check(total, f"edges V={V} {dtype}")
+
+
+def test_residual_below_fp32_resolution_is_flagged():
+    """Target and draft one-hot on the same id at tau 0.3 and a drafted token
+    from the far tail: the residual mass (about 2.6e-10) is below fp32's
+    resolution of the dominant id's weight. The GPU's draw must still be a
+    valid one (inside the oracle's window), reported as flagged by the
+    draw's widened band rather than compared."""
+    from test_parity_protocol import _dominant_case
+    host_arrays = _dominant_case()
+    seed = 2558530382594599338
+    cb = raw_batch(host_arrays["target"], host_arrays["draft"], host_arrays["draft_tokens"],
+                   host_arrays["draft_len"], host_arrays["temperature"])
+    g = run_gpu(batch_to(cb, DEV), seed)
+    r = parity.oracle_on(host(cb), seed)
+    assert r["band_draw"][0] > 1.0
+    rep = parity.compare(g, r, host_arrays["draft_len"], host_arrays["temperature"], 1)
+    check(rep, "residual below fp32 resolution")
+    assert rep.flagged == 1 and rep.flagged_wide == 1
